@@ -1,0 +1,379 @@
+"""Pins of the fp64 oracle against what the pages and the mathematics fix.
+
+Each pin is computed by code other than the oracle's own (exact rationals,
+pure-Python loops, bit-field definitions, an independent normal CDF) or is a
+value the pages print (tests/golden/printed_examples.json, cited there).
+"""
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle as O
+import moe_synth as S
+
+GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "printed_examples.json")))
+
+
+# ----------------------------------------------------------------- codebooks
+def test_nf4_codebook_invariants():
+    c = O.nf4_codebook()
+    assert c.dtype == np.float32 and c.shape == (16,)
+    assert c[0] == -1.0 and c[7] == 0.0 and c[15] == 1.0
+    assert np.all(np.diff(c) > 0)
+    assert (c < 0).sum() == 7 and (c > 0).sum() == 8
+
+
+def _phi(z):  # standard normal CDF from math.erfc (independent of scipy's ndtri)
+    return 0.5 * math.erfc(-z / math.sqrt(2.0))
+
+
+def _phi_inv(p):  # bisection on _phi
+    lo, hi = -10.0, 10.0
+    for _ in range(200):
+        mid = 0.5 * (lo + hi)
+        if _phi(mid) < p:
+            lo = mid
+        else:
+            hi = mid
+    return 0.5 * (lo + hi)
+
+
+def test_nf4_codebook_is_normal_quantiles():
+    """Each |c| times the largest quantile sits at its NormalFloat level."""
+    c = O.nf4_codebook().astype(np.float64)
+    delta = 1 - 0.5 * (1 / 30 + 1 / 32)
+    zmax = _phi_inv(delta)
+    pos_levels = [delta - i * (delta - 0.5) / 8 for i in range(8)]      # 8 levels, descending
+    neg_levels = [delta - i * (delta - 0.5) / 7 for i in range(7)]      # 7 levels, descending
+    for i, p in enumerate(pos_levels):
+        assert abs(_phi(c[15 - i] * zmax) - p) < 2e-7
+    for i, p in enumerate(neg_levels):
+        assert abs(_phi(-c[i] * zmax) - p) < 2e-7
+
+
+def test_e2m1_table_from_bit_fields():
+    v = O.e2m1_values()
+    for code in range(16):
+        s, e, m = code >> 3, (code >> 1) & 3, code & 1
+        mag = m * 0.5 if e == 0 else 2.0 ** (e - 1) * (1 + m / 2)
+        assert v[code] == (-mag if s else mag)
+
+
+# ----------------------------------------------------------------- NF4
+def test_nf4_printed_roundtrip():
+    g = GOLD["nf4_roundtrip"]
+    for seed in range(3):
+        w = np.random.default_rng(seed).standard_normal(g["w_shape"], dtype=np.float32)
+        packed, absmax = O.nf4_quantize(w)
+        assert list(packed.shape) == g["packed_shape"] and packed.dtype == np.uint8
+        assert list(absmax.shape) == g["absmax_shape"] and absmax.dtype == np.float32
+        wq = O.nf4_dequantize(packed, absmax, *g["w_shape"])
+        err = O.rel_err(wq, w)
+        assert round(err, 2) == g["rel_err_printed"]
+        p2, a2 = O.nf4_quantize(wq)
+        assert np.array_equal(p2, packed) == g["repack_idempotent"]
+        assert np.array_equal(a2, absmax)
+
+
+def _nearest_exact(w, a, table, tie="lower"):
+    """Index of the nearest table[i]*a to w in exact rationals."""
+    W, A = Fraction(float(w)), Fraction(float(a))
+    d = [abs(W - Fraction(float(t)) * A) for t in table]
+    best = min(d)
+    cands = [i for i, x in enumerate(d) if x == best]
+    if tie == "lower":
+        return cands[0]
+    return [i for i in cands if i % 2 == 0][0] if len(cands) > 1 else cands[0]
+
+
+def test_nf4_codes_are_exact_nearest_with_ties_low():
+    c = O.nf4_codebook()
+    rng = np.random.default_rng(7)
+    w = rng.standard_normal((3, 128)).astype(np.float32) * np.float32(0.02)
+    # plant exact ties between codes 6|7 and 7|8: c[6]/2 and c[8]/2 are fp32
+    w[0, 0] = 1.0
+    w[0, 1] = np.float32(c[8] / 2)
+    w[0, 2] = np.float32(c[6] / 2)
+    w[0, 3] = -0.0
+    for i in range(14):                 # other exactly representable midpoints
+        m = (np.float64(c[i]) + np.float64(c[i + 1])) / 2
+        if np.float64(np.float32(m)) == m:
+            w[1, 64 + i] = np.float32(m)
+    w[1, 64 + 15] = 1.0
+    packed, absmax = O.nf4_quantize(w)
+    codes = np.empty(w.shape, np.uint8)
+    codes[:, 0::2], codes[:, 1::2] = packed >> 4, packed & 15
+    for r in range(w.shape[0]):
+        for k in range(w.shape[1]):
+            a = absmax[r, k // 64]
+            assert codes[r, k] == _nearest_exact(w[r, k], a, c), (r, k)
+    assert codes[0, 1] == 7 and codes[0, 2] == 6
+
+
+def test_nf4_absmax_error_bound_zero_block_nibble_order():
+    c = O.nf4_codebook().astype(np.float64)
+    rng = np.random.default_rng(3)
+    w = rng.standard_normal((4, 256)).astype(np.float32)
+    w[2, 64:128] = 0.0                                   # all-zero block
+    w[3, 0], w[3, 1] = 5.0, -5.0                         # nibble order probe
+    packed, absmax = O.nf4_quantize(w)
+    wq = O.nf4_dequantize(packed, absmax, 4, 256)
+    blk = np.abs(wq).reshape(4, 4, 64).max(axis=2)
+    assert np.array_equal(blk.astype(np.float32), absmax)          # absmax survives exactly
+    half_gap = np.max(np.diff(c)) / 2
+    bound = np.repeat(absmax.astype(np.float64), 64, axis=1) * (half_gap + 2 ** -23)
+    assert np.all(np.abs(wq.astype(np.float64) - w) <= bound)
+    assert absmax[2, 1] == 0 and np.all(packed[2, 32:64] == 0x77) and np.all(wq[2, 64:128] == 0)
+    assert packed[3, 0] == 0xF0                            # high nibble = even k
+
+
+def test_nf4_absmax_share_printed():
+    g = GOLD["nf4_absmax_share"]
+    # one Qwen3-30B-A3B-shaped expert (gate + up + down = 3 * I * H weights,
+    # I = 768, H = 2048) packed as NF4 with fp32 absmax per 64
+    elems = 3 * 768 * 2048
+    codes, absmax = elems // 2, (elems // 64) * 4
+    assert absmax == g["absmax_bytes"] and codes + absmax == g["row_bytes"]
+
+
+# ----------------------------------------------------------------- MXFP4
+def test_mxfp4_printed_roundtrip():
+    g = GOLD["mxfp4_roundtrip"]
+    for seed in range(3):
+        w = np.random.default_rng(seed).standard_normal(g["w_shape"], dtype=np.float32)
+        codes, scales = O.mxfp4_quantize(w)
+        assert list(codes.reshape(w.shape[0], -1, 16).shape) == g["blocks_shape"]
+        assert list(scales.shape) == g["scales_shape"]
+        wq = O.mxfp4_dequantize(codes, scales, *g["w_shape"])
+        assert round(O.rel_err(wq, w), 2) in (0.11, g["rel_err_printed"])
+        c2, s2 = O.mxfp4_quantize(wq)
+        assert np.array_equal(c2, codes) and np.array_equal(s2, scales)
+
+
+def test_mxfp4_exact_nearest_ties_even_saturation():
+    mags = O.e2m1_values()[:8]
+    rng = np.random.default_rng(11)
+    w = rng.standard_normal((2, 64)).astype(np.float32)
+    # block 0: amax 7 -> X = floor(log2 7) - 2 = 0; plant ties and saturation
+    w[0, :32] = np.float32(0.1)
+    w[0, 0] = 7.0                                          # 6 < v < 8: saturates to 6
+    for i, t in enumerate([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, -2.5, -0.25]):
+        w[0, 1 + i] = t
+    codes, scales = O.mxfp4_quantize(w)
+    full = np.empty(w.shape, np.uint8)
+    full[:, 0::2], full[:, 1::2] = codes & 15, codes >> 4
+    for r in range(2):
+        for b in range(2):
+            blk = w[r, 32 * b:32 * b + 32].astype(np.float64)
+            amax = np.abs(blk).max()
+            X = max(-127, min(127, math.floor(math.log2(amax)) - 2))
+            assert scales[r, b] == X + 127
+            assert 4 <= amax / 2.0 ** X < 8
+            for i, v in enumerate(blk):
+                q = Fraction(float(v)) / Fraction(2) ** X
+                if abs(q) >= 6:
+                    mag = 7
+                else:
+                    d = [abs(abs(q) - Fraction(float(m))) for m in mags]
+                    best = min(d)
+                    cands = [j for j, x in enumerate(d) if x == best]
+                    mag = cands[0] if len(cands) == 1 else [j for j in cands if j % 2 == 0][0]
+                expect = mag | (8 if math.copysign(1.0, v) < 0 else 0)
+                assert full[r, 32 * b + i] == expect, (r, b, i, v)
+    assert full[0, 0] == 7
+    assert [full[0, 1 + i] & 7 for i in range(7)] == [0, 2, 2, 4, 4, 6, 6]
+    assert codes[0, 0] & 15 == 7                            # low nibble = even k
+
+
+def test_mxfp4_zero_block_and_nan_scale():
+    w = np.zeros((1, 64), np.float32)
+    w[0, 40] = 1.0
+    codes, scales = O.mxfp4_quantize(w)
+    assert scales[0, 0] == 0 and np.all(codes[0, :16] == 0)
+    out = O.mxfp4_dequantize(codes, scales, 1, 64)
+    assert np.all(out[0, :32] == 0) and out[0, 40] == 1.0
+    s2 = scales.copy(); s2[0, 1] = 255
+    assert np.all(np.isnan(O.mxfp4_dequantize(codes, s2, 1, 64)[0, 32:]))
+
+
+# ----------------------------------------------------------------- routing
+def _bf16(x):
+    return S.f32_to_bf16_bits(np.asarray(x, np.float32))
+
+
+def test_router_logits_bruteforce():
+    rng = np.random.default_rng(5)
+    xb = _bf16(rng.standard_normal((3, 8)))
+    W = rng.standard_normal((4, 8)).astype(np.float32)
+    b = rng.standard_normal(4).astype(np.float32)
+    L = O.router_logits(xb, W, b)
+    for t in range(3):
+        xs = [float(np.array([int(v) << 16], np.uint32).view(np.float32)[0]) for v in xb[t]]
+        for e in range(4):
+            ref = math.fsum(xs[h] * float(W[e, h]) for h in range(8)) + float(b[e])
+            assert abs(L[t, e] - ref) <= 1e-12 * (1 + abs(ref))
+
+
+def test_topk_bruteforce_ties_and_weights():
+    rng = np.random.default_rng(9)
+    L = rng.standard_normal((20, 6))
+    L[0] = [1.0, 3.0, 3.0, 0.5, 3.0, -1.0]                # ties -> lower id first
+    for k in (1, 2, 3, 6):
+        ids, w = O.topk_route(L, k, True)
+        for t in range(20):
+            order = sorted(range(6), key=lambda e: (-L[t, e], e))[:k]
+            assert list(ids[t]) == order
+            ex = [math.exp(L[t, e]) for e in order]
+            ref = [v / math.fsum(ex) for v in ex]
+            assert np.allclose(w[t], ref, rtol=1e-13, atol=0)
+            assert abs(w[t].sum() - 1.0) < 1e-12
+        if k == 1:
+            assert np.all(w == 1.0)
+        if k == 6:                                           # top_k = E: the full softmax
+            full = np.exp(L - L.max(1, keepdims=True)); full /= full.sum(1, keepdims=True)
+            assert np.allclose(np.take_along_axis(full, ids.astype(np.int64), 1), w, rtol=1e-13)
+    assert list(O.topk_route(L, 3, True)[0][0]) == [1, 2, 4]
+    ids, w = O.topk_route(L, 2, False)
+    full = np.exp(L) / np.exp(L).sum(1, keepdims=True)
+    assert np.allclose(w, np.take_along_axis(full, ids.astype(np.int64), 1), rtol=1e-12)
+
+
+def test_permute_bruteforce_stable():
+    rng = np.random.default_rng(2)
+    for E, T, k in ((5, 7, 2), (8, 1, 8), (3, 10, 1), (16, 9, 4)):
+        ids = np.stack([rng.choice(E, k, replace=False) for _ in range(T)]).astype(np.int32)
+        off, slots = O.permute(ids, E)
+        flat = ids.reshape(-1)
+        ref = sorted(range(T * k), key=lambda s: (flat[s], s))
+        assert list(slots) == ref
+        for e in range(E):
+            assert off[e + 1] - off[e] == int((flat == e).sum())
+        assert off[0] == 0 and off[E] == T * k
+
+
+# ----------------------------------------------------------------- GEMM / forward
+def _deq_py(fmt, packed, scale, N, K):
+    """Pure-Python decode (bit fields + tables), independent of the oracle's."""
+    tab = O.nf4_codebook() if fmt == O.FMT_NF4 else O.e2m1_values()
+    out = [[0.0] * K for _ in range(N)]
+    for n in range(N):
+        for k in range(K):
+            byte = int(packed[n, k // 2])
+            if fmt == O.FMT_NF4:
+                code = (byte >> 4) if k % 2 == 0 else (byte & 15)
+                out[n][k] = float(np.float32(tab[code]) * np.float32(scale[n, k // 64]))
+            else:
+                code = (byte & 15) if k % 2 == 0 else (byte >> 4)
+                out[n][k] = float(tab[code]) * 2.0 ** (int(scale[n, k // 32]) - 127)
+    return out
+
+
+@pytest.mark.parametrize("fmt", [O.FMT_NF4, O.FMT_MXFP4])
+def test_grouped_gemm_triple_loop(fmt):
+    rng = np.random.default_rng(4)
+    E, N, K = 3, 5, 128
+    Wf = rng.standard_normal((E, N, K)).astype(np.float32) * np.float32(0.02)
+    qs = [O.quantize(fmt, Wf[e]) for e in range(E)]
+    Bp = np.stack([q[0] for q in qs]); Bs = np.stack([q[1] for q in qs])
+    a = rng.standard_normal((6, K))
+    row_of = np.array([5, 0, 2, 2, 1])
+    off, gexp = [0, 2, 2, 5], [2, 0, 1]
+    c = O.grouped_gemm(a, row_of, fmt, Bp, Bs, N, K, off, gexp)
+    Wd = [_deq_py(fmt, Bp[e], Bs[e], N, K) for e in range(E)]
+    for g in range(3):
+        for r in range(off[g], off[g + 1]):
+            for n in range(N):
+                ref = math.fsum(a[row_of[r], kk] * Wd[gexp[g]][n][kk] for kk in range(K))
+                assert abs(c[r, n] - ref) <= 1e-12 * (1 + abs(ref))
+
+
+def test_unit_vector_picks_column():
+    rng = np.random.default_rng(8)
+    Wf = rng.standard_normal((1, 6, 64)).astype(np.float32)
+    p, s = O.nf4_quantize(Wf[0])
+    a = np.zeros((1, 64)); a[0, 17] = 1.0
+    c = O.grouped_gemm(a, None, O.FMT_NF4, p[None], s[None], 6, 64, [0, 1])
+    assert np.array_equal(c[0], O.nf4_dequantize(p, s, 6, 64)[:, 17].astype(np.float64))
+
+
+def test_swiglu_closed_forms():
+    g = np.array([0.0, 1.0, -2.0, 30.0]); u = np.array([3.0, 0.0, 1.0, 2.0])
+    h = O.swiglu(g, u)
+    assert h[0] == 0.0 and h[1] == 0.0
+    assert abs(h[2] - (-2.0 / (1 + math.exp(2.0)))) < 1e-15
+    assert abs(h[3] - 60.0) < 1e-9
+
+
+def _forward_py(layer, xb):
+    """Pure-Python forward on tiny shapes: loops, math.exp, no numpy algebra."""
+    fmt, E, H, I, k = layer["fmt"], layer["E"], layer["H"], layer["I"], layer["top_k"]
+    W13 = [_deq_py(fmt, layer["w13"][e], layer["w13_scale"][e], 2 * I, H) for e in range(E)]
+    W2 = [_deq_py(fmt, layer["w2"][e], layer["w2_scale"][e], H, I) for e in range(E)]
+    out = []
+    for t in range(xb.shape[0]):
+        x = [float(np.array([int(v) << 16], np.uint32).view(np.float32)[0]) for v in xb[t]]
+        L = [math.fsum(x[h] * float(layer["router_w"][e, h]) for h in range(H)) for e in range(E)]
+        order = sorted(range(E), key=lambda e: (-L[e], e))[:k]
+        ex = [math.exp(L[e] - L[order[0]]) for e in order]
+        ws = [v / math.fsum(ex) for v in ex]
+        o = [0.0] * H
+        for wj, e in zip(ws, order):
+            gu = [math.fsum(x[h] * W13[e][n][h] for h in range(H)) for n in range(2 * I)]
+            hh = [gu[i] / (1 + math.exp(-gu[i])) * gu[I + i] for i in range(I)]
+            for n in range(H):
+                o[n] += wj * math.fsum(hh[i] * W2[e][n][i] for i in range(I))
+        out.append(o)
+    return np.array(out)
+
+
+@pytest.mark.parametrize("fmt", [O.FMT_NF4, O.FMT_MXFP4])
+def test_moe_forward_bruteforce(fmt):
+    wl = S.custom(E=4, top_k=2, H=64, I=64, fmt=fmt)
+    W_r, _ = S.make_router(wl)
+    layer = dict(fmt=fmt, E=4, H=64, I=64, top_k=2, renormalize=1, router_w=W_r, router_b=None)
+    w13 = S.make_stack(wl, 0, "w13"); w2 = S.make_stack(wl, 0, "w2")
+    q13 = [O.quantize(fmt, w13[e]) for e in range(4)]
+    q2 = [O.quantize(fmt, w2[e]) for e in range(4)]
+    layer["w13"] = np.stack([q[0] for q in q13]); layer["w13_scale"] = np.stack([q[1] for q in q13])
+    layer["w2"] = np.stack([q[0] for q in q2]); layer["w2_scale"] = np.stack([q[1] for q in q2])
+    xb = S.make_x(wl, 3)
+    out = O.moe_forward(layer, xb)
+    ref = _forward_py(layer, xb)
+    assert np.allclose(out, ref, rtol=1e-10, atol=1e-14)
+
+
+def test_moe_forward_single_expert_k1_closed_form():
+    """k = 1 with one expert: out = y (routing weight exactly 1)."""
+    wl = S.custom(E=1, top_k=1, H=64, I=64)
+    W_r, _ = S.make_router(wl)
+    w13, w2 = S.make_stack(wl, 0, "w13")[0], S.make_stack(wl, 0, "w2")[0]
+    p13, s13 = O.nf4_quantize(w13); p2, s2 = O.nf4_quantize(w2)
+    layer = dict(fmt=0, E=1, H=64, I=64, top_k=1, renormalize=1, router_w=W_r, router_b=None,
+                 w13=p13[None], w13_scale=s13[None], w2=p2[None], w2_scale=s2[None])
+    xb = S.make_x(wl, 2)
+    x = O.bf16_bits_to_f64(xb)
+    W13 = O.nf4_dequantize(p13, s13, 128, 64).astype(np.float64)
+    W2 = O.nf4_dequantize(p2, s2, 64, 64).astype(np.float64)
+    gu = x @ W13.T
+    h = gu[:, :64] / (1 + np.exp(-gu[:, :64])) * gu[:, 64:]
+    assert np.allclose(O.moe_forward(layer, xb), h @ W2.T, rtol=1e-12, atol=0)
+
+
+def test_gate_up_halves_matter():
+    """Swapping the gate and up halves changes the output (gate = rows [0, I))."""
+    wl = S.custom(E=2, top_k=1, H=64, I=64)
+    W_r, _ = S.make_router(wl)
+    w13, w2 = S.make_stack(wl, 0, "w13"), S.make_stack(wl, 0, "w2")
+    def build(stack13):
+        q13 = [O.nf4_quantize(stack13[e]) for e in range(2)]; q2 = [O.nf4_quantize(w2[e]) for e in range(2)]
+        return dict(fmt=0, E=2, H=64, I=64, top_k=1, renormalize=1, router_w=W_r, router_b=None,
+                    w13=np.stack([q[0] for q in q13]), w13_scale=np.stack([q[1] for q in q13]),
+                    w2=np.stack([q[0] for q in q2]), w2_scale=np.stack([q[1] for q in q2]))
+    xb = S.make_x(wl, 2)
+    a = O.moe_forward(build(w13), xb)
+    b = O.moe_forward(build(np.concatenate([w13[:, 64:], w13[:, :64]], axis=1)), xb)
+    assert not np.allclose(a, b)
