@@ -1,0 +1,279 @@
+#!/usr/bin/env python3
+"""Benchmark of the routed MoE layer on 4-bit packed weights, one MI355X.
+
+One step = one MoE-layer forward (router, top-k, grouping, gate_up + SwiGLU,
+down, weighted combine) over one batch of T synthetic tokens, on the next of
+`layers` independently seeded layers (rotated so the weights are not
+cache-resident). Prints ONE JSON line.
+
+Default workload: OLMoE-1B-7B-shaped decode, E=64, top_k=8, H=2048, I=1024,
+T=1, NF4 blocksize 64, 64 layers.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+METRIC = "MoE-layer tokens/s + effective packed-weight HBM GB/s (decode T=1, prefill)"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=None)
+    ap.add_argument("--workload", default="olmoe_decode",
+                    choices=["olmoe_decode", "olmoe_prefill", "qwen3_zipf", "gptoss_mxfp4", "tiny"])
+    ap.add_argument("--tokens", type=int, default=None, help="T per step (workload default if unset)")
+    ap.add_argument("--layers", type=int, default=None)
+    ap.add_argument("--path", default="auto", choices=["auto", "small", "mfma"])
+    ap.add_argument("--graph", type=int, default=1, help="1: time HIP-graph replays as well")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def packed_bytes_per_expert(wl):
+    """Algorithmic bytes of one expert: codes + scales of gate_up and down."""
+    blk = 64 if wl.fmt == 0 else 32
+    sbytes = 4 if wl.fmt == 0 else 1
+    g = 2 * wl.I * (wl.H // 2 + (wl.H // blk) * sbytes)
+    d = wl.H * (wl.I // 2 + (wl.I // blk) * sbytes)
+    return g, d
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE={world}); "
+              "this build has no multi-GPU path.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import moe_synth as S
+    import bit_quantized_moe_expert_amd as M
+
+    wl = S.WORKLOADS[args.workload]
+    T = args.tokens or wl.tokens[0]
+    nlayers = args.layers or wl.layers
+    path = {"auto": M.PATH_AUTO, "small": M.PATH_SMALL_M, "mfma": M.PATH_MFMA}[args.path]
+    steps = args.steps or (nlayers * 20 if T <= 16 else nlayers * 4)
+    warmup = args.warmup if args.warmup is not None else min(steps, nlayers * 2)
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    print(f"[bench] {wl.name} T={T} layers={nlayers} steps={steps} warmup={warmup}", file=sys.stderr,
+          flush=True)
+
+    # ---- inputs: weights drawn on the device and quantized by the library (untimed)
+    layers, xs = [], []
+    t0 = time.time()
+    for l in range(nlayers):
+        W_r, b_r = S.make_router(wl, l)
+        w13 = S.make_stack_torch(wl, l, "w13", dev)
+        p13, s13 = M.quantize(w13, wl.fmt)
+        del w13
+        w2 = S.make_stack_torch(wl, l, "w2", dev)
+        p2, s2 = M.quantize(w2, wl.fmt)
+        del w2
+        layers.append(M.MoELayer(
+            fmt=wl.fmt, E=wl.E, H=wl.H, I=wl.I, top_k=wl.top_k, w13=p13, w13_scale=s13, w2=p2,
+            w2_scale=s2, router_w=torch.from_numpy(W_r).to(dev),
+            router_b=None if b_r is None else torch.from_numpy(b_r).to(dev),
+            renormalize=wl.renormalize, path=path))
+        xb = S.make_x(wl, T, l)
+        xs.append(torch.from_numpy(xb.view(np.int16)).to(dev).view(torch.bfloat16))
+    torch.cuda.synchronize()
+    print(f"[bench] setup {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+
+    fwd = M.Forward(layers[0], T, dev)
+    structs = [lay.struct() for lay in layers]
+    out = torch.empty(T, wl.H, dtype=torch.bfloat16, device=dev)
+    L = M.lib()
+    import ctypes
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    xptr = [ctypes.c_void_p(x.data_ptr()) for x in xs]
+    optr = ctypes.c_void_p(out.data_ptr())
+    srefs = [ctypes.byref(s) for s in structs]
+
+    def step(i):
+        st = L.nf4moe_moe_forward(srefs[i % nlayers], xptr[i % nlayers], T, optr, None, None,
+                                  fwd.wsp, fwd.nb, sp)
+        if st != 0:
+            M._check(st)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # ---- timed region (eager)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(steps):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    eager_ms = e0.elapsed_time(e1) / steps
+
+    # ---- HIP graph of one rotation over all layers, replayed
+    graph_ms = None
+    if args.graph:
+        try:
+            g = torch.cuda.CUDAGraph()
+            cs = torch.cuda.Stream()
+            cs.wait_stream(stream)
+            with torch.cuda.stream(cs):
+                csp = ctypes.c_void_p(cs.cuda_stream)
+                with torch.cuda.graph(g, stream=cs):
+                    for i in range(nlayers):
+                        st = L.nf4moe_moe_forward(srefs[i], xptr[i], T, optr, None, None, fwd.wsp,
+                                                  fwd.nb, ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+                        if st != 0:
+                            M._check(st)
+            torch.cuda.synchronize()
+            reps = max(1, steps // nlayers)
+            g.replay()
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for _ in range(reps):
+                g.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            graph_ms = e0.elapsed_time(e1) / (reps * nlayers)
+        except Exception as ex:  # graph capture is optional for the line
+            print(f"[bench] graph capture skipped: {ex}", file=sys.stderr, flush=True)
+
+    # ---- dominant kernel (gate_up + SwiGLU): HIP events around its launch on the same stream
+    prof_steps = min(steps, 8 * nlayers)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(prof_steps)]
+    for row in evs:
+        for ev in row:
+            ev.record(stream)
+    torch.cuda.synchronize()
+    for i in range(prof_steps):
+        fwd.set_layer(layers[i % nlayers])
+        fwd.profiled(xs[i % nlayers], out, [ev.cuda_event for ev in evs[i]])
+    torch.cuda.synchronize()
+    stage = np.array([[r[0].elapsed_time(r[1]), r[1].elapsed_time(r[2]), r[2].elapsed_time(r[3])]
+                      for r in evs])
+    route_ms, gate_ms, down_ms = (float(v) for v in np.median(stage, axis=0))
+    gate_mean_ms = float(np.mean(stage[:, 1]))
+
+    # ---- work per step
+    g_b, d_b = packed_bytes_per_expert(wl)
+    R = T * wl.top_k
+    # experts actually active per step, from the routing of every layer
+    act = []
+    for i in range(nlayers):
+        ids = torch.empty(T, wl.top_k, dtype=torch.int32, device=dev)
+        fwd.set_layer(layers[i])
+        fwd(xs[i], out=out, topk_ids=ids)
+        act.append(int(torch.unique(ids).numel()))
+    active = float(np.mean(act))
+    step_bytes = active * (g_b + d_b)
+    flops = 6.0 * R * wl.H * wl.I
+    ms = graph_ms if graph_ms is not None else eager_ms
+    value = T / (ms * 1e-3)
+    small = (path == M.PATH_SMALL_M) or (path == M.PATH_AUTO and R <= 64)
+    if small:
+        gate_bytes = active * g_b
+        roof = {"bound": "hbm", "achieved": gate_bytes / (gate_mean_ms * 1e-3) / 1e9,
+                "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+    else:
+        gate_flops = 4.0 * R * wl.H * wl.I
+        roof = {"bound": "mfma", "achieved": gate_flops / (gate_mean_ms * 1e-3) / 1e12,
+                "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = None
+    roof["kernel"] = "k_gemv<SwiGLU> (gate_up)" if small else "k_mfma<SwiGLU> (gate_up)"
+    roof["kernel_ms_mean"] = gate_mean_ms
+
+    # ---- CPU baseline: the fp64 oracle on a bounded sample of the same workload
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wl, T, layers, xs, dev, args.cpu_seconds)
+
+    line = {
+        "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": steps,
+        "warmup": warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32" if small else "bf16",
+        "data": "synthetic (seeded N(0,1) activations, N(0,0.02) weights quantized on device)",
+        "config": {"workload": wl.name, "format": "nf4_b64" if wl.fmt == 0 else "mxfp4_b32",
+                   "E": wl.E, "top_k": wl.top_k, "H": wl.H, "I": wl.I, "T": T, "layers": nlayers,
+                   "path": "small_m" if small else "mfma", "timing": "hip_graph" if graph_ms else "eager"},
+        "eager_ms_per_step": eager_ms, "graph_ms_per_step": graph_ms,
+        "effective_packed_GBps": step_bytes / (ms * 1e-3) / 1e9,
+        "algorithmic_TFLOPs": flops / (ms * 1e-3) / 1e12,
+        "active_experts_per_step": active,
+        "stage_ms_median": {"route": route_ms, "gate_up": gate_ms, "down_combine": down_ms},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(wl, T, layers, xs, dev, seconds):
+    """Time oracle.moe_forward (fp64, numpy) on host cores for a bounded sample:
+    whole layer calls of this workload, one token batch each, until `seconds`."""
+    import numpy as np
+    import torch
+    import moe_synth as S
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:  # pragma: no cover
+        threadpool_limits = None
+    cores = 1
+    total, calls, toks = 0.0, 0, 0
+    ctx = threadpool_limits(limits=cores) if threadpool_limits else None
+    try:
+        l = 0
+        while total < seconds and l < len(layers):
+            W_r, b_r = S.make_router(wl, l)
+            xb = S.make_x(wl, T, l)
+            Tc = min(T, 16)                                     # bounded token sample per call
+            xb = xb[:Tc]
+            L64 = O.router_logits(xb, W_r, b_r)
+            ids, _ = O.topk_route(L64, wl.top_k, bool(wl.renormalize))
+            need = sorted(set(ids.reshape(-1).tolist()))
+            w13 = S.make_stack_torch(wl, l, "w13", dev)
+            w2 = S.make_stack_torch(wl, l, "w2", dev)
+            E = wl.E
+            q13 = {e: O.quantize(wl.fmt, w13[e].cpu().numpy()) for e in need}
+            q2 = {e: O.quantize(wl.fmt, w2[e].cpu().numpy()) for e in need}
+            del w13, w2
+            torch.cuda.empty_cache()
+
+            class Pick:
+                def __init__(self, q, i):
+                    self.q, self.i = q, i
+
+                def __getitem__(self, e):
+                    return self.q[int(e)][self.i]
+            layer = dict(fmt=wl.fmt, E=E, H=wl.H, I=wl.I, top_k=wl.top_k, renormalize=wl.renormalize,
+                         w13=Pick(q13, 0), w13_scale=Pick(q13, 1), w2=Pick(q2, 0), w2_scale=Pick(q2, 1),
+                         router_w=W_r, router_b=b_r)
+            t = time.perf_counter()
+            O.moe_forward(layer, xb)
+            total += time.perf_counter() - t
+            calls += 1
+            toks += Tc
+            l += 1
+    finally:
+        if ctx is not None:
+            ctx.__exit__(None, None, None)
+    return {"value": toks / total, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{calls} layer calls of {min(T, 16)} token(s) each ({wl.name}), "
+                      f"{total:.1f}s of fp64 numpy on 1 host thread; quantization untimed"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,81 @@
+// Host-side declarations shared by the C ABI layer and the kernel files.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace nf4moe {
+
+constexpr int kChunk = 256;        // routed slots per grouping workgroup
+constexpr int kMfmaBM = 128;       // rows (tokens) per MFMA tile
+constexpr int kMaxTopK = 32;
+constexpr int kMaxE = 1024;
+
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline size_t align_up(size_t v, size_t a = 256) { return (v + a - 1) / a * a; }
+
+// Routing results and grouping scratch, all device memory.
+struct RouteBufs {
+  int32_t *topk_ids = nullptr;   // [T, k]
+  float *topk_w = nullptr;       // [T, k]
+  int32_t *expert_offsets = nullptr;  // [E + 1]
+  int32_t *sorted_slots = nullptr;    // [R]
+  int32_t *slot_pos = nullptr;        // [R] inverse of sorted_slots
+  int32_t *chunk_hist = nullptr;      // [E, nchunks] expert-major
+  int32_t *grp_expert = nullptr;      // [max groups] compacted non-empty groups
+  int32_t *grp_row0 = nullptr;
+  int32_t *grp_rows = nullptr;
+  int32_t *counters = nullptr;        // [0] groups, [1] tiles
+  int4 *tiles = nullptr;              // [max tiles] (expert, row0, rows, 0)
+};
+
+hipError_t launch_quantize(int fmt, const float *w, int64_t rows, int64_t K, uint8_t *packed,
+                           void *scale, hipStream_t s);
+hipError_t launch_dequantize(int fmt, const uint8_t *packed, const void *scale, int64_t rows,
+                             int64_t K, float *out, hipStream_t s);
+
+hipError_t launch_router_logits(const uint16_t *x, int T, int H, const float *W, const float *b,
+                                int E, float *logits, hipStream_t s);
+// top-k + softmax, then grouping. Fills every RouteBufs field.
+hipError_t launch_route(const float *logits, int T, int E, int k, int renorm, const RouteBufs &rb,
+                        int bm, hipStream_t s);
+// Fill n int32 with v (a kernel, so the sequence stays graph-capturable).
+hipError_t launch_fill_i32(int32_t *p, int n, int v, hipStream_t s);
+// Groups and tiles from caller-given group offsets / experts.
+hipError_t launch_groups_from_offsets(const int32_t *goff, const int32_t *gexp, int G, int R,
+                                      int E, const RouteBufs &rb, int bm, hipStream_t s);
+
+// Small-M (bandwidth-bound) kernels.
+enum Epi { EPI_SWIGLU = 0, EPI_PLAIN_F32 = 1, EPI_PLAIN_BF16 = 2, EPI_SLOT = 3 };
+struct GemmArgs {
+  int fmt;
+  const void *a;            // bf16 [*, K] (a_is_f32 = 0) or fp32 [*, K]
+  int a_is_f32;
+  const int32_t *a_row_of;  // row r reads a[a_row_of[r]] or, with a_div > 1, a[a_row_of[r] / a_div]
+  int a_div;
+  const uint8_t *B;         // [E, N, K/2]
+  const void *B_scale;
+  int64_t N, K;             // N = weight rows (2I for SwiGLU), K
+  int R;                    // rows of the routed problem
+  const int32_t *grp_expert, *grp_row0, *grp_rows, *n_grp;  // device group list
+  int max_grp;
+  const int4 *tiles;        // MFMA path
+  const int32_t *n_tiles;
+  int max_tiles;
+  int epi;
+  void *c;                  // SwiGLU: fp32 [R, N/2]; plain: [R, N]; slot: fp32 [R_slots, N]
+  const int32_t *slot_of;   // EPI_SLOT: row r -> slot
+  const float *slot_w;      // EPI_SLOT: weight of slot
+};
+hipError_t launch_gemv_grouped(const GemmArgs &g, int ms_hint, hipStream_t s);
+hipError_t launch_mfma_grouped(const GemmArgs &g, hipStream_t s);
+
+// Token-centric down projection + combine for a handful of tokens.
+hipError_t launch_gemv_down_combine(int fmt, const float *h, const int32_t *slot_pos,
+                                    const int32_t *topk_ids, const float *topk_w, int T, int k,
+                                    const uint8_t *w2, const void *w2_scale, int H, int I,
+                                    uint16_t *out, hipStream_t s);
+// out[t] = bf16(sum_j slotbuf[t*k + j]) in j order.
+hipError_t launch_combine(const float *slotbuf, int T, int k, int H, uint16_t *out, hipStream_t s);
+
+}  // namespace nf4moe

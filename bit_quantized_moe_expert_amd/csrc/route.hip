@@ -1,0 +1,439 @@
+// Routing on the device: router logits, top-k + softmax, and the stable
+// grouping of routed slots by expert (histogram, one flat scan, scatter), plus
+// the group and tile tables the grouped GEMMs read. No host synchronisation.
+//
+// The pages keep this upstream of the kernel (page "How do I run a grouped GEMM
+// directly on NF4 packed MoE expert weights ...", section "Why it happens":
+// tokens are sorted by expert and scattered back outside the kernel; the
+// kernel takes a_cat sorted by expert with sizes + expert_ids). Here it is the
+// library's own first stage. Integer results are exact: a slot's position is
+// the number of slots routed to lower experts plus the number of earlier slots
+// routed to its own expert.
+#include <limits.h>
+
+#include "common.h"
+#include "internal.h"
+
+namespace nf4moe {
+
+// ---------------------------------------------------------------------------
+// Router logits, few tokens: one workgroup per expert, threads stride over H.
+// ---------------------------------------------------------------------------
+template <int TMAX>
+__global__ __launch_bounds__(256) void k_logits_rows(const uint16_t *__restrict__ x, int T, int H,
+                                                     const float *__restrict__ W,
+                                                     const float *__restrict__ b, int E,
+                                                     float *__restrict__ L) {
+  const int e = blockIdx.x;
+  const float *w = W + (int64_t)e * H;
+  float acc[TMAX];
+#pragma unroll
+  for (int t = 0; t < TMAX; ++t) acc[t] = 0.0f;
+  for (int h = threadIdx.x * 8; h < H; h += 256 * 8) {
+    const float4 w0 = *reinterpret_cast<const float4 *>(w + h);
+    const float4 w1 = *reinterpret_cast<const float4 *>(w + h + 4);
+#pragma unroll
+    for (int t = 0; t < TMAX; ++t) {
+      if (t < T) {
+        const uint4 xv = *reinterpret_cast<const uint4 *>(x + (int64_t)t * H + h);
+        float a = acc[t];
+        a = fmaf(bf16lo_to_f32(xv.x), w0.x, a);
+        a = fmaf(bf16hi_to_f32(xv.x), w0.y, a);
+        a = fmaf(bf16lo_to_f32(xv.y), w0.z, a);
+        a = fmaf(bf16hi_to_f32(xv.y), w0.w, a);
+        a = fmaf(bf16lo_to_f32(xv.z), w1.x, a);
+        a = fmaf(bf16hi_to_f32(xv.z), w1.y, a);
+        a = fmaf(bf16lo_to_f32(xv.w), w1.z, a);
+        a = fmaf(bf16hi_to_f32(xv.w), w1.w, a);
+        acc[t] = a;
+      }
+    }
+  }
+  __shared__ float red[4][TMAX];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+#pragma unroll
+  for (int t = 0; t < TMAX; ++t) {
+    const float v = wave_sum(acc[t]);
+    if (lane == 0) red[wave][t] = v;
+  }
+  __syncthreads();
+  if (threadIdx.x < T) {
+    const int t = threadIdx.x;
+    float v = ((red[0][t] + red[1][t]) + red[2][t]) + red[3][t];
+    if (b) v += b[e];
+    L[(int64_t)t * E + e] = v;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Router logits, many tokens: 32 tokens x 64 experts per workgroup, H in
+// steps of 64 through LDS; each thread owns 2 tokens x 4 experts.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_logits_tiled(const uint16_t *__restrict__ x, int T, int H,
+                                                      const float *__restrict__ W,
+                                                      const float *__restrict__ b, int E,
+                                                      float *__restrict__ L) {
+  __shared__ float xs[64][33];
+  __shared__ float ws[64][65];
+  const int tid = threadIdx.x;
+  const int t0 = blockIdx.x * 32, e0 = blockIdx.y * 64;
+  const int ty = tid >> 4, tx = tid & 15;
+  float acc[2][4] = {};
+  for (int h0 = 0; h0 < H; h0 += 64) {
+    {  // x: 32 tokens x 64 h, 8 bf16 per thread
+      const int tt = tid >> 3, hh = (tid & 7) * 8;
+      const int t = t0 + tt, h = h0 + hh;
+      uint4 xv = make_uint4(0, 0, 0, 0);
+      if (t < T && h < H) xv = *reinterpret_cast<const uint4 *>(x + (int64_t)t * H + h);
+      xs[hh + 0][tt] = bf16lo_to_f32(xv.x);
+      xs[hh + 1][tt] = bf16hi_to_f32(xv.x);
+      xs[hh + 2][tt] = bf16lo_to_f32(xv.y);
+      xs[hh + 3][tt] = bf16hi_to_f32(xv.y);
+      xs[hh + 4][tt] = bf16lo_to_f32(xv.z);
+      xs[hh + 5][tt] = bf16hi_to_f32(xv.z);
+      xs[hh + 6][tt] = bf16lo_to_f32(xv.w);
+      xs[hh + 7][tt] = bf16hi_to_f32(xv.w);
+    }
+    {  // W: 64 experts x 64 h, 16 fp32 per thread
+      const int ee = tid >> 2, hh = (tid & 3) * 16;
+      const int e = e0 + ee;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int h = h0 + hh + 4 * q;
+        float4 wv = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (e < E && h < H) wv = *reinterpret_cast<const float4 *>(W + (int64_t)e * H + h);
+        ws[hh + 4 * q + 0][ee] = wv.x;
+        ws[hh + 4 * q + 1][ee] = wv.y;
+        ws[hh + 4 * q + 2][ee] = wv.z;
+        ws[hh + 4 * q + 3][ee] = wv.w;
+      }
+    }
+    __syncthreads();
+#pragma unroll 8
+    for (int hh = 0; hh < 64; ++hh) {
+      const float xa0 = xs[hh][ty * 2], xa1 = xs[hh][ty * 2 + 1];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float wv = ws[hh][tx * 4 + q];
+        acc[0][q] = fmaf(xa0, wv, acc[0][q]);
+        acc[1][q] = fmaf(xa1, wv, acc[1][q]);
+      }
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int t = t0 + ty * 2 + i;
+    if (t >= T) continue;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int e = e0 + tx * 4 + q;
+      if (e < E) L[(int64_t)t * E + e] = acc[i][q] + (b ? b[e] : 0.0f);
+    }
+  }
+}
+
+hipError_t launch_router_logits(const uint16_t *x, int T, int H, const float *W, const float *b,
+                                int E, float *logits, hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  if (T <= 8) {
+    hipLaunchKernelGGL(k_logits_rows<8>, dim3(E), dim3(256), 0, s, x, T, H, W, b, E, logits);
+  } else {
+    hipLaunchKernelGGL(k_logits_tiled, dim3((unsigned)cdiv(T, 32), (unsigned)cdiv(E, 64)),
+                       dim3(256), 0, s, x, T, H, W, b, E, logits);
+  }
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// top-k + softmax: one wave per token. Lane l holds the logits of experts
+// l, l + 64, ...; k rounds of a wave-wide argmax under the order (logit
+// descending, id ascending); lane j keeps the j-th pick.
+// ---------------------------------------------------------------------------
+template <int EPL>
+__global__ __launch_bounds__(256) void k_topk(const float *__restrict__ L, int T, int E, int k,
+                                              int renorm, int32_t *__restrict__ ids,
+                                              float *__restrict__ wts) {
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const int lane = threadIdx.x & 63;
+  constexpr int kNone = INT_MAX;
+  float v[EPL];
+#pragma unroll
+  for (int j = 0; j < EPL; ++j) {
+    const int e = lane + 64 * j;
+    v[j] = e < E ? L[(int64_t)t * E + e] : -__builtin_inff();
+  }
+  uint32_t taken = 0;
+  int my_id = 0;
+  float my_v = 0.0f;
+  for (int i = 0; i < k; ++i) {
+    float bv = -__builtin_inff();
+    int bid = kNone;
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) {
+      const int e = lane + 64 * j;
+      if (e < E && !((taken >> j) & 1u)) {
+        if (bid == kNone || v[j] > bv || (v[j] == bv && e < bid)) {
+          bv = v[j];
+          bid = e;
+        }
+      }
+    }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) {
+      const float ov = __shfl_xor(bv, m, kWave);
+      const int oid = __shfl_xor(bid, m, kWave);
+      if (oid != kNone && (bid == kNone || ov > bv || (ov == bv && oid < bid))) {
+        bv = ov;
+        bid = oid;
+      }
+    }
+    if ((bid & 63) == lane) taken |= 1u << (bid >> 6);
+    if (lane == i) {
+      my_id = bid;
+      my_v = bv;
+    }
+  }
+  const float v0 = __shfl(my_v, 0, kWave);  // the largest logit
+  float wgt;
+  if (renorm) {
+    const float ex = lane < k ? expf(my_v - v0) : 0.0f;
+    wgt = ex / wave_sum(ex);
+  } else {
+    float part = 0.0f;
+#pragma unroll
+    for (int j = 0; j < EPL; ++j)
+      if (lane + 64 * j < E) part += expf(v[j] - v0);
+    wgt = expf(my_v - v0) / wave_sum(part);
+  }
+  if (lane < k) {
+    ids[(int64_t)t * k + lane] = my_id;
+    wts[(int64_t)t * k + lane] = wgt;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Grouping, stage 1: per-chunk expert histogram, stored expert-major
+// hist[e * nchunks + c], so one flat exclusive scan of hist gives, at (e, c),
+// the first sorted position of chunk c's slots routed to expert e.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_group_hist(const int32_t *__restrict__ ids, int R, int E,
+                                                    int nchunks, int32_t *__restrict__ hist) {
+  __shared__ int cnt[kMaxE];
+  for (int e = threadIdx.x; e < E; e += 256) cnt[e] = 0;
+  __syncthreads();
+  const int s = blockIdx.x * kChunk + threadIdx.x;
+  if (s < R) atomicAdd(&cnt[ids[s]], 1);
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += 256) hist[(int64_t)e * nchunks + blockIdx.x] = cnt[e];
+}
+
+// Exclusive scan of one value per thread across a 1024-thread block; *total
+// (shared memory) receives the block total. Every thread must call it.
+__device__ inline int block_scan_1024(int v, int *total) {
+  __shared__ int wsum[16];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int inc = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int o = __shfl_up(inc, d, kWave);
+    if (lane >= d) inc += o;
+  }
+  if (lane == 63) wsum[wave] = inc;
+  __syncthreads();
+  if (wave == 0) {
+    const int w = lane < 16 ? wsum[lane] : 0;
+    int wi = w;
+#pragma unroll
+    for (int d = 1; d < 16; d <<= 1) {
+      const int o = __shfl_up(wi, d, kWave);
+      if (lane >= d) wi += o;
+    }
+    if (lane < 16) wsum[lane] = wi - w;  // exclusive offset of each wave
+    if (lane == 15) *total = wi;
+  }
+  __syncthreads();
+  const int ex = wsum[wave] + inc - v;
+  __syncthreads();  // wsum is reused by the next call
+  return ex;
+}
+
+// Tiles of at most bm rows for every group; single workgroup of 1024 threads.
+__device__ void build_tiles(const int32_t *grp_expert, const int32_t *grp_row0,
+                            const int32_t *grp_rows, int n_grp, int bm, int4 *tiles,
+                            int32_t *n_tiles_out) {
+  __shared__ int s_total;
+  __shared__ int s_carry;
+  if (threadIdx.x == 0) s_carry = 0;
+  __syncthreads();
+  for (int g0 = 0; g0 < n_grp; g0 += 1024) {
+    const int g = g0 + threadIdx.x;
+    const int rows = g < n_grp ? grp_rows[g] : 0;
+    const int nt = (rows + bm - 1) / bm;
+    const int ex = block_scan_1024(nt, &s_total);
+    const int base = s_carry + ex;
+    for (int i = 0; i < nt; ++i) {
+      const int r0 = i * bm;
+      tiles[base + i] = make_int4(grp_expert[g], grp_row0[g] + r0, min(bm, rows - r0), 0);
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) s_carry += s_total;
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) *n_tiles_out = s_carry;
+}
+
+// Grouping, stage 2 (single workgroup): flat exclusive scan of the histogram,
+// expert offsets, the compacted list of non-empty experts, and the MFMA tiles.
+__global__ __launch_bounds__(1024) void k_group_scan(int32_t *__restrict__ hist, int E, int nchunks,
+                                                     int R, int bm, int32_t *__restrict__ off,
+                                                     int32_t *__restrict__ grp_expert,
+                                                     int32_t *__restrict__ grp_row0,
+                                                     int32_t *__restrict__ grp_rows,
+                                                     int32_t *__restrict__ counters,
+                                                     int4 *__restrict__ tiles) {
+  __shared__ int s_total;
+  const int64_t n = (int64_t)E * nchunks;
+  const int64_t per = (n + 1023) / 1024;
+  const int64_t i0 = per * threadIdx.x, i1 = min(n, i0 + per);
+  int sum = 0;
+  for (int64_t i = i0; i < i1; ++i) sum += hist[i];
+  int run = block_scan_1024(sum, &s_total);
+  for (int64_t i = i0; i < i1; ++i) {
+    const int v = hist[i];
+    hist[i] = run;
+    run += v;
+  }
+  __syncthreads();
+  // expert offsets and the compacted non-empty experts (ascending id)
+  int cnt_total = 0;
+  for (int e0 = 0; e0 < E; e0 += 1024) {
+    const int e = e0 + threadIdx.x;
+    int o = 0, c = 0;
+    if (e < E) {
+      o = hist[(int64_t)e * nchunks];
+      c = (e + 1 < E ? hist[(int64_t)(e + 1) * nchunks] : R) - o;
+      off[e] = o;
+    }
+    const int slot = block_scan_1024(c > 0 ? 1 : 0, &s_total);
+    if (c > 0) {
+      grp_expert[cnt_total + slot] = e;
+      grp_row0[cnt_total + slot] = o;
+      grp_rows[cnt_total + slot] = c;
+    }
+    cnt_total += s_total;
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    off[E] = R;
+    counters[0] = cnt_total;
+  }
+  __syncthreads();
+  build_tiles(grp_expert, grp_row0, grp_rows, cnt_total, bm, tiles, counters + 1);
+}
+
+// Grouping, stage 3: stable scatter. Within a chunk, a slot's rank among equal
+// experts comes from a wave-wide match (one ballot per id bit) plus the counts
+// of the earlier waves of the chunk.
+__global__ __launch_bounds__(256) void k_group_scatter(const int32_t *__restrict__ ids, int R, int E,
+                                                       int nchunks,
+                                                       const int32_t *__restrict__ base,
+                                                       int32_t *__restrict__ sorted_slots,
+                                                       int32_t *__restrict__ slot_pos) {
+  __shared__ int cnt[4][kMaxE];
+  const int wave = threadIdx.x >> 6;
+  for (int i = threadIdx.x; i < 4 * E; i += 256) cnt[i / E][i % E] = 0;
+  __syncthreads();
+  const int s = blockIdx.x * kChunk + threadIdx.x;
+  const bool valid = s < R;
+  const int e = valid ? ids[s] : E;  // E: sentinel shared by the idle lanes
+  const int nbits = 32 - __clz(E);
+  uint64_t m = ~0ull;
+  for (int bit = 0; bit < nbits; ++bit) {
+    const int on = (e >> bit) & 1;
+    const uint64_t bal = __ballot(on);
+    m &= on ? bal : ~bal;
+  }
+  const int rank = __popcll(m & lanemask_lt());
+  if (valid && rank == 0) cnt[wave][e] = __popcll(m);
+  __syncthreads();
+  if (valid) {
+    int pos = base[(int64_t)e * nchunks + blockIdx.x] + rank;
+    for (int w = 0; w < wave; ++w) pos += cnt[w][e];
+    sorted_slots[pos] = s;
+    slot_pos[s] = pos;
+  }
+}
+
+hipError_t launch_route(const float *logits, int T, int E, int k, int renorm, const RouteBufs &rb,
+                        int bm, hipStream_t s) {
+  const int R = T * k;
+  const dim3 tk((unsigned)cdiv(T, 4));
+  if (E <= 64)
+    hipLaunchKernelGGL(k_topk<1>, tk, dim3(256), 0, s, logits, T, E, k, renorm, rb.topk_ids, rb.topk_w);
+  else if (E <= 128)
+    hipLaunchKernelGGL(k_topk<2>, tk, dim3(256), 0, s, logits, T, E, k, renorm, rb.topk_ids, rb.topk_w);
+  else if (E <= 256)
+    hipLaunchKernelGGL(k_topk<4>, tk, dim3(256), 0, s, logits, T, E, k, renorm, rb.topk_ids, rb.topk_w);
+  else if (E <= 512)
+    hipLaunchKernelGGL(k_topk<8>, tk, dim3(256), 0, s, logits, T, E, k, renorm, rb.topk_ids, rb.topk_w);
+  else
+    hipLaunchKernelGGL(k_topk<16>, tk, dim3(256), 0, s, logits, T, E, k, renorm, rb.topk_ids, rb.topk_w);
+  const int nchunks = (int)cdiv(R, kChunk);
+  hipLaunchKernelGGL(k_group_hist, dim3(nchunks), dim3(256), 0, s, rb.topk_ids, R, E, nchunks,
+                     rb.chunk_hist);
+  hipLaunchKernelGGL(k_group_scan, dim3(1), dim3(1024), 0, s, rb.chunk_hist, E, nchunks, R, bm,
+                     rb.expert_offsets, rb.grp_expert, rb.grp_row0, rb.grp_rows, rb.counters,
+                     rb.tiles);
+  hipLaunchKernelGGL(k_group_scatter, dim3(nchunks), dim3(256), 0, s, rb.topk_ids, R, E, nchunks,
+                     rb.chunk_hist, rb.sorted_slots, rb.slot_pos);
+  return hipGetLastError();
+}
+
+// Caller-given groups (the grouped GEMM entry point): group g = rows
+// [off[g], off[g+1]) with expert gexp[g] (or g). Offsets are clamped to [0, R]
+// and groups naming an expert outside [0, E) are treated as empty, so a bad
+// table cannot make a kernel read or write out of bounds.
+__global__ __launch_bounds__(1024) void k_groups_from_offsets(const int32_t *__restrict__ goff,
+                                                              const int32_t *__restrict__ gexp,
+                                                              int G, int R, int E, int bm,
+                                                              int32_t *__restrict__ grp_expert,
+                                                              int32_t *__restrict__ grp_row0,
+                                                              int32_t *__restrict__ grp_rows,
+                                                              int32_t *__restrict__ counters,
+                                                              int4 *__restrict__ tiles) {
+  for (int g = threadIdx.x; g < G; g += 1024) {
+    int a = goff[g], b = goff[g + 1];
+    a = min(max(a, 0), R);
+    b = min(max(b, a), R);
+    const int e = gexp ? gexp[g] : g;
+    const bool ok = e >= 0 && e < E;
+    grp_expert[g] = ok ? e : 0;
+    grp_row0[g] = a;
+    grp_rows[g] = ok ? b - a : 0;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) counters[0] = G;
+  build_tiles(grp_expert, grp_row0, grp_rows, G, bm, tiles, counters + 1);
+}
+
+__global__ void k_fill_i32(int32_t *p, int n, int v) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+hipError_t launch_fill_i32(int32_t *p, int n, int v, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_fill_i32, dim3((unsigned)cdiv(n, 256)), dim3(256), 0, s, p, n, v);
+  return hipGetLastError();
+}
+
+hipError_t launch_groups_from_offsets(const int32_t *goff, const int32_t *gexp, int G, int R,
+                                      int E, const RouteBufs &rb, int bm, hipStream_t s) {
+  hipLaunchKernelGGL(k_groups_from_offsets, dim3(1), dim3(1024), 0, s, goff, gexp, G, R, E, bm,
+                     rb.grp_expert, rb.grp_row0, rb.grp_rows, rb.counters, rb.tiles);
+  return hipGetLastError();
+}
+
+}  // namespace nf4moe

@@ -1,0 +1,215 @@
+/*
+ * nf4moe.h -- C ABI of libnf4moe.so: the routed Mixture-of-Experts expert layer
+ * computed directly on 4-bit packed weights, for AMD Instinct MI355X (gfx950).
+ *
+ * The operation is the one described on the page "How do I run a grouped GEMM
+ * directly on NF4 packed MoE expert weights, without dequantizing to bf16
+ * first?" (sections "Why it happens", "Smallest correct example", "Supported
+ * scope") and in the grouped-nf4-gemm PKG-INFO (intro, "Try it on CPU right
+ * now", "The MXFP4 native-byte lane"): one grouped GEMM over an expert-major
+ * stack of 4-bit codes, each code decoded through a 16-entry codebook in
+ * registers, block-scaled, accumulated in fp32, with no bf16 copy of any expert
+ * written to memory. This library also does the routing (router logits, top-k,
+ * grouping) and the router-weighted combine, so one call runs a whole layer.
+ *
+ * Conventions for every entry point
+ *  - Pointers marked "device" are HIP device memory owned by the caller. The
+ *    library allocates no device memory and keeps no state between calls; the
+ *    scratch an operation needs is a caller-provided workspace.
+ *  - stream: a hipStream_t (NULL = the null stream). All device work is
+ *    enqueued asynchronously on it; no call synchronises the host, so the
+ *    forward pass can be captured in a HIP graph.
+ *  - Every argument is validated on the host before anything is enqueued; on
+ *    an error nothing is enqueued, the status is returned and
+ *    nf4moe_last_error() (thread-local) describes it.
+ *  - Element offsets are computed in 64 bits everywhere, so expert stacks may
+ *    exceed 2 GiB (the pages' "Limitations": every expert-base offset int64).
+ *  - bf16 tensors are passed as uint16_t bit patterns.
+ *  - Device faults surface as NF4MOE_ERR_HIP at the caller's next stream
+ *    synchronisation; nothing is retried or recovered.
+ *
+ * Formats (the pages' layouts, "Supported scope" and "The MXFP4 native-byte lane")
+ *  NF4_B64   codes uint8 [.., N, K/2], two codes per byte, HIGH nibble = even k;
+ *            scales float32 absmax [.., N, K/64]; value = codebook[code] * absmax
+ *            rounded once to fp32. K % 64 == 0. The 16 codebook values are the
+ *            NormalFloat construction (see nf4moe_codebook).
+ *  MXFP4_B32 codes uint8 [.., N, K/2], LOW nibble = even k, OCP e2m1 values;
+ *            scales uint8 e8m0 [.., N, K/32]; value = e2m1(code) * 2^(e8m0-127),
+ *            e8m0 = 255 is NaN. K % 32 == 0.
+ */
+#ifndef NF4MOE_H
+#define NF4MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  NF4MOE_OK = 0,
+  NF4MOE_ERR_INVALID_ARG = 1, /* bad size, null or misaligned pointer, bad enum */
+  NF4MOE_ERR_UNSUPPORTED = 2, /* valid request outside what this build supports */
+  NF4MOE_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required     */
+  NF4MOE_ERR_HIP = 4          /* a HIP runtime call failed (launch, device query) */
+} nf4moe_status_t;
+
+typedef enum { NF4MOE_FMT_NF4_B64 = 0, NF4MOE_FMT_MXFP4_B32 = 1 } nf4moe_format_t;
+typedef enum { NF4MOE_DT_F32 = 0, NF4MOE_DT_BF16 = 1 } nf4moe_dtype_t;
+
+/* Which grouped-GEMM kernel family runs. AUTO picks from the routed row count
+ * known on the host (R = T * top_k): small R runs the bandwidth-bound decode
+ * kernels, large R the MFMA kernels. The other values force one family (for
+ * A/B measurement and tests); the result must satisfy the same tolerance. */
+typedef enum { NF4MOE_PATH_AUTO = 0, NF4MOE_PATH_SMALL_M = 1, NF4MOE_PATH_MFMA = 2 } nf4moe_path_t;
+
+/* One MoE layer. All pointers are device memory owned by the caller.
+ * The fused gate_up stack is [E, 2I, H] (rows [0, I) gate, [I, 2I) up) and the
+ * down stack [E, H, I] -- the experts4bit-qlora README's fused expert-stack
+ * convention ("Quickstart") -- each stored in `fmt`. */
+typedef struct {
+  nf4moe_format_t fmt;
+  int32_t E;           /* experts, 1..1024                                   */
+  int32_t H;           /* hidden size (K of gate_up, N of down)              */
+  int32_t I;           /* intermediate size (K of down)                      */
+  int32_t top_k;       /* experts per token, 1..min(E, 32)                   */
+  int32_t renormalize; /* 1: softmax over the k selected logits; 0: full softmax at the ids */
+  int32_t path;        /* nf4moe_path_t                                      */
+  const uint8_t *w13;  /* [E, 2I, H/2] codes                                  */
+  const void *w13_scale; /* NF4: float [E, 2I, H/64]; MXFP4: uint8 [E, 2I, H/32] */
+  const uint8_t *w2;   /* [E, H, I/2] codes                                   */
+  const void *w2_scale;  /* NF4: float [E, H, I/64];  MXFP4: uint8 [E, H, I/32]  */
+  const float *router_w; /* [E, H] fp32                                        */
+  const float *router_b; /* [E] fp32 added to the logits, or NULL              */
+} nf4moe_layer_t;
+
+/* ---------------------------------------------------------------------------
+ * nf4moe_quantize -- fp32 weights [rows, K] (device, row-major) -> packed codes
+ * [rows, K/2] + scales (device). Off the timed path.
+ * NF4 (grouped-nf4-gemm PKG-INFO, "Try it on CPU right now", block 1): absmax =
+ *   max |w| over each 64-block, stored fp32; code = the exact nearest codebook
+ *   value to w/absmax (decided by fp64 midpoint comparisons), ties to the lower
+ *   code; an all-zero block stores absmax 0 and code 7 (0.0).
+ * MXFP4 (same section, block 2; OCP MX v1.0): X = floor(log2 amax) - 2 clamped
+ *   to [-127, 127], e8m0 = X + 127; code = nearest e2m1 of w / 2^X, ties to the
+ *   even code, saturating at 6; code bit 3 = the input's sign bit.
+ * Errors: INVALID_ARG for null pointers, rows < 0, K not a multiple of the block,
+ * packed not 4-byte aligned. rows == 0 is a no-op. Non-finite inputs give
+ * unspecified codes.
+ * ------------------------------------------------------------------------- */
+nf4moe_status_t nf4moe_quantize(nf4moe_format_t fmt, const float *w, int64_t rows, int64_t K,
+                                uint8_t *packed, void *scale, void *stream);
+
+/* nf4moe_dequantize -- packed codes + scales (device) -> fp32 [rows, K] (device).
+ * A test export of the decode the GEMM kernels perform in registers: every
+ * element equals the reference decode bit for bit ("Expected result": the
+ * per-element decode is identical). Errors as for nf4moe_quantize. */
+nf4moe_status_t nf4moe_dequantize(nf4moe_format_t fmt, const uint8_t *packed, const void *scale,
+                                  int64_t rows, int64_t K, float *w_out, void *stream);
+
+/* nf4moe_router_logits -- logits[t, e] = sum_h x[t, h] * router_w[e, h] (+ router_b[e]),
+ * x bf16 [T, H], router_w fp32 [E, H], logits fp32 [T, E] (all device); fp32
+ * accumulation. The first step of the routed layer (the router, outside the
+ * kernel on the pages' "Why it happens" dataflow, inside this library).
+ * Errors: INVALID_ARG for T < 0, E outside 1..1024, H <= 0 or H % 8, null pointers. */
+nf4moe_status_t nf4moe_router_logits(const uint16_t *x, int32_t T, int32_t H,
+                                     const float *router_w, const float *router_b, int32_t E,
+                                     float *logits, void *stream);
+
+/* nf4moe_route_workspace_bytes -- workspace nf4moe_route_permute needs. */
+size_t nf4moe_route_workspace_bytes(int32_t T, int32_t E, int32_t top_k);
+
+/* nf4moe_route_permute -- top-k + softmax and grouping by expert, from given fp32
+ * logits [T, E] (device). Outputs (device):
+ *   topk_ids [T, k] int32: the k largest logits per token, ordered by (logit
+ *     descending, expert id ascending);
+ *   topk_w [T, k] fp32: renormalize=1 -> exp(L_j - L_0) / sum_j' exp(L_j' - L_0);
+ *     renormalize=0 -> softmax over all E at the selected ids;
+ *   expert_offsets [E+1] int32: rows of expert e are [off[e], off[e+1]);
+ *   sorted_slots [T*k] int32: slots s = t*k + j grouped by expert, ascending s
+ *     within an expert (a stable counting sort).
+ * This is the pages' "a_cat sorted by expert, sizes + expert_ids" grouping
+ * ("Why it happens" dataflow), done on the device with no host sync.
+ * ids, offsets and slots are exact integers (bit-identical to a stable sort of
+ * the same fp32 logits). Errors: INVALID_ARG (T < 0, E outside 1..1024, top_k
+ * outside 1..min(E, 32), null pointers), WORKSPACE (ws_bytes too small). */
+nf4moe_status_t nf4moe_route_permute(const float *logits, int32_t T, int32_t E, int32_t top_k,
+                                     int32_t renormalize, int32_t *topk_ids, float *topk_w,
+                                     int32_t *expert_offsets, int32_t *sorted_slots,
+                                     void *ws, size_t ws_bytes, void *stream);
+
+/* nf4moe_gemm_workspace_bytes -- workspace nf4moe_grouped_gemm needs. */
+size_t nf4moe_gemm_workspace_bytes(int32_t G, int32_t R);
+
+/* nf4moe_grouped_gemm -- the pages' gemm_4bit_grouped ("Smallest correct example",
+ * "Supported scope"): c[r, :] = a[row(r), :] . W[e(r)]^T over routed groups,
+ * W decoded from 4-bit codes in registers, fp32 accumulation.
+ *   a        bf16 [a_rows, K] (device, 16-byte aligned rows: K % 8 == 0)
+ *   a_row_of int32 [R] (device) or NULL: row r reads a[a_row_of[r]] (gather),
+ *            NULL means a[r] (then a_rows >= R)
+ *   B, B_scale  expert stack [E, N, K/2] + scales in `fmt` (device)
+ *   G, group_offsets int32 [G+1] (device): group g = rows [off[g], off[g+1]),
+ *            off[0] = 0, non-decreasing, off[G] = R (the caller guarantees this;
+ *            kernels clamp to R so a violation cannot write out of bounds)
+ *   group_experts int32 [G] (device) or NULL (group g uses expert g); values in [0, E)
+ *   c        [R, N] fp32 or bf16 (RNE) in group order (device)
+ *   path     nf4moe_path_t
+ * Empty groups are allowed. Errors: INVALID_ARG (K or N not a multiple of the
+ * format block / of 64, null pointers, R < 0, G outside 1..65536), WORKSPACE. */
+nf4moe_status_t nf4moe_grouped_gemm(nf4moe_format_t fmt, const uint16_t *a, const int32_t *a_row_of,
+                                    int32_t a_rows, const uint8_t *B, const void *B_scale, int32_t E,
+                                    int64_t N, int64_t K, int32_t G, const int32_t *group_offsets,
+                                    const int32_t *group_experts, int32_t R, void *c,
+                                    nf4moe_dtype_t c_dtype, int32_t path, void *ws, size_t ws_bytes,
+                                    void *stream);
+
+/* nf4moe_workspace_bytes -- workspace nf4moe_moe_forward needs for T <= T_max. */
+size_t nf4moe_workspace_bytes(const nf4moe_layer_t *layer, int32_t T_max);
+
+/* nf4moe_moe_forward -- one routed MoE layer: router logits, top-k + softmax,
+ * grouping by expert, grouped gate_up GEMM with in-register decode, SwiGLU
+ * (silu(gate) * up), grouped down GEMM, and the router-weighted combine
+ * out[t] = bf16_RNE( sum_j w[t, j] * y[t*k + j] ) summed in fp32. The pages'
+ * moe_layer_forward "gate -> GLU -> down" (grouped-nf4-gemm PKG-INFO, "The NVMe
+ * tier") plus the routing and combine the pages leave upstream.
+ *   x   bf16 [T, H] (device, 16-byte aligned, H % 64 == 0)
+ *   out bf16 [T, H] (device)
+ *   topk_ids_out [T, k] int32 / topk_w_out [T, k] fp32: optional copies of the
+ *   routing decision (device, may be NULL).
+ * Intermediates (h, partial products) stay fp32; no bf16 expert weight is
+ * written anywhere. Errors: INVALID_ARG (layer fields, sizes, pointers),
+ * WORKSPACE (ws_bytes < nf4moe_workspace_bytes(layer, T)). T == 0 is a no-op. */
+nf4moe_status_t nf4moe_moe_forward(const nf4moe_layer_t *layer, const uint16_t *x, int32_t T,
+                                   uint16_t *out, int32_t *topk_ids_out, float *topk_w_out,
+                                   void *ws, size_t ws_bytes, void *stream);
+
+/* nf4moe_moe_forward_profiled -- nf4moe_moe_forward (same kernels, same result,
+ * no topk copies) that also records caller-created HIP events (hipEvent_t) on
+ * `stream`: events[0] before the router, events[1] after routing + grouping,
+ * events[2] after the gate_up + SwiGLU kernel, events[3] after the down
+ * projection and combine. For measurement. Errors as for nf4moe_moe_forward,
+ * plus INVALID_ARG for a NULL events array. */
+nf4moe_status_t nf4moe_moe_forward_profiled(const nf4moe_layer_t *layer, const uint16_t *x,
+                                            int32_t T, uint16_t *out, void *ws, size_t ws_bytes,
+                                            void *stream, void *const *events);
+
+/* nf4moe_codebook -- host copy of the 16 fp32 decode values the kernels use for
+ * `fmt` (index = 4-bit code). No device access. Returns INVALID_ARG for a bad fmt
+ * or NULL out. */
+nf4moe_status_t nf4moe_codebook(nf4moe_format_t fmt, float out[16]);
+
+/* Human-readable name of a status; never NULL. */
+const char *nf4moe_status_string(nf4moe_status_t st);
+
+/* Thread-local description of this thread's last non-OK status ("" if none). */
+const char *nf4moe_last_error(void);
+
+/* Library version string. */
+const char *nf4moe_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NF4MOE_H */

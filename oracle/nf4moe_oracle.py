@@ -166,25 +166,32 @@ def mxfp4_quantize(w: np.ndarray):
     N, K = w.shape
     if K % MXFP4_BLOCK:
         raise ValueError("K must be a multiple of 32")
-    blocks = w.reshape(N, K // MXFP4_BLOCK, MXFP4_BLOCK).astype(np.float64)
-    amax = np.abs(blocks).max(axis=2)
-    X = np.full(amax.shape, -127, dtype=np.int64)
-    nz = amax > 0
-    _, e = np.frexp(amax[nz])            # amax = m * 2^e, m in [0.5, 1)
-    X[nz] = (e.astype(np.int64) - 1) - 2
-    X = np.clip(X, -127, 127)
-    v = np.ldexp(blocks, -X[..., None])  # exact power-of-two scaling
-    av = np.abs(v)
     mags = e2m1_values()[:8].astype(np.float64)
-    d = np.abs(av[..., None] - mags)
-    best = d.min(axis=-1, keepdims=True)
-    cand = d == best
-    # among the (at most two) nearest magnitudes take the even code
-    even = cand & (np.arange(8) % 2 == 0)
-    mag_code = np.where(even.any(axis=-1), np.argmax(even, axis=-1), np.argmax(cand, axis=-1))
-    mag_code = np.where(av >= 6.0, 7, mag_code)             # saturate
-    codes = (mag_code | np.where(np.signbit(v), 8, 0)).astype(np.uint8).reshape(N, K)
+    codes = np.empty((N, K), dtype=np.uint8)
+    X_all = np.empty((N, K // MXFP4_BLOCK), dtype=np.int64)
+    step = max(1, (1 << 16) // K)                             # bound the temporaries
+    for r0 in range(0, N, step):
+        blocks = w[r0:r0 + step].reshape(-1, K // MXFP4_BLOCK, MXFP4_BLOCK).astype(np.float64)
+        amax = np.abs(blocks).max(axis=2)
+        X = np.full(amax.shape, -127, dtype=np.int64)
+        nz = amax > 0
+        _, e = np.frexp(amax[nz])            # amax = m * 2^e, m in [0.5, 1)
+        X[nz] = (e.astype(np.int64) - 1) - 2
+        X = np.clip(X, -127, 127)
+        v = np.ldexp(blocks, -X[..., None])  # exact power-of-two scaling
+        av = np.abs(v)
+        d = np.abs(av[..., None] - mags)
+        best = d.min(axis=-1, keepdims=True)
+        cand = d == best
+        # among the (at most two) nearest magnitudes take the even code
+        even = cand & (np.arange(8) % 2 == 0)
+        mag_code = np.where(even.any(axis=-1), np.argmax(even, axis=-1), np.argmax(cand, axis=-1))
+        mag_code = np.where(av >= 6.0, 7, mag_code)             # saturate
+        c = (mag_code | np.where(np.signbit(v), 8, 0)).astype(np.uint8)
+        codes[r0:r0 + step] = c.reshape(-1, K)
+        X_all[r0:r0 + step] = X
     packed = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    X = X_all
     return packed, (X + 127).astype(np.uint8)
 
 

@@ -1,0 +1,117 @@
+"""Shared helpers of the GPU parity tests: device layers, the oracle-side layers
+built from the same fp32 inputs, the output bound, and the near-tie rule."""
+from __future__ import annotations
+
+import numpy as np
+
+import moe_synth as S
+import oracle as O
+
+# The output contract: |gpu - oracle| <= 1e-2 * |oracle| + 1e-3 * rms(oracle),
+# elementwise, against the unrounded fp64 oracle.
+REL, ABS_RMS = 1e-2, 1e-3
+
+
+def check_bound(gpu, ref, what=""):
+    gpu = np.asarray(gpu, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert gpu.shape == ref.shape, (gpu.shape, ref.shape)
+    assert np.all(np.isfinite(gpu)), f"{what}: non-finite output"
+    rms = float(np.sqrt(np.mean(ref ** 2))) if ref.size else 0.0
+    err = np.abs(gpu - ref)
+    bound = REL * np.abs(ref) + ABS_RMS * rms
+    ratio = float(np.max(err / np.maximum(bound, 1e-300))) if ref.size else 0.0
+    bad = int(np.sum(err > bound))
+    assert bad == 0, f"{what}: {bad} of {err.size} elements outside the bound (max err/bound {ratio:.3f})"
+    return ratio
+
+
+def bf16_to_np(t):
+    """torch bf16 tensor -> fp64 numpy (exact)."""
+    import torch
+    bits = t.detach().contiguous().view(torch.int16).cpu().numpy().astype(np.uint16)
+    return O.bf16_bits_to_f64(bits)
+
+
+def bits_to_torch_bf16(bits, device="cuda"):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(device).view(torch.bfloat16)
+
+
+class LazyStack:
+    """Oracle-side packed weights, quantized by the oracle one expert at a time
+    from the fp32 source (numpy array or a torch device tensor [E, N, K])."""
+
+    def __init__(self, fmt, src):
+        self.fmt, self.src, self.cache = fmt, src, {}
+
+    def _get(self, e):
+        if e not in self.cache:
+            w = self.src[e]
+            if not isinstance(w, np.ndarray):
+                w = w.detach().cpu().numpy()
+            self.cache[e] = O.quantize(self.fmt, np.ascontiguousarray(w, np.float32))
+        return self.cache[e]
+
+    def packed(self):
+        return _Proj(self, 0)
+
+    def scale(self):
+        return _Proj(self, 1)
+
+
+class _Proj:
+    def __init__(self, st, i):
+        self.st, self.i = st, i
+
+    def __getitem__(self, e):
+        return self.st._get(int(e))[self.i]
+
+
+def build_layers(wl: S.Workload, layer=0, device="cuda", on_device_rng=False, path=0):
+    """Returns (device MoELayer, oracle layer dict, fp32 sources)."""
+    import torch
+    import bit_quantized_moe_expert_amd as M
+    W_r, b_r = S.make_router(wl, layer)
+    if on_device_rng:
+        w13 = S.make_stack_torch(wl, layer, "w13", device)
+        w2 = S.make_stack_torch(wl, layer, "w2", device)
+        w13_d, w2_d = w13, w2
+    else:
+        w13 = S.make_stack(wl, layer, "w13")
+        w2 = S.make_stack(wl, layer, "w2")
+        w13_d = torch.from_numpy(w13).to(device)
+        w2_d = torch.from_numpy(w2).to(device)
+    p13, s13 = M.quantize(w13_d, wl.fmt)
+    p2, s2 = M.quantize(w2_d, wl.fmt)
+    dev_layer = M.MoELayer(
+        fmt=wl.fmt, E=wl.E, H=wl.H, I=wl.I, top_k=wl.top_k,
+        w13=p13, w13_scale=s13, w2=p2, w2_scale=s2,
+        router_w=torch.from_numpy(W_r).to(device),
+        router_b=None if b_r is None else torch.from_numpy(b_r).to(device),
+        renormalize=wl.renormalize, path=path)
+    st13, st2 = LazyStack(wl.fmt, w13), LazyStack(wl.fmt, w2)
+    o_layer = dict(fmt=wl.fmt, E=wl.E, H=wl.H, I=wl.I, top_k=wl.top_k, renormalize=wl.renormalize,
+                   w13=st13.packed(), w13_scale=st13.scale(), w2=st2.packed(), w2_scale=st2.scale(),
+                   router_w=W_r, router_b=b_r)
+    return dev_layer, o_layer, (w13, w2)
+
+
+def check_routing_near_ties(gpu_ids, L64, k, renorm=True):
+    """Tokens where the GPU (fp32 logits) picked differently from the oracle
+    (fp64 logits) are allowed only where the logits that swapped are within
+    tau = 1e-5 * (1 + max|L|). Returns the number of such tokens."""
+    ids_o, _ = O.topk_route(L64, k, renorm)
+    tau = 1e-5 * (1.0 + np.max(np.abs(L64), axis=1))
+    n = 0
+    for t in range(L64.shape[0]):
+        if np.array_equal(gpu_ids[t], ids_o[t]):
+            continue
+        n += 1
+        assert len(set(gpu_ids[t].tolist())) == k, f"token {t}: repeated expert"
+        for j in range(k):
+            a, b = int(gpu_ids[t, j]), int(ids_o[t, j])
+            if a != b:
+                assert abs(L64[t, a] - L64[t, b]) <= tau[t], (
+                    f"token {t} slot {j}: gpu {a} ({L64[t, a]}) vs oracle {b} ({L64[t, b]})")
+    return n

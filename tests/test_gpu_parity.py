@@ -1,0 +1,248 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 oracle.
+
+Bit-exact: NF4 / MXFP4 codes and scales, every decoded weight, top-k ids,
+expert offsets and the sorted slot permutation. Toleranced (the output
+contract): |gpu - oracle| <= 1e-2 |oracle| + 1e-3 rms(oracle) elementwise.
+"""
+import numpy as np
+import pytest
+
+import moe_synth as S
+import oracle as O
+from gpu_helpers import (bf16_to_np, bits_to_torch_bf16, build_layers, check_bound,
+                         check_routing_near_ties)
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import bit_quantized_moe_expert_amd as M  # noqa: E402
+
+DEV = "cuda"
+
+
+def _planted_weights(fmt, rows, K, seed):
+    rng = np.random.default_rng(seed)
+    w = (rng.standard_normal((rows, K)) * 0.02).astype(np.float32)
+    blk = O.block_size(fmt)
+    w[0, :blk] = 0.0                                         # all-zero block
+    w[1, :blk] = -0.0                                        # negative zeros
+    w[1, blk:2 * blk] = np.float32(1e-30) * rng.standard_normal(blk).astype(np.float32)  # tiny
+    w[2, :blk] = rng.standard_normal(blk).astype(np.float32) * np.float32(1e30)          # huge
+    if fmt == O.FMT_NF4:
+        c = O.nf4_codebook()
+        w[3, 0] = 1.0
+        for i in range(15):                                  # exact midpoints where representable
+            m = (np.float64(c[i]) + np.float64(c[i + 1])) / 2
+            if np.float64(np.float32(m)) == m:
+                w[3, 1 + i] = np.float32(m)
+    else:
+        w[3, 0] = 7.0                                        # X = 0; saturating element
+        for i, t in enumerate([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, -0.25, -2.5, 6.0]):
+            w[3, 1 + i] = t
+        w[4, :blk] = np.float32(2.0 ** -140)                # subnormal block max
+    return w
+
+
+@pytest.mark.parametrize("fmt,rows,K", [(O.FMT_NF4, 8, 256), (O.FMT_NF4, 37, 2048),
+                                        (O.FMT_NF4, 5, 2944), (O.FMT_MXFP4, 8, 256),
+                                        (O.FMT_MXFP4, 37, 2048), (O.FMT_MXFP4, 5, 2880)])
+def test_quantize_dequantize_bitexact(fmt, rows, K):
+    w = _planted_weights(fmt, rows, K, seed=rows * 7 + K)
+    pk_o, sc_o = O.quantize(fmt, w)
+    pk, sc = M.quantize(torch.from_numpy(w).to(DEV), fmt)
+    torch.cuda.synchronize()
+    assert np.array_equal(pk.cpu().numpy(), pk_o), "codes differ"
+    assert np.array_equal(sc.cpu().numpy().view(np.uint8), sc_o.view(np.uint8)), "scales differ"
+    deq = M.dequantize(pk, sc, K, fmt).cpu().numpy()
+    ref = O.dequantize(fmt, pk_o, sc_o, rows, K)
+    assert np.array_equal(deq.view(np.uint32), ref.view(np.uint32)), "decoded values differ"
+
+
+def test_quantize_large_stack_bitexact_sample():
+    """A C1-sized gate_up stack quantized on the device; sampled experts bit-exact."""
+    wl = S.WORKLOADS["olmoe_decode"]
+    w13 = S.make_stack_torch(wl, 0, "w13", DEV)
+    pk, sc = M.quantize(w13, wl.fmt)
+    for e in (0, 31, 63):
+        pk_o, sc_o = O.quantize(wl.fmt, w13[e].cpu().numpy())
+        assert np.array_equal(pk[e].cpu().numpy(), pk_o)
+        assert np.array_equal(sc[e].cpu().numpy(), sc_o)
+
+
+@pytest.mark.parametrize("T,E,H,bias", [(1, 64, 2048, False), (5, 8, 256, True),
+                                         (300, 128, 2048, True), (33, 100, 320, False)])
+def test_router_logits(T, E, H, bias):
+    wl = S.custom(E=E, top_k=2, H=H, I=64, zipf_s=1.2 if bias else 0.0)
+    xb = S.make_x(wl, T)
+    W, b = S.make_router(wl)
+    got = M.router_logits(bits_to_torch_bf16(xb), torch.from_numpy(W).to(DEV),
+                          None if b is None else torch.from_numpy(b).to(DEV)).cpu().numpy()
+    ref = O.router_logits(xb, W, b)
+    mag = np.abs(O.bf16_bits_to_f64(xb)) @ np.abs(W.astype(np.float64)).T
+    assert np.all(np.abs(got - ref) <= 2e-6 * mag + 1e-6)
+
+
+def _route_case(T, E, k, renorm, ties, seed):
+    rng = np.random.default_rng(seed)
+    L = rng.standard_normal((T, E)).astype(np.float32)
+    if ties:
+        L = (np.round(L * 2) / 2).astype(np.float32)          # many exact ties
+    got = M.route_permute(torch.from_numpy(L).to(DEV), k, renorm)
+    torch.cuda.synchronize()
+    ids_o, w_o = O.topk_route(L.astype(np.float64), k, renorm)
+    off_o, slots_o = O.permute(ids_o, E)
+    assert np.array_equal(got["topk_ids"].cpu().numpy(), ids_o)
+    assert np.array_equal(got["expert_offsets"].cpu().numpy(), off_o)
+    assert np.array_equal(got["sorted_slots"].cpu().numpy(), slots_o)
+    assert np.max(np.abs(got["topk_w"].cpu().numpy() - w_o)) <= 1e-6
+
+
+@pytest.mark.parametrize("T,E,k", [(1, 64, 8), (16, 8, 2), (300, 128, 8), (4097, 64, 8),
+                                   (50, 1000, 32), (7, 8, 8), (64, 4, 1), (600, 1024, 4)])
+@pytest.mark.parametrize("renorm", [1, 0])
+def test_route_permute_bitexact(T, E, k, renorm):
+    _route_case(T, E, k, renorm, ties=False, seed=T + E + k)
+    _route_case(T, E, k, renorm, ties=True, seed=T * 3 + E)
+
+
+def test_route_permute_empty():
+    got = M.route_permute(torch.zeros(0, 16, dtype=torch.float32, device=DEV), 2)
+    assert np.array_equal(got["expert_offsets"].cpu().numpy(), np.zeros(17, np.int32))
+
+
+# --------------------------------------------------------------------- grouped GEMM
+def _grouped_case(fmt, N, K, E, sizes, experts, path, out_dtype, gather, seed):
+    rng = np.random.default_rng(seed)
+    Wf = (rng.standard_normal((E, N, K)) * 0.02).astype(np.float32)
+    pk, sc = M.quantize(torch.from_numpy(Wf).to(DEV), fmt)
+    qs = [O.quantize(fmt, Wf[e]) for e in range(E)]
+    Bp = np.stack([q[0] for q in qs]); Bs = np.stack([q[1] for q in qs])
+    R = int(sum(sizes))
+    off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    rows_a = R + 5 if gather else R
+    ab = S.f32_to_bf16_bits(rng.standard_normal((rows_a, K)).astype(np.float32))
+    row_of = rng.integers(0, rows_a, R).astype(np.int32) if gather else None
+    c = M.grouped_gemm(bits_to_torch_bf16(ab), pk, sc, torch.from_numpy(off).to(DEV), K, R,
+                       group_experts=torch.from_numpy(np.array(experts, np.int32)).to(DEV),
+                       a_row_of=None if row_of is None else torch.from_numpy(row_of).to(DEV),
+                       fmt=fmt, out_dtype=out_dtype, path=path)
+    got = bf16_to_np(c) if out_dtype == torch.bfloat16 else c.cpu().numpy().astype(np.float64)
+    ref = O.grouped_gemm(O.bf16_bits_to_f64(ab), row_of, fmt, Bp, Bs, N, K, off, experts)
+    return got, ref
+
+
+@pytest.mark.parametrize("fmt", [O.FMT_NF4, O.FMT_MXFP4])
+@pytest.mark.parametrize("path", [M.PATH_SMALL_M, M.PATH_MFMA])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_grouped_gemm_page_example(fmt, path, dtype):
+    """E, N, K = 8, 256, 512; sizes [3, 1, 4]; expert_ids [5, 0, 2]; relative
+    Frobenius error <= 1e-2 (the page's own check), plus the elementwise bound."""
+    od = torch.float32 if dtype == "f32" else torch.bfloat16
+    got, ref = _grouped_case(fmt, 256, 512, 8, [3, 1, 4], [5, 0, 2], path, od, False, seed=11)
+    fro = np.linalg.norm(got - ref) / np.linalg.norm(ref)
+    assert fro <= 1e-2
+    check_bound(got, ref, "page example")
+
+
+@pytest.mark.parametrize("fmt,N,K", [(O.FMT_NF4, 200, 320), (O.FMT_MXFP4, 136, 288),
+                                     (O.FMT_NF4, 384, 1024), (O.FMT_MXFP4, 2880, 2880)])
+@pytest.mark.parametrize("path", [M.PATH_SMALL_M, M.PATH_MFMA])
+def test_grouped_gemm_ragged(fmt, N, K, path):
+    sizes = [1, 130, 0, 169, 2] if path == M.PATH_MFMA else [1, 0, 5, 2, 9]
+    got, ref = _grouped_case(fmt, N, K, 6, sizes, [3, 0, 5, 1, 4], path, torch.float32, True,
+                             seed=N + K)
+    check_bound(got, ref, f"ragged fmt={fmt} N={N} K={K} path={path}")
+
+
+# --------------------------------------------------------------------- full forward
+def _forward_case(wl, T, path=0, on_device_rng=False, sample=None):
+    dev_layer, o_layer, _ = build_layers(wl, 0, DEV, on_device_rng=on_device_rng, path=path)
+    xb = S.make_x(wl, T)
+    x = bits_to_torch_bf16(xb)
+    out, ids, _w = M.moe_forward(dev_layer, x, return_routing=True)
+    torch.cuda.synchronize()
+    got = bf16_to_np(out)
+    gids = ids.cpu().numpy()
+    rows = np.arange(T) if sample is None else np.asarray(sample)
+    L64 = O.router_logits(xb[rows], o_layer["router_w"], o_layer["router_b"])
+    nties = check_routing_near_ties(gids[rows], L64, wl.top_k, bool(wl.renormalize))
+    ref = O.moe_forward(o_layer, xb[rows], topk_ids_override=gids[rows])
+    ratio = check_bound(got[rows], ref, f"{wl.name} T={T} path={path}")
+    return dict(out=out, ratio=ratio, near_ties=nties, layer=dev_layer, x=x)
+
+
+SMALL = [
+    S.WORKLOADS["tiny"],
+    S.custom(E=16, top_k=4, H=512, I=256, wid=21),
+    S.custom(E=16, top_k=4, H=512, I=256, zipf_s=1.2, wid=22),
+    S.custom(E=8, top_k=2, H=320, I=288, fmt=O.FMT_MXFP4, wid=23),
+    S.custom(E=12, top_k=3, H=384, I=192, renormalize=0, wid=24),
+]
+
+
+@pytest.mark.parametrize("wl", SMALL, ids=lambda w: w.name)
+@pytest.mark.parametrize("T", [1, 2, 5, 16, 333])
+@pytest.mark.parametrize("path", [M.PATH_AUTO, M.PATH_SMALL_M, M.PATH_MFMA])
+def test_forward_small_shapes(wl, T, path):
+    _forward_case(wl, T, path)
+
+
+def test_forward_deterministic():
+    wl = S.custom(E=16, top_k=4, H=512, I=256, wid=25)
+    for T, path in ((1, 0), (300, 2), (40, 1)):
+        r = _forward_case(wl, T, path)
+        again = M.moe_forward(r["layer"], r["x"])
+        torch.cuda.synchronize()
+        assert torch.equal(r["out"].view(torch.int16), again.view(torch.int16))
+
+
+def test_forward_degenerate_routing():
+    # k = 1; top_k = E; one expert takes every token (a large bias)
+    for wl in (S.custom(E=4, top_k=1, H=256, I=128, wid=26), S.custom(E=8, top_k=8, H=256, I=128, wid=27)):
+        for path in (1, 2):
+            _forward_case(wl, 20, path)
+    wl = S.custom(E=8, top_k=2, H=256, I=128, wid=28)
+    dev_layer, o_layer, _ = build_layers(wl, 0, DEV, path=2)
+    bias = np.zeros(8, np.float32); bias[3] = 50.0
+    dev_layer.router_b = torch.from_numpy(bias).to(DEV)
+    o_layer["router_b"] = bias
+    xb = S.make_x(wl, 200)
+    out, ids, _ = M.moe_forward(dev_layer, bits_to_torch_bf16(xb), return_routing=True)
+    gids = ids.cpu().numpy()
+    assert np.all(gids[:, 0] == 3)
+    ref = O.moe_forward(o_layer, xb, topk_ids_override=gids)
+    check_bound(bf16_to_np(out), ref, "one expert takes all")
+
+
+def test_forward_zero_tokens():
+    wl = S.WORKLOADS["tiny"]
+    dev_layer, _, _ = build_layers(wl)
+    out = M.Forward(dev_layer, 4)(torch.zeros(0, wl.H, dtype=torch.bfloat16, device=DEV))
+    assert out.shape == (0, wl.H)
+
+
+# --------------------------------------------------------------------- full-size workloads
+@pytest.mark.slow
+def test_full_olmoe_decode():
+    _forward_case(S.WORKLOADS["olmoe_decode"], 1, on_device_rng=True)
+
+
+@pytest.mark.slow
+def test_full_olmoe_prefill_sampled():
+    wl = S.WORKLOADS["olmoe_prefill"]
+    _forward_case(wl, 4096, on_device_rng=True, sample=[0, 4095])
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("T,sample", [(1, None), (16, [0, 15]), (512, [0, 511])])
+def test_full_qwen3_zipf(T, sample):
+    _forward_case(S.WORKLOADS["qwen3_zipf"], T, on_device_rng=True, sample=sample)
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("T,sample", [(1, None), (2048, [2047])])
+def test_full_gptoss_mxfp4(T, sample):
+    _forward_case(S.WORKLOADS["gptoss_mxfp4"], T, on_device_rng=True, sample=sample)
