@@ -361,8 +361,13 @@ static nf4moe_status_t forward_impl(const nf4moe_layer_t *layer, const uint16_t 
   if ((e = mark(0)) != hipSuccess) return hip_status(e, "event record");
   e = launch_router_logits(x, T, L.H, L.router_w, L.router_b, L.E, fc.logits, s);
   if (e != hipSuccess) return hip_status(e, "router launch");
-  e = launch_route(fc.logits, T, L.E, L.top_k, L.renormalize, fc.rb, kMfmaBM, s);
-  if (e != hipSuccess) return hip_status(e, "route launch");
+  // One decode token on the small-M path: top-k and grouping happen inside the
+  // gate_up kernel; otherwise they are their own launches.
+  const bool fused_route = use == NF4MOE_PATH_SMALL_M && T == 1 && L.E <= 128;
+  if (!fused_route) {
+    e = launch_route(fc.logits, T, L.E, L.top_k, L.renormalize, fc.rb, kMfmaBM, s);
+    if (e != hipSuccess) return hip_status(e, "route launch");
+  }
   if ((e = mark(1)) != hipSuccess) return hip_status(e, "event record");
 
   // gate_up + SwiGLU -> h [R, I] fp32 in expert-sorted order
@@ -386,6 +391,13 @@ static nf4moe_status_t forward_impl(const nf4moe_layer_t *layer, const uint16_t 
   g.max_tiles = rp.max_tiles;
   g.epi = EPI_SWIGLU;
   g.c = fc.h;
+  if (fused_route) {
+    g.route_logits = fc.logits;
+    g.route_E = L.E;
+    g.route_k = L.top_k;
+    g.route_renorm = L.renormalize;
+    g.route_out = fc.rb;
+  }
   const int ms = T == 1 ? 1 : 4;
   e = use == NF4MOE_PATH_SMALL_M ? launch_gemv_grouped(g, ms, s) : launch_mfma_grouped(g, s);
   if (e != hipSuccess) return hip_status(e, "gate_up launch");
@@ -398,6 +410,7 @@ static nf4moe_status_t forward_impl(const nf4moe_layer_t *layer, const uint16_t 
     if (e != hipSuccess) return hip_status(e, "down launch");
   } else {
     GemmArgs d = g;
+    d.route_logits = nullptr;
     d.a = fc.h;
     d.a_is_f32 = 1;
     d.a_row_of = nullptr;

@@ -69,14 +69,55 @@ __device__ inline uint32_t f32_to_bf16_rne(float f) {
   return u >> 16;
 }
 
+// Codebook value of a 4-bit code computed with a select tree on literals, so a
+// table build touches no memory.
+__device__ inline float nf4_value_sel(uint32_t c) {
+  const float a0 = (c & 1) ? nf4_value(1) : nf4_value(0), a1 = (c & 1) ? nf4_value(3) : nf4_value(2);
+  const float a2 = (c & 1) ? nf4_value(5) : nf4_value(4), a3 = (c & 1) ? nf4_value(7) : nf4_value(6);
+  const float a4 = (c & 1) ? nf4_value(9) : nf4_value(8), a5 = (c & 1) ? nf4_value(11) : nf4_value(10);
+  const float a6 = (c & 1) ? nf4_value(13) : nf4_value(12), a7 = (c & 1) ? nf4_value(15) : nf4_value(14);
+  const float b0 = (c & 2) ? a1 : a0, b1 = (c & 2) ? a3 : a2, b2 = (c & 2) ? a5 : a4, b3 = (c & 2) ? a7 : a6;
+  const float d0 = (c & 4) ? b1 : b0, d1 = (c & 4) ? b3 : b2;
+  return (c & 8) ? d1 : d0;
+}
+__device__ inline float e2m1_value_sel(uint32_t c) {
+  const uint32_t m = c & 7;
+  // 0, 0.5, 1, 1.5, 2, 3, 4, 6: exponent/mantissa fields of the magnitude
+  const float mag = m < 2 ? 0.5f * (float)m : (float)(2 + (m & 1)) * (float)(1u << ((m >> 1) - 1)) * 0.5f;
+  return (c & 8) ? -mag : mag;
+}
+template <int FMT>
+__device__ inline float2 pair_value(uint32_t b) {
+  return FMT == 0 ? make_float2(nf4_value_sel(b >> 4), nf4_value_sel(b & 15))
+                  : make_float2(e2m1_value_sel(b & 15), e2m1_value_sel(b >> 4));
+}
+
 // ---------------------------------------------------------------------------
-// Wave reductions (64 lanes). Every lane receives the result.
+// Wave reductions (64 lanes). Every lane receives the result. Within a row of
+// 16 lanes: DPP (quad xor 1, quad xor 2, half-row mirror, row mirror); across
+// rows: lane shuffles.
 // ---------------------------------------------------------------------------
-__device__ inline float wave_sum(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
+template <int CTRL>
+__device__ inline float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+__device__ inline float row16_sum(float v) {
+  v += dpp<0xB1>(v);   // quad_perm [1,0,3,2]
+  v += dpp<0x4E>(v);   // quad_perm [2,3,0,1]
+  v += dpp<0x141>(v);  // row_half_mirror
+  v += dpp<0x140>(v);  // row_mirror
   return v;
 }
+// Sum over aligned groups of LPR lanes (LPR in {16, 32, 64}).
+template <int LPR>
+__device__ inline float seg_sum(float v) {
+  static_assert(LPR == 16 || LPR == 32 || LPR == 64, "segment");
+  v = row16_sum(v);
+  if (LPR >= 32) v += __shfl_xor(v, 16, kWave);
+  if (LPR >= 64) v += __shfl_xor(v, 32, kWave);
+  return v;
+}
+__device__ inline float wave_sum(float v) { return seg_sum<64>(v); }
 
 __device__ inline float wave_max(float v) {
 #pragma unroll
@@ -99,14 +140,28 @@ __device__ inline uint64_t lanemask_lt() {
 // ---------------------------------------------------------------------------
 // LDS decode table: byte -> (value of even-k code, value of odd-k code) as two
 // fp32, replicated kRep times so the lanes of one LDS access read distinct
-// banks. Entry (byte b, replica r) lives at float2 index b * kRep + r.
+// banks. Entry (byte b, replica r) lives at float2 index b * kRep + r. Built by
+// `nthreads` threads starting at `first_thread` with register arithmetic only
+// (no memory latency); consecutive threads write consecutive 16-byte words so
+// the writes are conflict-free.
 // ---------------------------------------------------------------------------
 template <int FMT, int kRep>
-__device__ inline void build_pair_table(float2 *tab) {
-  for (int i = threadIdx.x; i < 256 * kRep; i += blockDim.x) {
-    const uint32_t b = (uint32_t)i / kRep;
-    tab[i] = make_float2(even_value<FMT>(b), odd_value<FMT>(b));
+__device__ inline void build_pair_table(float2 *tab, int first_thread, int nthreads) {
+  constexpr int kWords = 256 * kRep / 2;  // float4 words, kRep / 2 per byte
+  float4 *dst = reinterpret_cast<float4 *>(tab);
+  const int t = (int)threadIdx.x - first_thread;
+  if (t < 0 || t >= nthreads) return;
+  for (int f = t; f < kWords; f += nthreads) {  // consecutive lanes, consecutive words
+    const float2 v = pair_value<FMT>((uint32_t)(f / (kRep / 2)));
+    dst[f] = make_float4(v.x, v.y, v.x, v.y);
   }
+}
+
+// Byte offset (b * 256 + lanebyte) of table entry (b, lane & 31) for a 32-replica
+// table of 8-byte entries: one v_perm_b32 places byte j of `word` above the
+// lane's replica offset.
+__device__ inline uint32_t tab_offset(uint32_t word, uint32_t lanebyte, int j) {
+  return __builtin_amdgcn_perm(word, lanebyte, 0x0c0c0400u + ((uint32_t)j << 8));
 }
 
 }  // namespace nf4moe

@@ -22,14 +22,6 @@ namespace nf4moe {
 
 constexpr int kGemvRep = 32;  // LDS table replicas
 
-// Sum over aligned groups of LPR lanes (LPR a power of two <= 64).
-template <int LPR>
-__device__ inline float seg_sum(float v) {
-#pragma unroll
-  for (int m = LPR / 2; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
-  return v;
-}
-
 template <int FMT>
 __device__ inline float block_scale(const void *scale, int64_t idx) {
   if (FMT == 0) return reinterpret_cast<const float *>(scale)[idx];
@@ -67,16 +59,17 @@ __device__ inline void load_act32(const void *a, int64_t off, float *xr) {
 }
 
 // Dot product of one 16-byte chunk of codes (32 weights) with 32 activations
-// for MS activation rows at once; each byte is looked up once.
+// for MS activation rows at once; each byte is one v_perm (table address) and
+// one 8-byte LDS read, then two FMAs per activation row.
 template <int MS>
-__device__ inline void chunk_dot(const float2 *tab, uint4 q, const float (*xr)[32], float *dot) {
+__device__ inline void chunk_dot(const char *tab, uint32_t lanebyte, uint4 q, const float (*xr)[32],
+                                 float *dot) {
   const uint32_t w[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
   for (int d = 0; d < 4; ++d) {
 #pragma unroll
     for (int bsel = 0; bsel < 4; ++bsel) {
-      const uint32_t byte = (w[d] >> (8 * bsel)) & 0xffu;
-      const float2 p = tab[byte * kGemvRep];
+      const float2 p = *reinterpret_cast<const float2 *>(tab + tab_offset(w[d], lanebyte, bsel));
       const int k = 8 * d + 2 * bsel;
 #pragma unroll
       for (int m = 0; m < MS; ++m) {
@@ -87,35 +80,138 @@ __device__ inline void chunk_dot(const float2 *tab, uint4 q, const float (*xr)[3
   }
 }
 
-// One workgroup = 4 waves; blockIdx.y = group, blockIdx.x = block of output
-// columns. Each wave reads NL wave-loads of weight rows (RPL rows per
+// One workgroup = kGemvWaves waves; blockIdx.y = group, blockIdx.x = block of
+// output columns. Each wave reads NL wave-loads of weight rows (RPL rows per
 // wave-load when a row is shorter than 64 chunks; at most 16 rows and 8
 // 16-byte loads in flight per lane) and applies them to the group's rows MS at
-// a time.
-template <int FMT, int EPI, int AF32, int LPR, int NJ, int MS>
-__global__ __launch_bounds__(256) void k_gemv(GemmArgs p) {
+// a time. Weight and first activation loads are issued before the LDS table is
+// built, so the table build overlaps their latency.
+constexpr int kGemvWaves = 8;
+
+// Wave-loads (16 bytes per lane each) a wave keeps in flight: 8 / NJ, at most
+// 16 rows per wave, and 4 when four activation rows are held in registers.
+template <int LPR, int NJ, int MS>
+constexpr int gemv_loads() {
+  constexpr int a = 8 / NJ, b = 16 / (64 / LPR), c = MS >= 4 ? (LPR == 16 ? 2 : 4) : 8;
+  return a < b ? (a < c ? a : c) : (b < c ? b : c);
+}
+
+// Routing of a single token inside the gate_up kernel (wave 0): rank of each
+// expert under (logit descending, id ascending) from readlane broadcasts; the
+// k selected experts in ascending id order go to s_sorted_e. With publish set,
+// also writes every routing output (ids, weights, offsets, permutation, group
+// list, tiles) for the kernels that follow.
+template <int EPL>
+__device__ inline void route_one_token(const GemmArgs &p, bool publish, int *s_sorted_e) {
+  const int lane = threadIdx.x & 63;
+  const int E = p.route_E, k = p.route_k;
+  float v[EPL];
+  int rank[EPL];
+#pragma unroll
+  for (int j = 0; j < EPL; ++j) {
+    const int e = lane + 64 * j;
+    v[j] = e < E ? p.route_logits[e] : -__builtin_inff();
+    rank[j] = 0;
+  }
+#pragma unroll
+  for (int jj = 0; jj < EPL; ++jj) {
+#pragma unroll 16
+    for (int src = 0; src < 64; ++src) {
+      const int f = src + 64 * jj;
+      if (f >= E) break;
+      const float u = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v[jj]), src));
+#pragma unroll
+      for (int j = 0; j < EPL; ++j) {
+        const int e = lane + 64 * j;
+        rank[j] += (u > v[j] || (u == v[j] && f < e)) ? 1 : 0;
+      }
+    }
+  }
+  uint64_t sel[EPL];
+  int below = 0;  // selected experts with a smaller id, accumulated over j
+  float vmax = -__builtin_inff(), part = 0.0f, full = 0.0f;
+#pragma unroll
+  for (int j = 0; j < EPL; ++j) {
+    const int e = lane + 64 * j;
+    const bool chosen = e < E && rank[j] < k;
+    sel[j] = __ballot(chosen);
+    if (e < E && rank[j] == 0) vmax = v[j];
+  }
+  vmax = wave_max(vmax);
+#pragma unroll
+  for (int j = 0; j < EPL; ++j) {
+    const int e = lane + 64 * j;
+    const bool chosen = e < E && rank[j] < k;
+    const float ex = e < E ? expf(v[j] - vmax) : 0.0f;
+    part += chosen ? ex : 0.0f;
+    full += ex;
+  }
+  const float denom = wave_sum(p.route_renorm ? part : full);
+#pragma unroll
+  for (int j = 0; j < EPL; ++j) {
+    const int e = lane + 64 * j;
+    const int pos_e = below + __popcll(sel[j] & lanemask_lt());  // selected ids < e
+    const bool chosen = e < E && rank[j] < k;
+    if (chosen) s_sorted_e[pos_e] = e;
+    if (publish) {
+      const RouteBufs &o = p.route_out;
+      if (e < E) o.expert_offsets[e] = pos_e;
+      if (chosen) {
+        const int r = rank[j];
+        o.topk_ids[r] = e;
+        o.topk_w[r] = expf(v[j] - vmax) / denom;
+        o.slot_pos[r] = pos_e;
+        o.sorted_slots[pos_e] = r;
+        o.grp_expert[pos_e] = e;
+        o.grp_row0[pos_e] = pos_e;
+        o.grp_rows[pos_e] = 1;
+        o.tiles[pos_e] = make_int4(e, pos_e, 1, 0);
+      }
+    }
+    below += __popcll(sel[j]);
+  }
+  if (publish && lane == 0) {
+    p.route_out.expert_offsets[E] = k;
+    p.route_out.counters[0] = k;
+    p.route_out.counters[1] = k;
+  }
+}
+
+// One workgroup = kGemvWaves waves; blockIdx.y = group, blockIdx.x = block of
+// output columns. The LDS table is built (and, for ROUTE > 0, the token routed)
+// before any weight load, so that each wave then consumes its rows as they
+// arrive: the workgroup barrier would otherwise wait for every load in flight.
+template <int FMT, int EPI, int AF32, int LPR, int NJ, int MS, int ROUTE>
+__global__ __launch_bounds__(kGemvWaves * 64) void k_gemv(GemmArgs p) {
   constexpr int RPL = 64 / LPR;
-  constexpr int NL = (8 / NJ) < (16 / RPL) ? (8 / NJ) : (16 / RPL);
+  constexpr int NL = gemv_loads<LPR, NJ, MS>();
   constexpr int WR = NL * RPL;                       // weight rows per wave (<= 16)
   constexpr int RPU = (EPI == EPI_SWIGLU) ? 2 : 1;   // weight rows per output column
   constexpr int UPW = WR / RPU;                      // output columns per wave
   static_assert(MS * UPW <= 64, "one lane per output");
   __shared__ float2 tab_all[256 * kGemvRep];
+  __shared__ int s_sorted_e[kMaxTopK];
 
   const int gi = blockIdx.y;
-  const int ngrp = p.n_grp ? *p.n_grp : p.max_grp;
-  if (gi >= ngrp) return;                            // uniform over the workgroup
-  const int rows = p.grp_rows[gi];
-  if (rows <= 0) return;
-  build_pair_table<FMT, kGemvRep>(tab_all);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if constexpr (ROUTE > 0) {
+    if (gi >= p.route_k) return;                     // uniform over the workgroup
+    if (wave == 0) route_one_token<ROUTE>(p, blockIdx.x == 0 && gi == 0, s_sorted_e);
+  } else {
+    const int ngrp = p.n_grp ? *p.n_grp : p.max_grp;
+    if (gi >= ngrp) return;                          // uniform over the workgroup
+    if (p.grp_rows[gi] <= 0) return;
+  }
+  build_pair_table<FMT, kGemvRep>(tab_all, ROUTE > 0 ? 64 : 0,
+                                 ROUTE > 0 ? kGemvWaves * 64 - 64 : kGemvWaves * 64);
   __syncthreads();
 
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int e = p.grp_expert[gi], row0 = p.grp_row0[gi];
+  const int e = ROUTE > 0 ? s_sorted_e[gi] : p.grp_expert[gi];
+  const int row0 = ROUTE > 0 ? gi : p.grp_row0[gi];
+  const int rows = ROUTE > 0 ? 1 : p.grp_rows[gi];
   const int64_t ncol = (EPI == EPI_SWIGLU) ? p.N / 2 : p.N;
-  const int64_t u0 = ((int64_t)blockIdx.x * 4 + wave) * UPW;
+  const int64_t u0 = ((int64_t)blockIdx.x * kGemvWaves + wave) * UPW;
   if (u0 >= ncol) return;                            // no barrier follows
-  const float2 *tab = tab_all + (lane & (kGemvRep - 1));
   const int sr = lane / LPR, li = lane % LPR;
   const int64_t nch = p.K / 32;                      // 16-byte chunks per row
   const int64_t rowbytes = p.K / 2;
@@ -123,9 +219,70 @@ __global__ __launch_bounds__(256) void k_gemv(GemmArgs p) {
   const int64_t sc_per_row = p.K / Fmt<FMT>::kBlock;
   const int64_t sc_base = (int64_t)e * p.N * sc_per_row;
 
-  // Issue every weight load of this wave first.
+  // Activations: raw loads first (bf16 bits or fp32), converted only once the
+  // weight loads below are in flight.
+  constexpr int XW = AF32 ? 8 : 4;                   // 16-byte words per 32 activations
+  uint4 xraw[MS][NJ][XW];
+  auto issue_x = [&](int m0) {
+#pragma unroll
+    for (int m = 0; m < MS; ++m) {
+      const bool live = (m0 + m) < rows;
+      const int r = row0 + (live ? m0 + m : 0);
+      int64_t arow = ROUTE > 0 ? 0 : r;
+      if (ROUTE == 0 && p.a_row_of) arow = p.a_row_of[r] / p.a_div;
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const int64_t c = li + (int64_t)LPR * j;
+        const int64_t off = arow * p.K + (c < nch ? c : 0) * 32;
+        const uint4 *src = AF32 ? reinterpret_cast<const uint4 *>(reinterpret_cast<const float *>(p.a) + off)
+                                : reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(p.a) + off);
+#pragma unroll
+        for (int w = 0; w < XW; ++w) xraw[m][j][w] = src[w];
+      }
+    }
+  };
+  // Values in lanes past the row end or rows past the group are finite (the
+  // addresses are clamped) and never reach an output: their chunks carry a zero
+  // scale and their rows are not stored.
+  float xr[MS][NJ][32];
+  auto convert_x = [&]() {
+#pragma unroll
+    for (int m = 0; m < MS; ++m) {
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+#pragma unroll
+        for (int w = 0; w < XW; ++w) {
+          const uint4 v = xraw[m][j][w];
+          if (AF32) {
+            xr[m][j][4 * w + 0] = __uint_as_float(v.x);
+            xr[m][j][4 * w + 1] = __uint_as_float(v.y);
+            xr[m][j][4 * w + 2] = __uint_as_float(v.z);
+            xr[m][j][4 * w + 3] = __uint_as_float(v.w);
+          } else {
+            xr[m][j][8 * w + 0] = bf16lo_to_f32(v.x);
+            xr[m][j][8 * w + 1] = bf16hi_to_f32(v.x);
+            xr[m][j][8 * w + 2] = bf16lo_to_f32(v.y);
+            xr[m][j][8 * w + 3] = bf16hi_to_f32(v.y);
+            xr[m][j][8 * w + 4] = bf16lo_to_f32(v.z);
+            xr[m][j][8 * w + 5] = bf16hi_to_f32(v.z);
+            xr[m][j][8 * w + 6] = bf16lo_to_f32(v.w);
+            xr[m][j][8 * w + 7] = bf16hi_to_f32(v.w);
+          }
+        }
+      }
+    }
+  };
+  issue_x(0);
+  if constexpr (MS > 1) convert_x();  // several rows: convert now, fewer live registers
+  __builtin_amdgcn_sched_barrier(0);  // keep the activation loads first
+
+  // Weight loads of this wave, after the activations and in row order (code,
+  // then scale), so that row i waits only for its own data: vector loads
+  // retire in issue order. Addresses are clamped into the expert's rows so
+  // every load is unconditional; an out-of-range row or chunk gets scale 0.
   uint4 wq[NL][NJ];
   float sc[NL][NJ];
+  bool sok[NL][NJ];
 #pragma unroll
   for (int i = 0; i < NL; ++i) {
     const int q = i * RPL + sr;                      // position in the wave's row list
@@ -137,39 +294,30 @@ __global__ __launch_bounds__(256) void k_gemv(GemmArgs p) {
       col = u0 + q;
       wrow = col;
     }
+    const bool rok = col < ncol;
+    const int64_t wr = rok ? wrow : 0;
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
       const int64_t c = li + (int64_t)LPR * j;
-      if (col < ncol && c < nch) {
-        wq[i][j] = *reinterpret_cast<const uint4 *>(Be + wrow * rowbytes + c * 16);
-        const int64_t sidx = FMT == 0 ? (c >> 1) : c;
-        sc[i][j] = block_scale<FMT>(p.B_scale, sc_base + wrow * sc_per_row + sidx);
-      } else {
-        wq[i][j] = make_uint4(0, 0, 0, 0);
-        sc[i][j] = 0.0f;
-      }
+      const bool ok = rok && c < nch;
+      const int64_t cc = c < nch ? c : 0;
+      wq[i][j] = *reinterpret_cast<const uint4 *>(Be + wr * rowbytes + cc * 16);
+      const int64_t sidx = FMT == 0 ? (cc >> 1) : cc;
+      sc[i][j] = block_scale<FMT>(p.B_scale, sc_base + wr * sc_per_row + sidx);
+      sok[i][j] = ok;
     }
   }
+  __builtin_amdgcn_sched_barrier(0);  // every load is in flight before any wait
 
+  const char *tab = reinterpret_cast<const char *>(tab_all);
+  const uint32_t lanebyte = (uint32_t)(lane & (kGemvRep - 1)) * 8u;
   const int my_m = lane / UPW, my_u = lane % UPW;
   for (int m0 = 0; m0 < rows; m0 += MS) {
-    float xr[MS][NJ][32];
-#pragma unroll
-    for (int m = 0; m < MS; ++m) {
-      const int r = row0 + m0 + m;
-      const bool live = (m0 + m) < rows;
-      int64_t arow = r;
-      if (live && p.a_row_of) arow = p.a_row_of[r] / p.a_div;
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        const int64_t c = li + (int64_t)LPR * j;
-        if (live && c < nch) {
-          load_act32<AF32>(p.a, arow * p.K + c * 32, xr[m][j]);
-        } else {
-#pragma unroll
-          for (int t = 0; t < 32; ++t) xr[m][j][t] = 0.0f;
-        }
-      }
+    if (m0 > 0) {
+      issue_x(m0);
+      convert_x();
+    } else if constexpr (MS == 1) {
+      convert_x();
     }
     float acc[MS][NL];
 #pragma unroll
@@ -186,13 +334,17 @@ __global__ __launch_bounds__(256) void k_gemv(GemmArgs p) {
         float dot[MS];
 #pragma unroll
         for (int m = 0; m < MS; ++m) dot[m] = 0.0f;
-        chunk_dot<MS>(tab, wq[i][j], xj, dot);
+        chunk_dot<MS>(tab, lanebyte, wq[i][j], xj, dot);
 #pragma unroll
-        for (int m = 0; m < MS; ++m) acc[m][i] = fmaf(sc[i][j], dot[m], acc[m][i]);
+        for (int m = 0; m < MS; ++m) acc[m][i] = fmaf(sok[i][j] ? sc[i][j] : 0.0f, dot[m], acc[m][i]);
       }
+      // keep the scheduler from hoisting every row's LDS lookups at once
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int i = 0; i < NL; ++i)
 #pragma unroll
       for (int m = 0; m < MS; ++m) acc[m][i] = seg_sum<LPR>(acc[m][i]);
-    }
     // Route each finished row value to the lane that stores it.
     float v0 = 0.0f, v1 = 0.0f;
 #pragma unroll
@@ -231,15 +383,15 @@ __global__ __launch_bounds__(256) void k_gemv(GemmArgs p) {
   }
 }
 
-template <int FMT, int EPI, int AF32, int LPR, int NJ, int MS>
+template <int FMT, int EPI, int AF32, int LPR, int NJ, int MS, int ROUTE = 0>
 static void launch_gemv_t(const GemmArgs &g, hipStream_t s) {
   constexpr int RPL = 64 / LPR;
-  constexpr int NL = (8 / NJ) < (16 / RPL) ? (8 / NJ) : (16 / RPL);
+  constexpr int NL = gemv_loads<LPR, NJ, MS>();
   constexpr int WR = NL * RPL;
   constexpr int UPW = WR / ((EPI == EPI_SWIGLU) ? 2 : 1);
   const int64_t ncol = (EPI == EPI_SWIGLU) ? g.N / 2 : g.N;
-  const dim3 grid((unsigned)cdiv(ncol, 4 * UPW), (unsigned)g.max_grp);
-  hipLaunchKernelGGL((k_gemv<FMT, EPI, AF32, LPR, NJ, MS>), grid, dim3(256), 0, s, g);
+  const dim3 grid((unsigned)cdiv(ncol, kGemvWaves * UPW), (unsigned)(ROUTE > 0 ? g.route_k : g.max_grp));
+  hipLaunchKernelGGL((k_gemv<FMT, EPI, AF32, LPR, NJ, MS, ROUTE>), grid, dim3(kGemvWaves * 64), 0, s, g);
 }
 
 template <int FMT, int EPI, int AF32, int LPR, int NJ>
@@ -287,7 +439,33 @@ static hipError_t pick_epi(const GemmArgs &g, int ms, hipStream_t s) {
   }
 }
 
+template <int FMT>
+static hipError_t launch_routed(const GemmArgs &g, hipStream_t s) {
+  const int64_t nch = g.K / 32;
+  const bool two = g.route_E > 64;
+  if (nch > 128) return hipErrorInvalidValue;
+  if (nch > 64) {
+    if (two) launch_gemv_t<FMT, EPI_SWIGLU, 0, 64, 2, 1, 2>(g, s);
+    else launch_gemv_t<FMT, EPI_SWIGLU, 0, 64, 2, 1, 1>(g, s);
+  } else if (nch > 32) {
+    if (two) launch_gemv_t<FMT, EPI_SWIGLU, 0, 64, 1, 1, 2>(g, s);
+    else launch_gemv_t<FMT, EPI_SWIGLU, 0, 64, 1, 1, 1>(g, s);
+  } else if (nch > 16) {
+    if (two) launch_gemv_t<FMT, EPI_SWIGLU, 0, 32, 1, 1, 2>(g, s);
+    else launch_gemv_t<FMT, EPI_SWIGLU, 0, 32, 1, 1, 1>(g, s);
+  } else {
+    if (two) launch_gemv_t<FMT, EPI_SWIGLU, 0, 16, 1, 1, 2>(g, s);
+    else launch_gemv_t<FMT, EPI_SWIGLU, 0, 16, 1, 1, 1>(g, s);
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_gemv_grouped(const GemmArgs &g, int ms_hint, hipStream_t s) {
+  if (g.route_logits) {
+    if (g.epi != EPI_SWIGLU || g.a_is_f32 || g.route_E > 128 || g.route_k > kMaxTopK)
+      return hipErrorInvalidValue;
+    return g.fmt == 0 ? launch_routed<0>(g, s) : launch_routed<1>(g, s);
+  }
   if (g.max_grp <= 0) return hipSuccess;
   return g.fmt == 0 ? pick_epi<0>(g, ms_hint, s) : pick_epi<1>(g, ms_hint, s);
 }
@@ -310,22 +488,23 @@ __global__ __launch_bounds__(256) void k_down_combine(const float *__restrict__ 
                                                       uint16_t *__restrict__ out) {
   __shared__ float2 tab_all[256 * kGemvRep];
   __shared__ float red[4][RB];
-  build_pair_table<FMT, kGemvRep>(tab_all);
-  __syncthreads();
+  build_pair_table<FMT, kGemvRep>(tab_all, 0, 256);
+  __syncthreads();  // before any global load: the barrier would wait for them
   const int t = blockIdx.y;
   const int n0 = blockIdx.x * RB;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const float2 *tab = tab_all + (lane & (kGemvRep - 1));
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int nch = I / 32;
   const int Q = k * nch;
   const int QW = (Q + 3) / 4;
   const int64_t rowbytes = I / 2;
   const int64_t sc_per_row = I / Fmt<FMT>::kBlock;
 
-  float hv[NQ][32];
+  // (slot, chunk) pairs of this lane, their weight rows and activations
   const uint8_t *wbase[NQ];
   int64_t sbase[NQ];
   bool live[NQ];
+  int64_t hoff[NQ];
+  float wj[NQ];
 #pragma unroll
   for (int qi = 0; qi < NQ; ++qi) {
     const int ql = qi * 64 + lane;
@@ -335,18 +514,20 @@ __global__ __launch_bounds__(256) void k_down_combine(const float *__restrict__ 
     const int c = live[qi] ? q % nch : 0;
     const int slot = t * k + j;
     const int e = topk_ids[slot];
-    const float wj = topk_w[slot];
-    const int64_t r = slot_pos[slot];
-    if (live[qi]) {
-      load_act32<1>(h, r * I + (int64_t)c * 32, hv[qi]);
-#pragma unroll
-      for (int i = 0; i < 32; ++i) hv[qi][i] *= wj;
-    } else {
-#pragma unroll
-      for (int i = 0; i < 32; ++i) hv[qi][i] = 0.0f;
-    }
+    wj[qi] = topk_w[slot];
+    hoff[qi] = (int64_t)slot_pos[slot] * I + (int64_t)c * 32;
     wbase[qi] = w2 + (int64_t)e * H * rowbytes + (int64_t)c * 16;
     sbase[qi] = (int64_t)e * H * sc_per_row + (FMT == 0 ? (c >> 1) : c);
+  }
+  // Loads: activations first, then weights in row order (vector loads retire
+  // in issue order, so row n waits only for its own data); all unconditional
+  // from clamped addresses. An idle lane gets weight 0, a row past H scale 0.
+  uint4 hraw[NQ][8];
+#pragma unroll
+  for (int qi = 0; qi < NQ; ++qi) {
+    const uint4 *src = reinterpret_cast<const uint4 *>(h + hoff[qi]);
+#pragma unroll
+    for (int w = 0; w < 8; ++w) hraw[qi][w] = src[w];
   }
   uint4 wq[RB][NQ];
   float sc[RB][NQ];
@@ -355,15 +536,26 @@ __global__ __launch_bounds__(256) void k_down_combine(const float *__restrict__ 
 #pragma unroll
     for (int qi = 0; qi < NQ; ++qi) {
       const int row = n0 + n;
-      if (live[qi] && row < H) {
-        wq[n][qi] = *reinterpret_cast<const uint4 *>(wbase[qi] + (int64_t)row * rowbytes);
-        sc[n][qi] = block_scale<FMT>(w2s, sbase[qi] + (int64_t)row * sc_per_row);
-      } else {
-        wq[n][qi] = make_uint4(0, 0, 0, 0);
-        sc[n][qi] = 0.0f;
-      }
+      const int64_t rc = row < H ? row : H - 1;
+      wq[n][qi] = *reinterpret_cast<const uint4 *>(wbase[qi] + rc * rowbytes);
+      sc[n][qi] = block_scale<FMT>(w2s, sbase[qi] + rc * sc_per_row);
     }
   }
+  __builtin_amdgcn_sched_barrier(0);  // every load is in flight before any wait
+  float hv[NQ][32];
+#pragma unroll
+  for (int qi = 0; qi < NQ; ++qi) {
+    const float wv = live[qi] ? wj[qi] : 0.0f;
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+      hv[qi][4 * w + 0] = __uint_as_float(hraw[qi][w].x) * wv;
+      hv[qi][4 * w + 1] = __uint_as_float(hraw[qi][w].y) * wv;
+      hv[qi][4 * w + 2] = __uint_as_float(hraw[qi][w].z) * wv;
+      hv[qi][4 * w + 3] = __uint_as_float(hraw[qi][w].w) * wv;
+    }
+  }
+  const char *tab = reinterpret_cast<const char *>(tab_all);
+  const uint32_t lanebyte = (uint32_t)(lane & (kGemvRep - 1)) * 8u;
 #pragma unroll
   for (int n = 0; n < RB; ++n) {
     float acc = 0.0f;
@@ -373,8 +565,8 @@ __global__ __launch_bounds__(256) void k_down_combine(const float *__restrict__ 
       float xj[1][32];
 #pragma unroll
       for (int i = 0; i < 32; ++i) xj[0][i] = hv[qi][i];
-      chunk_dot<1>(tab, wq[n][qi], xj, &dot);
-      acc = fmaf(sc[n][qi], dot, acc);
+      chunk_dot<1>(tab, lanebyte, wq[n][qi], xj, &dot);
+      acc = fmaf((n0 + n < H) ? sc[n][qi] : 0.0f, dot, acc);
     }
     acc = wave_sum(acc);
     if (lane == 0) red[wave][n] = acc;

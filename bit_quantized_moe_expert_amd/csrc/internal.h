@@ -66,6 +66,13 @@ struct GemmArgs {
   void *c;                  // SwiGLU: fp32 [R, N/2]; plain: [R, N]; slot: fp32 [R_slots, N]
   const int32_t *slot_of;   // EPI_SLOT: row r -> slot
   const float *slot_w;      // EPI_SLOT: weight of slot
+  // One-token routing folded into the gate_up kernel: when route_logits is set
+  // (T = 1, E <= 128), every workgroup ranks the E logits itself and takes the
+  // blockIdx.y-th selected expert (ascending id); workgroup (0, 0) also writes
+  // the routing results into route_out for the kernels that follow.
+  const float *route_logits;
+  int route_E, route_k, route_renorm;
+  RouteBufs route_out;
 };
 hipError_t launch_gemv_grouped(const GemmArgs &g, int ms_hint, hipStream_t s);
 hipError_t launch_mfma_grouped(const GemmArgs &g, hipStream_t s);

@@ -43,7 +43,8 @@ __device__ inline bf16x8_t as_bf16x8(uint32_t a, uint32_t b, uint32_t c, uint32_
 __device__ inline void build_nf4_bf16_table(uint2 *tab) {
   for (int i = threadIdx.x; i < 256 * kMRep; i += blockDim.x) {
     const uint32_t b = (uint32_t)i / kMRep;
-    const float ve = even_value<0>(b), vo = odd_value<0>(b);
+    const float2 pv = pair_value<0>(b);
+    const float ve = pv.x, vo = pv.y;
     const uint32_t he = f32_to_bf16_rne(ve), ho = f32_to_bf16_rne(vo);
     const uint32_t le = f32_to_bf16_rne(ve - bf16_to_f32(he));
     const uint32_t lo = f32_to_bf16_rne(vo - bf16_to_f32(ho));
@@ -55,7 +56,8 @@ __device__ inline void build_nf4_bf16_table(uint2 *tab) {
 __device__ inline void build_e2m1_f32_table(uint2 *tab) {
   for (int i = threadIdx.x; i < 256 * kMRep; i += blockDim.x) {
     const uint32_t b = (uint32_t)i / kMRep;
-    tab[i] = make_uint2(__float_as_uint(even_value<1>(b)), __float_as_uint(odd_value<1>(b)));
+    const float2 pv = pair_value<1>(b);
+    tab[i] = make_uint2(__float_as_uint(pv.x), __float_as_uint(pv.y));
   }
 }
 

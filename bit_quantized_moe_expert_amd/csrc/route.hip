@@ -261,7 +261,7 @@ __device__ inline int block_scan_1024(int v, int *total) {
 
 // Tiles of at most bm rows for every group; single workgroup of 1024 threads.
 __device__ void build_tiles(const int32_t *grp_expert, const int32_t *grp_row0,
-                            const int32_t *grp_rows, int n_grp, int bm, int4 *tiles,
+                            const int32_t *grp_rows, int n_grp, int bm, int max_tiles, int4 *tiles,
                             int32_t *n_tiles_out) {
   __shared__ int s_total;
   __shared__ int s_carry;
@@ -273,7 +273,7 @@ __device__ void build_tiles(const int32_t *grp_expert, const int32_t *grp_row0,
     const int nt = (rows + bm - 1) / bm;
     const int ex = block_scan_1024(nt, &s_total);
     const int base = s_carry + ex;
-    for (int i = 0; i < nt; ++i) {
+    for (int i = 0; i < nt && base + i < max_tiles; ++i) {
       const int r0 = i * bm;
       tiles[base + i] = make_int4(grp_expert[g], grp_row0[g] + r0, min(bm, rows - r0), 0);
     }
@@ -281,13 +281,14 @@ __device__ void build_tiles(const int32_t *grp_expert, const int32_t *grp_row0,
     if (threadIdx.x == 0) s_carry += s_total;
     __syncthreads();
   }
-  if (threadIdx.x == 0) *n_tiles_out = s_carry;
+  if (threadIdx.x == 0) *n_tiles_out = min(s_carry, max_tiles);
 }
 
 // Grouping, stage 2 (single workgroup): flat exclusive scan of the histogram,
 // expert offsets, the compacted list of non-empty experts, and the MFMA tiles.
 __global__ __launch_bounds__(1024) void k_group_scan(int32_t *__restrict__ hist, int E, int nchunks,
-                                                     int R, int bm, int32_t *__restrict__ off,
+                                                     int R, int bm, int max_tiles,
+                                                     int32_t *__restrict__ off,
                                                      int32_t *__restrict__ grp_expert,
                                                      int32_t *__restrict__ grp_row0,
                                                      int32_t *__restrict__ grp_rows,
@@ -317,7 +318,7 @@ __global__ __launch_bounds__(1024) void k_group_scan(int32_t *__restrict__ hist,
       off[e] = o;
     }
     const int slot = block_scan_1024(c > 0 ? 1 : 0, &s_total);
-    if (c > 0) {
+    if (c > 0 && cnt_total + slot < E) {
       grp_expert[cnt_total + slot] = e;
       grp_row0[cnt_total + slot] = o;
       grp_rows[cnt_total + slot] = c;
@@ -330,7 +331,7 @@ __global__ __launch_bounds__(1024) void k_group_scan(int32_t *__restrict__ hist,
     counters[0] = cnt_total;
   }
   __syncthreads();
-  build_tiles(grp_expert, grp_row0, grp_rows, cnt_total, bm, tiles, counters + 1);
+  build_tiles(grp_expert, grp_row0, grp_rows, cnt_total, bm, max_tiles, tiles, counters + 1);
 }
 
 // Grouping, stage 3: stable scatter. Within a chunk, a slot's rank among equal
@@ -361,14 +362,105 @@ __global__ __launch_bounds__(256) void k_group_scatter(const int32_t *__restrict
   if (valid) {
     int pos = base[(int64_t)e * nchunks + blockIdx.x] + rank;
     for (int w = 0; w < wave; ++w) pos += cnt[w][e];
-    sorted_slots[pos] = s;
-    slot_pos[s] = pos;
+    if (pos >= 0 && pos < R) {  // always true for a consistent histogram
+      sorted_slots[pos] = s;
+      slot_pos[s] = pos;
+    }
   }
+}
+
+// ---------------------------------------------------------------------------
+// Decode-sized routing tail (T <= kSmallT tokens, E <= kSmallE experts) in one
+// workgroup of 1024 threads: top-k by rank (each (token, expert) counts the
+// experts ordered before it, in parallel), softmax, counting sort with exact
+// stable ranks, the non-empty expert list and the MFMA tiles.
+// ---------------------------------------------------------------------------
+constexpr int kSmallT = 8;
+constexpr int kSmallE = 256;
+
+__global__ __launch_bounds__(1024) void k_route_tail_small(const float *__restrict__ L, int T, int E,
+                                                           int k, int renorm, int bm, int max_tiles,
+                                                           RouteBufs o) {
+  __shared__ float Ls[kSmallT * kSmallE];
+  __shared__ int sel_id[kSmallT * kMaxTopK];
+  __shared__ float sel_v[kSmallT * kMaxTopK];
+  __shared__ int cnt[kSmallE];
+  __shared__ int offs[kSmallE];
+  __shared__ int s_total;
+  const int tid = threadIdx.x;
+  const int TE = T * E, R = T * k;
+  for (int i = tid; i < TE; i += 1024) Ls[i] = L[i];
+  for (int e = tid; e < E; e += 1024) cnt[e] = 0;
+  __syncthreads();
+  for (int i = tid; i < TE; i += 1024) {
+    const int t = i / E, e = i - t * E;
+    const float v = Ls[i];
+    const float *row = Ls + t * E;
+    int rank = 0;
+    for (int f = 0; f < E; ++f) {
+      const float u = row[f];
+      rank += (u > v || (u == v && f < e)) ? 1 : 0;
+    }
+    if (rank < k) {
+      sel_id[t * k + rank] = e;
+      sel_v[t * k + rank] = v;
+    }
+  }
+  __syncthreads();
+  if (tid < R) {
+    const int t = tid / k, j = tid - t * k;
+    const float v0 = sel_v[t * k];
+    float w;
+    if (renorm) {
+      float sum = 0.0f;
+      for (int q = 0; q < k; ++q) sum += expf(sel_v[t * k + q] - v0);
+      w = expf(sel_v[tid] - v0) / sum;
+    } else {
+      float sum = 0.0f;
+      for (int f = 0; f < E; ++f) sum += expf(Ls[t * E + f] - v0);
+      w = expf(sel_v[tid] - v0) / sum;
+    }
+    o.topk_ids[tid] = sel_id[tid];
+    o.topk_w[tid] = w;
+    atomicAdd(&cnt[sel_id[tid]], 1);
+  }
+  __syncthreads();
+  const int c = tid < E ? cnt[tid] : 0;
+  const int ex = block_scan_1024(c, &s_total);
+  if (tid < E) {
+    offs[tid] = ex;
+    o.expert_offsets[tid] = ex;
+  }
+  if (tid == 0) o.expert_offsets[E] = R;
+  const int slot = block_scan_1024(c > 0 ? 1 : 0, &s_total);
+  if (c > 0) {
+    o.grp_expert[slot] = tid;
+    o.grp_row0[slot] = ex;
+    o.grp_rows[slot] = c;
+  }
+  if (tid == 0) o.counters[0] = s_total;
+  if (tid < R) {  // stable position: earlier slots routed to the same expert
+    const int e = sel_id[tid];
+    int rank = 0;
+    for (int q = 0; q < tid; ++q) rank += sel_id[q] == e ? 1 : 0;
+    const int pos = offs[e] + rank;
+    o.sorted_slots[pos] = tid;
+    o.slot_pos[tid] = pos;
+  }
+  const int ngrp = s_total;
+  __syncthreads();
+  build_tiles(o.grp_expert, o.grp_row0, o.grp_rows, ngrp, bm, max_tiles, o.tiles, o.counters + 1);
 }
 
 hipError_t launch_route(const float *logits, int T, int E, int k, int renorm, const RouteBufs &rb,
                         int bm, hipStream_t s) {
   const int R = T * k;
+  if (T <= kSmallT && E <= kSmallE) {
+    const int max_tiles = (int)cdiv(R, bm) + (R < E ? R : E);
+    hipLaunchKernelGGL(k_route_tail_small, dim3(1), dim3(1024), 0, s, logits, T, E, k, renorm, bm,
+                       max_tiles, rb);
+    return hipGetLastError();
+  }
   const dim3 tk((unsigned)cdiv(T, 4));
   if (E <= 64)
     hipLaunchKernelGGL(k_topk<1>, tk, dim3(256), 0, s, logits, T, E, k, renorm, rb.topk_ids, rb.topk_w);
@@ -383,8 +475,9 @@ hipError_t launch_route(const float *logits, int T, int E, int k, int renorm, co
   const int nchunks = (int)cdiv(R, kChunk);
   hipLaunchKernelGGL(k_group_hist, dim3(nchunks), dim3(256), 0, s, rb.topk_ids, R, E, nchunks,
                      rb.chunk_hist);
+  const int max_tiles = (int)cdiv(R, bm) + (R < E ? R : E);
   hipLaunchKernelGGL(k_group_scan, dim3(1), dim3(1024), 0, s, rb.chunk_hist, E, nchunks, R, bm,
-                     rb.expert_offsets, rb.grp_expert, rb.grp_row0, rb.grp_rows, rb.counters,
+                     max_tiles, rb.expert_offsets, rb.grp_expert, rb.grp_row0, rb.grp_rows, rb.counters,
                      rb.tiles);
   hipLaunchKernelGGL(k_group_scatter, dim3(nchunks), dim3(256), 0, s, rb.topk_ids, R, E, nchunks,
                      rb.chunk_hist, rb.sorted_slots, rb.slot_pos);
@@ -398,6 +491,7 @@ hipError_t launch_route(const float *logits, int T, int E, int k, int renorm, co
 __global__ __launch_bounds__(1024) void k_groups_from_offsets(const int32_t *__restrict__ goff,
                                                               const int32_t *__restrict__ gexp,
                                                               int G, int R, int E, int bm,
+                                                              int max_tiles,
                                                               int32_t *__restrict__ grp_expert,
                                                               int32_t *__restrict__ grp_row0,
                                                               int32_t *__restrict__ grp_rows,
@@ -415,7 +509,7 @@ __global__ __launch_bounds__(1024) void k_groups_from_offsets(const int32_t *__r
   }
   __syncthreads();
   if (threadIdx.x == 0) counters[0] = G;
-  build_tiles(grp_expert, grp_row0, grp_rows, G, bm, tiles, counters + 1);
+  build_tiles(grp_expert, grp_row0, grp_rows, G, bm, max_tiles, tiles, counters + 1);
 }
 
 __global__ void k_fill_i32(int32_t *p, int n, int v) {
@@ -431,8 +525,9 @@ hipError_t launch_fill_i32(int32_t *p, int n, int v, hipStream_t s) {
 
 hipError_t launch_groups_from_offsets(const int32_t *goff, const int32_t *gexp, int G, int R,
                                       int E, const RouteBufs &rb, int bm, hipStream_t s) {
+  const int max_tiles = (int)cdiv(R, bm) + G;
   hipLaunchKernelGGL(k_groups_from_offsets, dim3(1), dim3(1024), 0, s, goff, gexp, G, R, E, bm,
-                     rb.grp_expert, rb.grp_row0, rb.grp_rows, rb.counters, rb.tiles);
+                     max_tiles, rb.grp_expert, rb.grp_row0, rb.grp_rows, rb.counters, rb.tiles);
   return hipGetLastError();
 }
 
