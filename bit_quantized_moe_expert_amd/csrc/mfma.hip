@@ -6,8 +6,11 @@
 // ...", section "Supported scope"), used once per-expert row counts make it a
 // dense contraction. Design for gfx950:
 //  - tiles of up to 128 routed rows of one expert (from the device tile
-//    table) by 128 weight rows, K in steps of 64 (one NF4 absmax block);
-//    4 waves, each 64 x 64 as 2 x 2 blocks of v_mfma_f32_32x32x16_bf16;
+//    table) by 256 weight rows, K in steps of 64 (one NF4 absmax block);
+//    8 waves, each 64 x 64 as 2 x 2 blocks of v_mfma_f32_32x32x16_bf16;
+//  - the activation tile is double-buffered in LDS and the next K-step's
+//    activation and weight loads are issued before the current step's MFMAs,
+//    so one barrier per step finds them mostly landed;
 //  - A rows are gathered (token of each routed slot) into LDS as bf16; fp32
 //    activations (h of the down projection) are split into bf16 hi + lo;
 //  - each lane's B operand is 8 consecutive k of one weight row; the K order
@@ -32,43 +35,48 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 constexpr int kBM = kMfmaBM;  // 128
 constexpr int kBK = 64;
 constexpr int kApad = 72;     // bf16 per LDS row of A (64 + 8 padding)
-constexpr int kMRep = 16;     // LDS table replicas
 
 __device__ inline bf16x8_t as_bf16x8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
   const uint4 v = make_uint4(a, b, c, d);
   return __builtin_bit_cast(bf16x8_t, v);
 }
 
-// NF4: byte -> (bf16 hi of even, bf16 hi of odd | bf16 lo of even, lo of odd).
-__device__ inline void build_nf4_bf16_table(uint2 *tab) {
-  for (int i = threadIdx.x; i < 256 * kMRep; i += blockDim.x) {
-    const uint32_t b = (uint32_t)i / kMRep;
-    const float2 pv = pair_value<0>(b);
-    const float ve = pv.x, vo = pv.y;
-    const uint32_t he = f32_to_bf16_rne(ve), ho = f32_to_bf16_rne(vo);
-    const uint32_t le = f32_to_bf16_rne(ve - bf16_to_f32(he));
-    const uint32_t lo = f32_to_bf16_rne(vo - bf16_to_f32(ho));
-    tab[i] = make_uint2(he | (ho << 16), le | (lo << 16));
-  }
-}
+// LDS decode table at LDS address 0: entry for byte b = 32 replicas of 8
+// bytes (256 B), so entry (b, lane & 31) sits at byte offset b * 256 + 8 *
+// (lane & 31), one v_perm_b32 away from the code word (tab_offset), and the
+// 32 lanes of a half-wave read distinct banks whatever the codes.
+// NF4 entry: (bf16 hi of even | hi of odd << 16, bf16 lo of even | lo of odd
+// << 16), hi = RNE bf16 of the fp32 codebook value, lo = RNE bf16 of the rest.
+// MXFP4 entry: (even value, odd value) as fp32.
+constexpr int kTabBytes = 256 * 32 * 8;
 
-// MXFP4: byte -> (even value, odd value) as fp32.
-__device__ inline void build_e2m1_f32_table(uint2 *tab) {
-  for (int i = threadIdx.x; i < 256 * kMRep; i += blockDim.x) {
-    const uint32_t b = (uint32_t)i / kMRep;
-    const float2 pv = pair_value<1>(b);
-    tab[i] = make_uint2(__float_as_uint(pv.x), __float_as_uint(pv.y));
+template <int FMT>
+__device__ inline void build_mfma_table(uint4 *tab) {
+  for (int f = threadIdx.x; f < kTabBytes / 16; f += blockDim.x) {
+    const uint32_t b = (uint32_t)f >> 4;   // 16 words of two replicas per entry
+    const float2 pv = pair_value<FMT>(b);
+    uint2 v;
+    if (FMT == 0) {
+      const uint32_t he = f32_to_bf16_rne(pv.x), ho = f32_to_bf16_rne(pv.y);
+      const uint32_t le = f32_to_bf16_rne(pv.x - bf16_to_f32(he));
+      const uint32_t lo = f32_to_bf16_rne(pv.y - bf16_to_f32(ho));
+      v = make_uint2(he | (ho << 16), le | (lo << 16));
+    } else {
+      v = make_uint2(__float_as_uint(pv.x), __float_as_uint(pv.y));
+    }
+    tab[f] = make_uint4(v.x, v.y, v.x, v.y);
   }
 }
 
 template <int FMT, int EPI, int AF32>
-__global__ __launch_bounds__(256, 2) void k_mfma(GemmArgs p, int ntn, int per) {
-  __shared__ __attribute__((aligned(16))) uint16_t Ahi[kBM * kApad];
-  __shared__ __attribute__((aligned(16))) uint16_t Alo[AF32 ? kBM * kApad : 8];
-  __shared__ uint2 tab_all[256 * kMRep];
+__global__ __launch_bounds__(512) void k_mfma(GemmArgs p, int ntn, int per) {
+  constexpr int ABUF = kBM * kApad * 2;               // bytes per A buffer
+  constexpr int NBUF = AF32 ? 4 : 2;                  // hi[2] (+ lo[2])
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kTabBytes + NBUF * ABUF];
 
   // XCD-aware order: hardware XCD = blockIdx.x % 8; give each XCD a contiguous
-  // run of (n-tile major, tile minor) work.
+  // run of (n-tile major, tile minor) work, so the M-tiles of one expert and
+  // one weight tile share that XCD's L2.
   const int L = blockIdx.x;
   const int Lp = (L & 7) * per + (L >> 3);
   if (Lp >= p.max_tiles * ntn) return;
@@ -77,46 +85,105 @@ __global__ __launch_bounds__(256, 2) void k_mfma(GemmArgs p, int ntn, int per) {
   const int4 tile = p.tiles[ti];  // expert, row0, rows
   const int e = tile.x, trow0 = tile.y, trows = tile.z;
 
-  if (FMT == 0)
-    build_nf4_bf16_table(tab_all);
-  else
-    build_e2m1_f32_table(tab_all);
+  build_mfma_table<FMT>(reinterpret_cast<uint4 *>(smem));
+  auto abuf = [&](int hi_lo, int buf) -> uint16_t * {
+    return reinterpret_cast<uint16_t *>(smem + kTabBytes + (hi_lo * 2 + buf) * ABUF);
+  };
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
-  const int wm = wave & 1, wn = wave >> 1;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int wm = wave & 1, wn = wave >> 1;           // 2 x 4 waves, 64 x 64 each
   const int g = lane >> 5, l32 = lane & 31;
-  const uint2 *tab = tab_all + (lane & (kMRep - 1));
+  const uint32_t lanebyte = (uint32_t)l32 * 8;
 
   const int64_t N = p.N, K = p.K;
   const int64_t ncol = (EPI == EPI_SWIGLU) ? N / 2 : N;
   int64_t colbase, nrow[2];
   if (EPI == EPI_SWIGLU) {
-    colbase = (int64_t)nt * 64 + wn * 32;
+    colbase = (int64_t)nt * 128 + wn * 32;
     nrow[0] = colbase + l32;          // gate row
     nrow[1] = ncol + colbase + l32;   // up row
   } else {
-    colbase = (int64_t)nt * 128 + wn * 64;
+    colbase = (int64_t)nt * 256 + wn * 64;
     nrow[0] = colbase + l32;
     nrow[1] = colbase + 32 + l32;
   }
   bool nvalid[2];
   nvalid[0] = (EPI == EPI_SWIGLU) ? (colbase + l32 < ncol) : (nrow[0] < N);
   nvalid[1] = (EPI == EPI_SWIGLU) ? (colbase + l32 < ncol) : (nrow[1] < N);
+  const int64_t nrow_c[2] = {nvalid[0] ? nrow[0] : 0, nvalid[1] ? nrow[1] : 0};
 
   const int64_t rowbytes = K / 2;
   const uint8_t *Be = p.B + (int64_t)e * N * rowbytes;
   const int64_t sc_per_row = K / Fmt<FMT>::kBlock;
   const int64_t sc_base = (int64_t)e * N * sc_per_row;
 
-  // A-tile row owned by this thread for the LDS fill
-  const int am = tid >> 1, ahf = tid & 1;
+  // A-tile slice owned by this thread for the LDS fill: row am, 16 elements
+  // starting at k0 + 16 * aq. Rows past the tile read a valid row (the tile's
+  // first) and are zeroed when stored.
+  const int am = tid >> 2, aq = tid & 3;
   const bool arow_ok = am < trows;
-  int64_t arow = 0;
-  if (arow_ok) {
-    const int r = trow0 + am;
+  int64_t arow;
+  {
+    const int r = trow0 + (arow_ok ? am : 0);
     arow = p.a_row_of ? (int64_t)(p.a_row_of[r] / p.a_div) : (int64_t)r;
   }
+  constexpr int AW = AF32 ? 4 : 2;                    // 16-byte words per thread
+  uint4 areg[AW];
+  bool a_ok = false;
+  auto load_a = [&](int64_t k0) {
+    const int64_t kk = k0 + 16 * aq;
+    a_ok = arow_ok && kk < K;
+    const int64_t kc = kk < K ? kk : 0;
+    const uint4 *src = AF32 ? reinterpret_cast<const uint4 *>(reinterpret_cast<const float *>(p.a) + arow * K + kc)
+                            : reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(p.a) + arow * K + kc);
+#pragma unroll
+    for (int i = 0; i < AW; ++i) areg[i] = src[i];
+  };
+  auto store_a = [&](int buf) {
+    uint16_t *dh = abuf(0, buf) + am * kApad + 16 * aq;
+    if (AF32) {
+      uint16_t *dl = abuf(1, buf) + am * kApad + 16 * aq;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t f[4] = {areg[i].x, areg[i].y, areg[i].z, areg[i].w};
+        uint32_t hb[4], lb[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t hi = a_ok ? (f[q] & 0xffff0000u) : 0u;  // truncated hi
+          hb[q] = hi >> 16;
+          lb[q] = a_ok ? f32_to_bf16_rne(__uint_as_float(f[q]) - __uint_as_float(hi)) : 0u;
+        }
+        *reinterpret_cast<uint2 *>(dh + 4 * i) = make_uint2(hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16));
+        *reinterpret_cast<uint2 *>(dl + 4 * i) = make_uint2(lb[0] | (lb[1] << 16), lb[2] | (lb[3] << 16));
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        *reinterpret_cast<uint4 *>(dh + 8 * i) = a_ok ? areg[i] : make_uint4(0, 0, 0, 0);
+    }
+  };
+  // B: one 16-byte chunk of codes per lane and N-block, k in [k0 + 32 g, +32),
+  // plus the raw scale and whether it counts. The scale is masked only when it
+  // is consumed, a K-step later, so nothing waits on these loads early.
+  auto load_b = [&](int64_t k0, uint4 *bq, uint32_t *braw, bool *bok) {
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const int64_t kk = k0 + 32 * g;
+      bok[b] = nvalid[b] && kk < K;
+      const int64_t kc = kk < K ? kk : 0;
+      bq[b] = *reinterpret_cast<const uint4 *>(Be + nrow_c[b] * rowbytes + kc / 2);
+      const int64_t sidx = FMT == 0 ? (k0 < K ? k0 / 64 : 0) : kc / 32;
+      if (FMT == 0)
+        braw[b] = reinterpret_cast<const uint32_t *>(p.B_scale)[sc_base + nrow_c[b] * sc_per_row + sidx];
+      else
+        braw[b] = reinterpret_cast<const uint8_t *>(p.B_scale)[sc_base + nrow_c[b] * sc_per_row + sidx];
+    }
+  };
+  auto scale_of = [&](uint32_t raw, bool ok) -> float {
+    const float v = FMT == 0 ? __uint_as_float(raw) : e8m0_to_f32(raw);
+    return ok ? v : 0.0f;
+  };
 
   f32x16_t C[2][2];
 #pragma unroll
@@ -126,57 +193,18 @@ __global__ __launch_bounds__(256, 2) void k_mfma(GemmArgs p, int ntn, int per) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) C[i][j][v] = 0.0f;
 
-  for (int64_t k0 = 0; k0 < K; k0 += kBK) {
-    // ---- A tile -> LDS: this thread fills row am, k in [k0 + 32 ahf, +32)
-    {
-      const int64_t kk = k0 + 32 * ahf;
-      const bool ok = arow_ok && kk < K;
-      uint16_t *dh = Ahi + am * kApad + 32 * ahf;
-      if (AF32) {
-        uint16_t *dl = Alo + am * kApad + 32 * ahf;
-        const float4 *src = reinterpret_cast<const float4 *>(
-            reinterpret_cast<const float *>(p.a) + arow * K + kk);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          float4 v = ok ? src[i] : make_float4(0.f, 0.f, 0.f, 0.f);
-          const float f[4] = {v.x, v.y, v.z, v.w};
-          uint32_t hb[4], lb[4];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const uint32_t hi = __float_as_uint(f[q]) & 0xffff0000u;  // truncated hi
-            hb[q] = hi >> 16;
-            lb[q] = f32_to_bf16_rne(f[q] - __uint_as_float(hi));
-          }
-          *reinterpret_cast<uint2 *>(dh + 4 * i) = make_uint2(hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16));
-          *reinterpret_cast<uint2 *>(dl + 4 * i) = make_uint2(lb[0] | (lb[1] << 16), lb[2] | (lb[3] << 16));
-        }
-      } else {
-        const uint4 *src = reinterpret_cast<const uint4 *>(
-            reinterpret_cast<const uint16_t *>(p.a) + arow * K + kk);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          *reinterpret_cast<uint4 *>(dh + 8 * i) = ok ? src[i] : make_uint4(0, 0, 0, 0);
-      }
-    }
-    // ---- B: one 16-byte chunk of codes per lane and N-block: k in [k0 + 32 g, +32)
-    uint4 bq[2];
-    float bs[2];
-#pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      const int64_t kk = k0 + 32 * g;
-      if (nvalid[b] && kk < K) {
-        bq[b] = *reinterpret_cast<const uint4 *>(Be + nrow[b] * rowbytes + kk / 2);
-        const int64_t sidx = FMT == 0 ? (k0 / 64) : (kk / 32);
-        if (FMT == 0)
-          bs[b] = reinterpret_cast<const float *>(p.B_scale)[sc_base + nrow[b] * sc_per_row + sidx];
-        else
-          bs[b] = e8m0_to_f32(reinterpret_cast<const uint8_t *>(p.B_scale)[sc_base + nrow[b] * sc_per_row + sidx]);
-      } else {
-        bq[b] = make_uint4(0, 0, 0, 0);
-        bs[b] = 0.0f;
-      }
-    }
-    __syncthreads();
+  // One K-step on LDS buffer `cur` with codes bq and scales bs, prefetching
+  // the next step into (bqn, brn, bokn) and the other LDS buffer.
+  auto step = [&](int64_t k0, int cur, const uint4 *bq, const float *bs, uint4 *bqn, uint32_t *brn, bool *bokn) {
+    // Next step's loads fly while this step computes. They are issued (from
+    // clamped, valid addresses) and stored even after the last step, so no
+    // branch splits the load/wait bookkeeping; the extra buffer is unused.
+    const bool more = k0 + kBK < K;
+    load_a(k0 + kBK);
+    load_b(k0 + kBK, bqn, brn, bokn);
+    __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the MFMAs
+    const uint16_t *Ah = abuf(0, cur);
+    const uint16_t *Al = abuf(1, AF32 ? cur : 0);
 
     f32x16_t P[2][2];
 #pragma unroll
@@ -193,16 +221,16 @@ __global__ __launch_bounds__(256, 2) void k_mfma(GemmArgs p, int ntn, int per) {
       for (int mb = 0; mb < 2; ++mb) {
         const int row = wm * 64 + mb * 32 + l32;
         const int col = 32 * g + 8 * s;
-        ah[mb] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4 *>(Ahi + row * kApad + col));
+        ah[mb] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4 *>(Ah + row * kApad + col));
         if (AF32)
-          al[mb] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4 *>(Alo + row * kApad + col));
+          al[mb] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4 *>(Al + row * kApad + col));
       }
 #pragma unroll
       for (int b = 0; b < 2; ++b) {
         const uint32_t word = s == 0 ? bq[b].x : (s == 1 ? bq[b].y : (s == 2 ? bq[b].z : bq[b].w));
         uint2 t[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) t[q] = tab[((word >> (8 * q)) & 0xffu) * kMRep];
+        for (int q = 0; q < 4; ++q) t[q] = *reinterpret_cast<const uint2 *>(smem + tab_offset(word, lanebyte, q));
         if (FMT == 0) {
           const bf16x8_t bh = as_bf16x8(t[0].x, t[1].x, t[2].x, t[3].x);
           const bf16x8_t bl = as_bf16x8(t[0].y, t[1].y, t[2].y, t[3].y);
@@ -239,7 +267,31 @@ __global__ __launch_bounds__(256, 2) void k_mfma(GemmArgs p, int ntn, int per) {
 #pragma unroll
           for (int v = 0; v < 16; ++v) C[mb][b][v] = fmaf(bs[b], P[mb][b][v], C[mb][b][v]);
     }
+    __builtin_amdgcn_sched_barrier(0);  // the A store waits for its loads: keep it last
+    store_a(cur ^ 1);
     __syncthreads();
+    return more;
+  };
+
+  uint4 bq0[2], bq1[2];
+  uint32_t br0[2], br1[2];
+  bool bok0[2], bok1[2];
+  float bs0[2], bs1[2];
+  load_a(0);
+  load_b(0, bq0, br0, bok0);
+  store_a(0);
+  __syncthreads();
+  bs0[0] = scale_of(br0[0], bok0[0]);
+  bs0[1] = scale_of(br0[1], bok0[1]);
+
+  // Unrolled by two so the register sets alternate without copies.
+  for (int64_t k0 = 0;; k0 += 2 * kBK) {
+    if (!step(k0, 0, bq0, bs0, bq1, br1, bok1)) break;
+    bs1[0] = scale_of(br1[0], bok1[0]);
+    bs1[1] = scale_of(br1[1], bok1[1]);
+    if (!step(k0 + kBK, 1, bq1, bs1, bq0, br0, bok0)) break;
+    bs0[0] = scale_of(br0[0], bok0[0]);
+    bs0[1] = scale_of(br0[1], bok0[1]);
   }
 
   // ---- epilogue. 32x32 accumulator: lane holds column l32, rows
@@ -280,11 +332,11 @@ __global__ __launch_bounds__(256, 2) void k_mfma(GemmArgs p, int ntn, int per) {
 template <int FMT, int EPI, int AF32>
 static hipError_t launch_mfma_t(const GemmArgs &g, hipStream_t s) {
   const int64_t ncol = (EPI == EPI_SWIGLU) ? g.N / 2 : g.N;
-  const int ntn = (int)((EPI == EPI_SWIGLU) ? cdiv(ncol, 64) : cdiv(ncol, 128));
+  const int ntn = (int)((EPI == EPI_SWIGLU) ? cdiv(ncol, 128) : cdiv(ncol, 256));
   const int64_t total = (int64_t)g.max_tiles * ntn;
   const int64_t padded = cdiv(total, 8) * 8;
   const int per = (int)(padded / 8);
-  hipLaunchKernelGGL((k_mfma<FMT, EPI, AF32>), dim3((unsigned)padded), dim3(256), 0, s, g, ntn, per);
+  hipLaunchKernelGGL((k_mfma<FMT, EPI, AF32>), dim3((unsigned)padded), dim3(512), 0, s, g, ntn, per);
   return hipGetLastError();
 }
 
