@@ -35,7 +35,54 @@ def parse():
     ap.add_argument("--graph", type=int, default=1, help="1: time HIP-graph replays as well")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain elementwise copy of MIB MiB (read + write once) five "
+                         "times, for scaling the FETCH_SIZE / WRITE_SIZE counters, and exit")
     return ap.parse_args()
+
+
+def copy_calibration(mib):
+    """A plain copy kernel of known size: torch.neg reads n fp32 and writes n fp32."""
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration": {"kernel": "torch.neg fp32", "read_bytes": 4 * n,
+                                           "write_bytes": 4 * n, "launches": 5}}), flush=True)
+
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+# Sources a kernel's code depends on; their hash ties a stored counter record
+# (profiles/traffic.json) to the kernel it was measured on.
+KERNEL_SOURCES = {"small": ["gemv.hip", "common.h", "internal.h"],
+                  "mfma": ["mfma.hip", "common.h", "internal.h"]}
+
+
+def kernel_source_hash(kind):
+    import hashlib
+    h = hashlib.sha256()
+    d = os.path.join(ROOT, "bit_quantized_moe_expert_amd", "csrc")
+    for f in KERNEL_SOURCES[kind]:
+        with open(os.path.join(d, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload, kind):
+    """HBM bytes per launch of the dominant kernel from the committed FETCH_SIZE /
+    WRITE_SIZE counter record, or None when there is none or the kernel's
+    sources changed since it was taken."""
+    try:
+        with open(os.path.join(ROOT, "profiles", "traffic.json")) as fh:
+            rec = json.load(fh)[workload]
+    except (OSError, KeyError, ValueError):
+        return None
+    if rec.get("source_hash") != kernel_source_hash(kind):
+        return None
+    return float(rec["hbm_bytes_per_launch"])
 
 
 def packed_bytes_per_expert(wl):
@@ -49,6 +96,9 @@ def packed_bytes_per_expert(wl):
 
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE={world}); "
@@ -153,7 +203,7 @@ def main():
 
     # ---- dominant kernel (gate_up + SwiGLU): HIP events around its launch on the same stream
     prof_steps = min(steps, 8 * nlayers)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(prof_steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(prof_steps)]
     for row in evs:
         for ev in row:
             ev.record(stream)
@@ -165,7 +215,9 @@ def main():
     stage = np.array([[r[0].elapsed_time(r[1]), r[1].elapsed_time(r[2]), r[2].elapsed_time(r[3])]
                       for r in evs])
     route_ms, gate_ms, down_ms = (float(v) for v in np.median(stage, axis=0))
-    gate_mean_ms = float(np.mean(stage[:, 1]))
+    # the gate_up kernel's own duration (events taken by its launch)
+    gate_kernel = np.array([r[4].elapsed_time(r[5]) for r in evs])
+    gate_mean_ms = float(np.mean(gate_kernel))
 
     # ---- work per step
     g_b, d_b = packed_bytes_per_expert(wl)
@@ -192,9 +244,11 @@ def main():
         roof = {"bound": "mfma", "achieved": gate_flops / (gate_mean_ms * 1e-3) / 1e12,
                 "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
+    kind = "small" if small else "mfma"
+    roof["traffic"] = measured_traffic(wl.name if T == wl.tokens[0] else f"{wl.name}_T{T}", kind)
     roof["kernel"] = "k_gemv<SwiGLU> (gate_up)" if small else "k_mfma<SwiGLU> (gate_up)"
     roof["kernel_ms_mean"] = gate_mean_ms
+    roof["kernel_source_hash"] = kernel_source_hash(kind)
 
     # ---- CPU baseline: the fp64 oracle on a bounded sample of the same workload
     cpu = None
@@ -213,7 +267,8 @@ def main():
         "effective_packed_GBps": step_bytes / (ms * 1e-3) / 1e9,
         "algorithmic_TFLOPs": flops / (ms * 1e-3) / 1e12,
         "active_experts_per_step": active,
-        "stage_ms_median": {"route": route_ms, "gate_up": gate_ms, "down_combine": down_ms},
+        "stage_ms_median": {"route": route_ms, "gate_up_kernel": float(np.median(gate_kernel)),
+                            "down_combine": down_ms},
         "roofline": roof,
         "cpu_baseline": cpu,
     }

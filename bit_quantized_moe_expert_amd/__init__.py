@@ -50,6 +50,13 @@ def lib() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise RuntimeError(f"{LIB_PATH} is missing: build it with "
                            "`python -m bit_quantized_moe_expert_amd.build`")
+    # The library must run on the same HIP runtime as torch, which owns the
+    # device memory and streams it is handed. torch ships its own
+    # libamdhip64.so.7; importing torch first makes the dynamic loader bind this
+    # library's libamdhip64.so.7 dependency to that copy instead of loading a
+    # second runtime from the system ROCm (two runtimes in one process do not
+    # share devices).
+    import torch  # noqa: F401
     L = ctypes.CDLL(LIB_PATH)
     vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
     sig = {
@@ -292,8 +299,11 @@ class Forward:
 
 
     def profiled(self, x, out, events):
-        """Same computation; records 4 caller HIP events (handles) between stages."""
-        arr = (ctypes.c_void_p * 4)(*events)
+        """Same computation with 6 caller HIP event handles: [0..3] recorded between
+        stages, [4], [5] the gate_up kernel's own start and end."""
+        if len(events) != 6:
+            raise ValueError("profiled() takes 6 events")
+        arr = (ctypes.c_void_p * 6)(*events)
         _check(lib().nf4moe_moe_forward_profiled(ctypes.byref(self.st), _ptr(x), x.shape[0], _ptr(out),
                                                  self.wsp, self.nb, _stream(), arr))
         return out

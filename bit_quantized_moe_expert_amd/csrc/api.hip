@@ -399,6 +399,10 @@ static nf4moe_status_t forward_impl(const nf4moe_layer_t *layer, const uint16_t 
     g.route_out = fc.rb;
   }
   const int ms = T == 1 ? 1 : 4;
+  if (events) {  // the gate_up kernel's own start / end timestamps
+    g.ev_start = events[4];
+    g.ev_stop = events[5];
+  }
   e = use == NF4MOE_PATH_SMALL_M ? launch_gemv_grouped(g, ms, s) : launch_mfma_grouped(g, s);
   if (e != hipSuccess) return hip_status(e, "gate_up launch");
   if ((e = mark(2)) != hipSuccess) return hip_status(e, "event record");
@@ -411,6 +415,7 @@ static nf4moe_status_t forward_impl(const nf4moe_layer_t *layer, const uint16_t 
   } else {
     GemmArgs d = g;
     d.route_logits = nullptr;
+    d.ev_start = d.ev_stop = nullptr;
     d.a = fc.h;
     d.a_is_f32 = 1;
     d.a_row_of = nullptr;

@@ -391,7 +391,7 @@ static void launch_gemv_t(const GemmArgs &g, hipStream_t s) {
   constexpr int UPW = WR / ((EPI == EPI_SWIGLU) ? 2 : 1);
   const int64_t ncol = (EPI == EPI_SWIGLU) ? g.N / 2 : g.N;
   const dim3 grid((unsigned)cdiv(ncol, kGemvWaves * UPW), (unsigned)(ROUTE > 0 ? g.route_k : g.max_grp));
-  hipLaunchKernelGGL((k_gemv<FMT, EPI, AF32, LPR, NJ, MS, ROUTE>), grid, dim3(kGemvWaves * 64), 0, s, g);
+  NF4MOE_LAUNCH(g, (k_gemv<FMT, EPI, AF32, LPR, NJ, MS, ROUTE>), grid, dim3(kGemvWaves * 64), s, g);
 }
 
 template <int FMT, int EPI, int AF32, int LPR, int NJ>

@@ -1,6 +1,7 @@
 // Host-side declarations shared by the C ABI layer and the kernel files.
 #pragma once
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 #include <stddef.h>
 #include <stdint.h>
 
@@ -73,7 +74,20 @@ struct GemmArgs {
   const float *route_logits;
   int route_E, route_k, route_renorm;
   RouteBufs route_out;
+  // Optional timing: when set, the kernel is launched with these two HIP
+  // events, which take the kernel's own start and end timestamps.
+  void *ev_start, *ev_stop;
 };
+
+// Launch through hipExtLaunchKernelGGL when the arguments carry events.
+#define NF4MOE_LAUNCH(G, KERNEL, GRID, BLOCK, STREAM, ...)                                          \
+  do {                                                                                            \
+    if ((G).ev_start)                                                                             \
+      hipExtLaunchKernelGGL(KERNEL, GRID, BLOCK, 0, STREAM, (hipEvent_t)(G).ev_start,             \
+                            (hipEvent_t)(G).ev_stop, 0, __VA_ARGS__);                             \
+    else                                                                                          \
+      hipLaunchKernelGGL(KERNEL, GRID, BLOCK, 0, STREAM, __VA_ARGS__);                            \
+  } while (0)
 hipError_t launch_gemv_grouped(const GemmArgs &g, int ms_hint, hipStream_t s);
 hipError_t launch_mfma_grouped(const GemmArgs &g, hipStream_t s);
 

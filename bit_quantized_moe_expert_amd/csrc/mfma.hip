@@ -336,7 +336,7 @@ static hipError_t launch_mfma_t(const GemmArgs &g, hipStream_t s) {
   const int64_t total = (int64_t)g.max_tiles * ntn;
   const int64_t padded = cdiv(total, 8) * 8;
   const int per = (int)(padded / 8);
-  hipLaunchKernelGGL((k_mfma<FMT, EPI, AF32>), dim3((unsigned)padded), dim3(512), 0, s, g, ntn, per);
+  NF4MOE_LAUNCH(g, (k_mfma<FMT, EPI, AF32>), dim3((unsigned)padded), dim3(512), s, g, ntn, per);
   return hipGetLastError();
 }
 

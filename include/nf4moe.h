@@ -185,11 +185,13 @@ nf4moe_status_t nf4moe_moe_forward(const nf4moe_layer_t *layer, const uint16_t *
                                    void *ws, size_t ws_bytes, void *stream);
 
 /* nf4moe_moe_forward_profiled -- nf4moe_moe_forward (same kernels, same result,
- * no topk copies) that also records caller-created HIP events (hipEvent_t) on
- * `stream`: events[0] before the router, events[1] after routing + grouping,
- * events[2] after the gate_up + SwiGLU kernel, events[3] after the down
- * projection and combine. For measurement. Errors as for nf4moe_moe_forward,
- * plus INVALID_ARG for a NULL events array. */
+ * no topk copies) that also uses six caller-created timing HIP events
+ * (hipEvent_t, hipEventDefault flags) on `stream`: events[0] is recorded before
+ * the router, events[1] after routing + grouping, events[2] after the gate_up +
+ * SwiGLU kernel, events[3] after the down projection and combine; events[4] and
+ * events[5] are handed to the gate_up kernel's launch (hipExtLaunchKernelGGL)
+ * and so carry that kernel's own start and end times. For measurement. Errors
+ * as for nf4moe_moe_forward, plus INVALID_ARG for a NULL events array. */
 nf4moe_status_t nf4moe_moe_forward_profiled(const nf4moe_layer_t *layer, const uint16_t *x,
                                             int32_t T, uint16_t *out, void *ws, size_t ws_bytes,
                                             void *stream, void *const *events);
