@@ -138,22 +138,67 @@ __device__ inline uint64_t lanemask_lt() {
 }
 
 // ---------------------------------------------------------------------------
+// Codebook gather without memory: lane c (mod 16) of the wave holds the value
+// of code c, and ds_bpermute fetches it for any per-lane code. All 64 lanes
+// must be active when the gather runs (inactive source lanes read as 0).
+// ---------------------------------------------------------------------------
+template <int FMT>
+__device__ inline float codebook_lane() {
+  const uint32_t c = threadIdx.x & 15;
+  return FMT == 0 ? nf4_value_sel(c) : e2m1_value_sel(c);
+}
+__device__ inline float codebook_gather(float cb_lane, uint32_t code) {
+  return __int_as_float(__builtin_amdgcn_ds_bpermute((int)(code << 2), __float_as_int(cb_lane)));
+}
+// (value of the even-k code, value of the odd-k code) of a packed byte.
+template <int FMT>
+__device__ inline float2 pair_gather(float cb_lane, uint32_t b) {
+  return FMT == 0 ? make_float2(codebook_gather(cb_lane, b >> 4), codebook_gather(cb_lane, b & 15))
+                  : make_float2(codebook_gather(cb_lane, b & 15), codebook_gather(cb_lane, b >> 4));
+}
+
+// Barrier that orders LDS only: global loads (and stores) issued before it
+// stay in flight, unlike __syncthreads(), whose workgroup fence also covers
+// global memory and so waits for every outstanding vector memory operation.
+__device__ inline void lds_barrier() {
+  __builtin_amdgcn_sched_barrier(0);  // no work moves across it, so no early waits
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// ---------------------------------------------------------------------------
 // LDS decode table: byte -> (value of even-k code, value of odd-k code) as two
 // fp32, replicated kRep times so the lanes of one LDS access read distinct
 // banks. Entry (byte b, replica r) lives at float2 index b * kRep + r. Built by
-// `nthreads` threads starting at `first_thread` with register arithmetic only
-// (no memory latency); consecutive threads write consecutive 16-byte words so
-// the writes are conflict-free.
+// whole waves (`first_wave` .. `first_wave + nwaves - 1`) with codebook
+// gathers; consecutive threads write consecutive 16-byte words so the writes
+// are conflict-free. The caller synchronises before reading it.
 // ---------------------------------------------------------------------------
 template <int FMT, int kRep>
-__device__ inline void build_pair_table(float2 *tab, int first_thread, int nthreads) {
+__device__ inline void build_pair_table(float2 *tab, int first_wave, int nwaves) {
   constexpr int kWords = 256 * kRep / 2;  // float4 words, kRep / 2 per byte
   float4 *dst = reinterpret_cast<float4 *>(tab);
-  const int t = (int)threadIdx.x - first_thread;
-  if (t < 0 || t >= nthreads) return;
-  for (int f = t; f < kWords; f += nthreads) {  // consecutive lanes, consecutive words
-    const float2 v = pair_value<FMT>((uint32_t)(f / (kRep / 2)));
-    dst[f] = make_float4(v.x, v.y, v.x, v.y);
+  const int w = (int)(threadIdx.x >> 6) - first_wave;
+  if (w < 0 || w >= nwaves) return;       // uniform per wave
+  const int t = w * 64 + (int)(threadIdx.x & 63), nthreads = nwaves * 64;
+  const float cb = codebook_lane<FMT>();
+  // Gathers in batches of 8 words, all issued before the first wait; uniform
+  // trip count, so the gathers always see full waves.
+  for (int f0 = 0; f0 < kWords; f0 += 8 * nthreads) {
+    float2 v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int f = f0 + i * nthreads + t;
+      const int fc = f < kWords ? f : kWords - 1;
+      v[i] = pair_gather<FMT>(cb, (uint32_t)(fc / (kRep / 2)));
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int f = f0 + i * nthreads + t;
+      if (f < kWords) dst[f] = make_float4(v[i].x, v[i].y, v[i].x, v[i].y);
+    }
   }
 }
 

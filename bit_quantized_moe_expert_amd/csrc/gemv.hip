@@ -87,6 +87,7 @@ __device__ inline void chunk_dot(const char *tab, uint32_t lanebyte, uint4 q, co
 // a time. Weight and first activation loads are issued before the LDS table is
 // built, so the table build overlaps their latency.
 constexpr int kGemvWaves = 8;
+constexpr int kGemvWavesRoute = kGemvWaves;  // waves sharing the one-token ranking
 
 // Wave-loads (16 bytes per lane each) a wave keeps in flight: 8 / NJ, at most
 // 16 rows per wave, and 4 when four activation rows are held in registers.
@@ -96,91 +97,146 @@ constexpr int gemv_loads() {
   return a < b ? (a < c ? a : c) : (b < c ? b : c);
 }
 
-// Routing of a single token inside the gate_up kernel (wave 0): rank of each
-// expert under (logit descending, id ascending) from readlane broadcasts; the
-// k selected experts in ascending id order go to s_sorted_e. With publish set,
-// also writes every routing output (ids, weights, offsets, permutation, group
-// list, tiles) for the kernels that follow.
+// Routing of a single token inside the gate_up kernel, spread over the
+// kGemvWaves waves of a workgroup. Rank of expert e under (logit descending,
+// id ascending) = number of experts f ordered before it; wave w counts the f in
+// its slice of E / kGemvWaves ids (route_partial), the partial counts meet in
+// LDS across the workgroup barrier, and route_finish sums them, selects the k
+// experts, and returns the expert of group `gi` (the gi-th selected id in
+// ascending order). With publish set, wave 0 also writes every routing output
+// (ids, weights, offsets, permutation, group list, tiles) for the kernels that
+// follow.
 template <int EPL>
-__device__ inline void route_one_token(const GemmArgs &p, bool publish, int *s_sorted_e) {
+struct RouteToken {
+  float v[EPL];      // logit of expert lane + 64 j (-inf past E)
+  int rank[EPL];     // its rank (set by route_finish)
+  uint64_t sel[EPL]; // ballot of the selected experts (set by route_finish)
+};
+
+template <int EPL>
+__device__ inline RouteToken<EPL> route_load(const GemmArgs &p) {
+  RouteToken<EPL> r;
   const int lane = threadIdx.x & 63;
-  const int E = p.route_E, k = p.route_k;
-  float v[EPL];
-  int rank[EPL];
 #pragma unroll
   for (int j = 0; j < EPL; ++j) {
     const int e = lane + 64 * j;
-    v[j] = e < E ? p.route_logits[e] : -__builtin_inff();
-    rank[j] = 0;
+    r.v[j] = e < p.route_E ? p.route_logits[e] : -__builtin_inff();
+  }
+  return r;
+}
+
+template <int EPL>
+__device__ inline void route_partial(const GemmArgs &p, const RouteToken<EPL> &r, int wave,
+                                     int (*s_rank)[64 * EPL]) {
+  constexpr int S = 64 * EPL / kGemvWavesRoute;   // ids per wave slice
+  const int lane = threadIdx.x & 63;
+  const int E = p.route_E;
+  int cnt[EPL];
+#pragma unroll
+  for (int j = 0; j < EPL; ++j) cnt[j] = 0;
+  float uu[S];
+#pragma unroll
+  for (int i = 0; i < S; ++i) {                     // all loads first, clamped, no branches
+    const int f = wave * S + i;                     // wave-uniform
+    uu[i] = p.route_logits[f < E ? f : E - 1];
   }
 #pragma unroll
-  for (int jj = 0; jj < EPL; ++jj) {
-#pragma unroll 16
-    for (int src = 0; src < 64; ++src) {
-      const int f = src + 64 * jj;
-      if (f >= E) break;
-      const float u = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v[jj]), src));
+  for (int i = 0; i < S; ++i) {
+    const int f = wave * S + i;
+    const float u = f < E ? uu[i] : -__builtin_inff();
 #pragma unroll
-      for (int j = 0; j < EPL; ++j) {
-        const int e = lane + 64 * j;
-        rank[j] += (u > v[j] || (u == v[j] && f < e)) ? 1 : 0;
-      }
+    for (int j = 0; j < EPL; ++j) {
+      const int e = lane + 64 * j;
+      cnt[j] += (u > r.v[j] || (u == r.v[j] && f < e)) ? 1 : 0;
     }
   }
-  uint64_t sel[EPL];
-  int below = 0;  // selected experts with a smaller id, accumulated over j
-  float vmax = -__builtin_inff(), part = 0.0f, full = 0.0f;
+#pragma unroll
+  for (int j = 0; j < EPL; ++j) s_rank[wave][lane + 64 * j] = cnt[j];
+}
+
+template <int EPL>
+__device__ inline int route_finish(const GemmArgs &p, RouteToken<EPL> &r, int gi,
+                                   const int (*s_rank)[64 * EPL]) {
+  const int lane = threadIdx.x & 63;
+  const int E = p.route_E, k = p.route_k;
+  int *rank = r.rank;
+  uint64_t *sel = r.sel;
 #pragma unroll
   for (int j = 0; j < EPL; ++j) {
-    const int e = lane + 64 * j;
-    const bool chosen = e < E && rank[j] < k;
-    sel[j] = __ballot(chosen);
-    if (e < E && rank[j] == 0) vmax = v[j];
+    rank[j] = 0;
+#pragma unroll
+    for (int w = 0; w < kGemvWavesRoute; ++w) rank[j] += s_rank[w][lane + 64 * j];
+    sel[j] = __ballot(lane + 64 * j < E && rank[j] < k);
   }
-  vmax = wave_max(vmax);
+  // expert of group gi: the selected id with gi selected ids below it
+  int e_gi = 0, below = 0;
 #pragma unroll
   for (int j = 0; j < EPL; ++j) {
-    const int e = lane + 64 * j;
-    const bool chosen = e < E && rank[j] < k;
-    const float ex = e < E ? expf(v[j] - vmax) : 0.0f;
-    part += chosen ? ex : 0.0f;
-    full += ex;
+    const bool chosen = (sel[j] >> lane) & 1;
+    const uint64_t hit = __ballot(chosen && below + __popcll(sel[j] & lanemask_lt()) == gi);
+    if (hit) e_gi = 64 * j + __builtin_ctzll(hit);
+    below += __popcll(sel[j]);
   }
-  const float denom = wave_sum(p.route_renorm ? part : full);
+  return e_gi;
+}
+
+// Routing outputs of the token for the kernels that follow (one wave of one
+// workgroup calls it, after its own weight loads are in flight).
+template <int EPL>
+__device__ inline void route_publish(const GemmArgs &p, const RouteToken<EPL> &r) {
+  const int lane = threadIdx.x & 63;
+  const int E = p.route_E, k = p.route_k;
+  const int *rank = r.rank;
+  const uint64_t *sel = r.sel;
+  {
+    float vmax = -__builtin_inff(), part = 0.0f, full = 0.0f;
 #pragma unroll
-  for (int j = 0; j < EPL; ++j) {
-    const int e = lane + 64 * j;
-    const int pos_e = below + __popcll(sel[j] & lanemask_lt());  // selected ids < e
-    const bool chosen = e < E && rank[j] < k;
-    if (chosen) s_sorted_e[pos_e] = e;
-    if (publish) {
-      const RouteBufs &o = p.route_out;
+    for (int j = 0; j < EPL; ++j)
+      if (lane + 64 * j < E && rank[j] == 0) vmax = r.v[j];
+    vmax = wave_max(vmax);
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) {
+      const bool chosen = (sel[j] >> lane) & 1;
+      const float ex = lane + 64 * j < E ? expf(r.v[j] - vmax) : 0.0f;
+      part += chosen ? ex : 0.0f;
+      full += ex;
+    }
+    const float denom = wave_sum(p.route_renorm ? part : full);
+    const RouteBufs &o = p.route_out;
+    int bl = 0;
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) {
+      const int e = lane + 64 * j;
+      const int pos_e = bl + __popcll(sel[j] & lanemask_lt());  // selected ids < e
+      const bool chosen = (sel[j] >> lane) & 1;
       if (e < E) o.expert_offsets[e] = pos_e;
       if (chosen) {
-        const int r = rank[j];
-        o.topk_ids[r] = e;
-        o.topk_w[r] = expf(v[j] - vmax) / denom;
-        o.slot_pos[r] = pos_e;
-        o.sorted_slots[pos_e] = r;
+        const int rk = rank[j];
+        o.topk_ids[rk] = e;
+        o.topk_w[rk] = expf(r.v[j] - vmax) / denom;
+        o.slot_pos[rk] = pos_e;
+        o.sorted_slots[pos_e] = rk;
         o.grp_expert[pos_e] = e;
         o.grp_row0[pos_e] = pos_e;
         o.grp_rows[pos_e] = 1;
         o.tiles[pos_e] = make_int4(e, pos_e, 1, 0);
       }
+      bl += __popcll(sel[j]);
     }
-    below += __popcll(sel[j]);
-  }
-  if (publish && lane == 0) {
-    p.route_out.expert_offsets[E] = k;
-    p.route_out.counters[0] = k;
-    p.route_out.counters[1] = k;
+    if (lane == 0) {
+      o.expert_offsets[E] = k;
+      o.counters[0] = k;
+      o.counters[1] = k;
+    }
   }
 }
 
 // One workgroup = kGemvWaves waves; blockIdx.y = group, blockIdx.x = block of
-// output columns. The LDS table is built (and, for ROUTE > 0, the token routed)
-// before any weight load, so that each wave then consumes its rows as they
-// arrive: the workgroup barrier would otherwise wait for every load in flight.
+// output columns. Grouped (ROUTE = 0): the group's activation and weight loads
+// are issued first and the LDS table is built while they fly; the barrier
+// after it orders LDS only. One token (ROUTE > 0): the logits load, table build
+// and partial ranks come first, and the weight stream starts right after the
+// barrier, once every wave knows its expert.
 template <int FMT, int EPI, int AF32, int LPR, int NJ, int MS, int ROUTE>
 __global__ __launch_bounds__(kGemvWaves * 64) void k_gemv(GemmArgs p) {
   constexpr int RPL = 64 / LPR;
@@ -190,28 +246,37 @@ __global__ __launch_bounds__(kGemvWaves * 64) void k_gemv(GemmArgs p) {
   constexpr int UPW = WR / RPU;                      // output columns per wave
   static_assert(MS * UPW <= 64, "one lane per output");
   __shared__ float2 tab_all[256 * kGemvRep];
-  __shared__ int s_sorted_e[kMaxTopK];
+  __shared__ int s_rank[(ROUTE > 0 ? kGemvWavesRoute : 1)][64 * (ROUTE > 0 ? ROUTE : 1)];
 
   const int gi = blockIdx.y;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  int e, row0, rows;
+  RouteToken<(ROUTE > 0 ? ROUTE : 1)> rt;
   if constexpr (ROUTE > 0) {
     if (gi >= p.route_k) return;                     // uniform over the workgroup
-    if (wave == 0) route_one_token<ROUTE>(p, blockIdx.x == 0 && gi == 0, s_sorted_e);
+    rt = route_load<ROUTE>(p);                        // in flight during the table build
+    e = 0;
+    row0 = gi;
+    rows = 1;
   } else {
     const int ngrp = p.n_grp ? *p.n_grp : p.max_grp;
     if (gi >= ngrp) return;                          // uniform over the workgroup
-    if (p.grp_rows[gi] <= 0) return;
+    rows = p.grp_rows[gi];
+    if (rows <= 0) return;
+    e = p.grp_expert[gi];
+    row0 = p.grp_row0[gi];
   }
-  build_pair_table<FMT, kGemvRep>(tab_all, ROUTE > 0 ? 64 : 0,
-                                 ROUTE > 0 ? kGemvWaves * 64 - 64 : kGemvWaves * 64);
-  __syncthreads();
-
-  const int e = ROUTE > 0 ? s_sorted_e[gi] : p.grp_expert[gi];
-  const int row0 = ROUTE > 0 ? gi : p.grp_row0[gi];
-  const int rows = ROUTE > 0 ? 1 : p.grp_rows[gi];
   const int64_t ncol = (EPI == EPI_SWIGLU) ? p.N / 2 : p.N;
   const int64_t u0 = ((int64_t)blockIdx.x * kGemvWaves + wave) * UPW;
-  if (u0 >= ncol) return;                            // no barrier follows
+  const bool wave_live = u0 < ncol;                  // uniform per wave
+  if constexpr (ROUTE > 0) {
+    // Table build and partial ranks while the logits load; one barrier; then
+    // every wave knows its expert and starts the weight stream.
+    build_pair_table<FMT, kGemvRep>(tab_all, 0, kGemvWaves);
+    route_partial<ROUTE>(p, rt, wave, s_rank);
+    lds_barrier();
+    e = route_finish<ROUTE>(p, rt, gi, s_rank);
+  }
   const int sr = lane / LPR, li = lane % LPR;
   const int64_t nch = p.K / 32;                      // 16-byte chunks per row
   const int64_t rowbytes = p.K / 2;
@@ -283,6 +348,7 @@ __global__ __launch_bounds__(kGemvWaves * 64) void k_gemv(GemmArgs p) {
   uint4 wq[NL][NJ];
   float sc[NL][NJ];
   bool sok[NL][NJ];
+  int64_t wrow_of[NL];
 #pragma unroll
   for (int i = 0; i < NL; ++i) {
     const int q = i * RPL + sr;                      // position in the wave's row list
@@ -295,19 +361,42 @@ __global__ __launch_bounds__(kGemvWaves * 64) void k_gemv(GemmArgs p) {
       wrow = col;
     }
     const bool rok = col < ncol;
-    const int64_t wr = rok ? wrow : 0;
+    wrow_of[i] = rok ? wrow : 0;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) sok[i][j] = rok && li + (int64_t)LPR * j < nch;
+  }
+  // Scales of every row first (a few bytes each), then the code chunks in row
+  // order. All unconditional: no branch may split the in-order accounting.
+#pragma unroll
+  for (int i = 0; i < NL; ++i)
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
       const int64_t c = li + (int64_t)LPR * j;
-      const bool ok = rok && c < nch;
       const int64_t cc = c < nch ? c : 0;
-      wq[i][j] = *reinterpret_cast<const uint4 *>(Be + wr * rowbytes + cc * 16);
       const int64_t sidx = FMT == 0 ? (cc >> 1) : cc;
-      sc[i][j] = block_scale<FMT>(p.B_scale, sc_base + wr * sc_per_row + sidx);
-      sok[i][j] = ok;
+      sc[i][j] = block_scale<FMT>(p.B_scale, sc_base + wrow_of[i] * sc_per_row + sidx);
     }
-  }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int i = 0; i < NL; ++i)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int64_t c = li + (int64_t)LPR * j;
+      const int64_t cc = c < nch ? c : 0;
+      wq[i][j] = *reinterpret_cast<const uint4 *>(Be + wrow_of[i] * rowbytes + cc * 16);
+      __builtin_amdgcn_sched_barrier(0);  // keep row order
+    }
   __builtin_amdgcn_sched_barrier(0);  // every load is in flight before any wait
+  if constexpr (ROUTE > 0) {
+    if (blockIdx.x == 0 && gi == 0 && wave == 0) route_publish<ROUTE>(p, rt);
+  }
+  if constexpr (ROUTE == 0) {
+    // The table build overlaps the loads' latency; the barrier orders LDS
+    // only, so the loads stay in flight through it.
+    build_pair_table<FMT, kGemvRep>(tab_all, 0, kGemvWaves);
+    lds_barrier();
+  }
+  if (!wave_live) return;                            // no barrier follows
 
   const char *tab = reinterpret_cast<const char *>(tab_all);
   const uint32_t lanebyte = (uint32_t)(lane & (kGemvRep - 1)) * 8u;
@@ -488,8 +577,6 @@ __global__ __launch_bounds__(256) void k_down_combine(const float *__restrict__ 
                                                       uint16_t *__restrict__ out) {
   __shared__ float2 tab_all[256 * kGemvRep];
   __shared__ float red[4][RB];
-  build_pair_table<FMT, kGemvRep>(tab_all, 0, 256);
-  __syncthreads();  // before any global load: the barrier would wait for them
   const int t = blockIdx.y;
   const int n0 = blockIdx.x * RB;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -499,11 +586,10 @@ __global__ __launch_bounds__(256) void k_down_combine(const float *__restrict__ 
   const int64_t rowbytes = I / 2;
   const int64_t sc_per_row = I / Fmt<FMT>::kBlock;
 
-  // (slot, chunk) pairs of this lane, their weight rows and activations
-  const uint8_t *wbase[NQ];
-  int64_t sbase[NQ];
+  // (slot, chunk) pairs of this lane: routing metadata first (written by the
+  // previous kernel), the LDS table built while it arrives, then addresses.
   bool live[NQ];
-  int64_t hoff[NQ];
+  int cq[NQ], eraw[NQ], praw[NQ];
   float wj[NQ];
 #pragma unroll
   for (int qi = 0; qi < NQ; ++qi) {
@@ -511,13 +597,24 @@ __global__ __launch_bounds__(256) void k_down_combine(const float *__restrict__ 
     const int q = wave * QW + ql;
     live[qi] = ql < QW && q < Q;
     const int j = live[qi] ? q / nch : 0;
-    const int c = live[qi] ? q % nch : 0;
+    cq[qi] = live[qi] ? q % nch : 0;
     const int slot = t * k + j;
-    const int e = topk_ids[slot];
+    eraw[qi] = topk_ids[slot];
     wj[qi] = topk_w[slot];
-    hoff[qi] = (int64_t)slot_pos[slot] * I + (int64_t)c * 32;
-    wbase[qi] = w2 + (int64_t)e * H * rowbytes + (int64_t)c * 16;
-    sbase[qi] = (int64_t)e * H * sc_per_row + (FMT == 0 ? (c >> 1) : c);
+    praw[qi] = slot_pos[slot];
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  build_pair_table<FMT, kGemvRep>(tab_all, 0, 4);
+  __builtin_amdgcn_sched_barrier(0);
+  const uint8_t *wbase[NQ];
+  int64_t sbase[NQ];
+  int64_t hoff[NQ];
+#pragma unroll
+  for (int qi = 0; qi < NQ; ++qi) {
+    const int c = cq[qi];
+    hoff[qi] = (int64_t)praw[qi] * I + (int64_t)c * 32;
+    wbase[qi] = w2 + (int64_t)eraw[qi] * H * rowbytes + (int64_t)c * 16;
+    sbase[qi] = (int64_t)eraw[qi] * H * sc_per_row + (FMT == 0 ? (c >> 1) : c);
   }
   // Loads: activations first, then weights in row order (vector loads retire
   // in issue order, so row n waits only for its own data); all unconditional
@@ -542,6 +639,7 @@ __global__ __launch_bounds__(256) void k_down_combine(const float *__restrict__ 
     }
   }
   __builtin_amdgcn_sched_barrier(0);  // every load is in flight before any wait
+  lds_barrier();                      // the table is complete; the loads stay in flight
   float hv[NQ][32];
 #pragma unroll
   for (int qi = 0; qi < NQ; ++qi) {
@@ -571,7 +669,7 @@ __global__ __launch_bounds__(256) void k_down_combine(const float *__restrict__ 
     acc = wave_sum(acc);
     if (lane == 0) red[wave][n] = acc;
   }
-  __syncthreads();
+  lds_barrier();
   if (threadIdx.x < RB && n0 + (int)threadIdx.x < H) {
     const int n = threadIdx.x;
     const float v = ((red[0][n] + red[1][n]) + red[2][n]) + red[3][n];

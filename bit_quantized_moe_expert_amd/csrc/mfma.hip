@@ -52,9 +52,10 @@ constexpr int kTabBytes = 256 * 32 * 8;
 
 template <int FMT>
 __device__ inline void build_mfma_table(uint4 *tab) {
-  for (int f = threadIdx.x; f < kTabBytes / 16; f += blockDim.x) {
+  const float cb = codebook_lane<FMT>();
+  for (int f = threadIdx.x; f < kTabBytes / 16; f += blockDim.x) {  // 8 full-wave rounds
     const uint32_t b = (uint32_t)f >> 4;   // 16 words of two replicas per entry
-    const float2 pv = pair_value<FMT>(b);
+    const float2 pv = pair_gather<FMT>(cb, b);
     uint2 v;
     if (FMT == 0) {
       const uint32_t he = f32_to_bf16_rne(pv.x), ho = f32_to_bf16_rne(pv.y);
