@@ -7,7 +7,8 @@
 // dense contraction. Design for gfx950:
 //  - tiles of up to 128 routed rows of one expert (from the device tile
 //    table) by 256 weight rows, K in steps of 64 (one NF4 absmax block);
-//    8 waves, each 64 x 64 as 2 x 2 blocks of v_mfma_f32_32x32x16_bf16;
+//    8 waves, each 128 x 32 (all rows, 32 weight rows) as 4 blocks of
+//    v_mfma_f32_32x32x16_bf16, so each decoded code feeds 4 MFMAs;
 //  - the activation tile is double-buffered in LDS and the next K-step's
 //    activation and weight loads are issued before the current step's MFMAs,
 //    so one barrier per step finds them mostly landed;
@@ -21,7 +22,8 @@
 //    block) absmax multiplies the block's accumulator in fp32. MXFP4 values
 //    times their power-of-two scale are exact in bf16, so one product suffices
 //    and the scale is folded into B;
-//  - SwiGLU pairs gate column n and up column n + I inside one wave.
+//  - SwiGLU: gate column n and up column n + I are computed by paired waves
+//    and meet through LDS in the epilogue.
 // Workgroups are remapped so consecutive tiles sharing a weight tile land on
 // the same XCD (its L2), with tiles of one expert adjacent.
 #include "common.h"
@@ -93,26 +95,25 @@ __global__ __launch_bounds__(512) void k_mfma(GemmArgs p, int ntn, int per) {
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
-  const int wm = wave & 1, wn = wave >> 1;           // 2 x 4 waves, 64 x 64 each
   const int g = lane >> 5, l32 = lane & 31;
   const uint32_t lanebyte = (uint32_t)l32 * 8;
 
+  // Every wave covers all 128 rows of the tile and 32 weight rows (output
+  // columns), lane column l32. SwiGLU: waves 0-3 take gate columns
+  // nt * 128 + 32 w, waves 4-7 the matching up columns (+ I); the two halves
+  // meet through LDS in the epilogue.
   const int64_t N = p.N, K = p.K;
   const int64_t ncol = (EPI == EPI_SWIGLU) ? N / 2 : N;
-  int64_t colbase, nrow[2];
+  int64_t col, nrow;
   if (EPI == EPI_SWIGLU) {
-    colbase = (int64_t)nt * 128 + wn * 32;
-    nrow[0] = colbase + l32;          // gate row
-    nrow[1] = ncol + colbase + l32;   // up row
+    col = (int64_t)nt * 128 + 32 * (wave & 3) + l32;
+    nrow = col + (wave >> 2) * ncol;
   } else {
-    colbase = (int64_t)nt * 256 + wn * 64;
-    nrow[0] = colbase + l32;
-    nrow[1] = colbase + 32 + l32;
+    col = (int64_t)nt * 256 + 32 * wave + l32;
+    nrow = col;
   }
-  bool nvalid[2];
-  nvalid[0] = (EPI == EPI_SWIGLU) ? (colbase + l32 < ncol) : (nrow[0] < N);
-  nvalid[1] = (EPI == EPI_SWIGLU) ? (colbase + l32 < ncol) : (nrow[1] < N);
-  const int64_t nrow_c[2] = {nvalid[0] ? nrow[0] : 0, nvalid[1] ? nrow[1] : 0};
+  const bool nvalid = col < ncol;
+  const int64_t nrow_c = nvalid ? nrow : 0;
 
   const int64_t rowbytes = K / 2;
   const uint8_t *Be = p.B + (int64_t)e * N * rowbytes;
@@ -164,39 +165,33 @@ __global__ __launch_bounds__(512) void k_mfma(GemmArgs p, int ntn, int per) {
         *reinterpret_cast<uint4 *>(dh + 8 * i) = a_ok ? areg[i] : make_uint4(0, 0, 0, 0);
     }
   };
-  // B: one 16-byte chunk of codes per lane and N-block, k in [k0 + 32 g, +32),
-  // plus the raw scale and whether it counts. The scale is masked only when it
-  // is consumed, a K-step later, so nothing waits on these loads early.
-  auto load_b = [&](int64_t k0, uint4 *bq, uint32_t *braw, bool *bok) {
-#pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      const int64_t kk = k0 + 32 * g;
-      bok[b] = nvalid[b] && kk < K;
-      const int64_t kc = kk < K ? kk : 0;
-      bq[b] = *reinterpret_cast<const uint4 *>(Be + nrow_c[b] * rowbytes + kc / 2);
-      const int64_t sidx = FMT == 0 ? (k0 < K ? k0 / 64 : 0) : kc / 32;
-      if (FMT == 0)
-        braw[b] = reinterpret_cast<const uint32_t *>(p.B_scale)[sc_base + nrow_c[b] * sc_per_row + sidx];
-      else
-        braw[b] = reinterpret_cast<const uint8_t *>(p.B_scale)[sc_base + nrow_c[b] * sc_per_row + sidx];
-    }
+  // B: one 16-byte chunk of codes per lane, k in [k0 + 32 g, +32), plus the
+  // raw scale and whether it counts. The scale is masked only when it is
+  // consumed, a K-step later, so nothing waits on these loads early.
+  auto load_b = [&](int64_t k0, uint4 &bq, uint32_t &braw, bool &bok) {
+    const int64_t kk = k0 + 32 * g;
+    bok = nvalid && kk < K;
+    const int64_t kc = kk < K ? kk : 0;
+    bq = *reinterpret_cast<const uint4 *>(Be + nrow_c * rowbytes + kc / 2);
+    const int64_t sidx = FMT == 0 ? (k0 < K ? k0 / 64 : 0) : kc / 32;
+    if (FMT == 0)
+      braw = reinterpret_cast<const uint32_t *>(p.B_scale)[sc_base + nrow_c * sc_per_row + sidx];
+    else
+      braw = reinterpret_cast<const uint8_t *>(p.B_scale)[sc_base + nrow_c * sc_per_row + sidx];
   };
   auto scale_of = [&](uint32_t raw, bool ok) -> float {
     const float v = FMT == 0 ? __uint_as_float(raw) : e8m0_to_f32(raw);
     return ok ? v : 0.0f;
   };
 
-  f32x16_t C[2][2];
+  const f32x16_t zero16 = {};
+  f32x16_t C[4], P[4];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) C[i][j][v] = 0.0f;
+  for (int mb = 0; mb < 4; ++mb) C[mb] = zero16;
 
-  // One K-step on LDS buffer `cur` with codes bq and scales bs, prefetching
+  // One K-step on LDS buffer `cur` with codes bq and scale bs, prefetching
   // the next step into (bqn, brn, bokn) and the other LDS buffer.
-  auto step = [&](int64_t k0, int cur, const uint4 *bq, const float *bs, uint4 *bqn, uint32_t *brn, bool *bokn) {
+  auto step = [&](int64_t k0, int cur, const uint4 &bq, float bs, uint4 &bqn, uint32_t &brn, bool &bokn) {
     // Next step's loads fly while this step computes. They are issued (from
     // clamped, valid addresses) and stored even after the last step, so no
     // branch splits the load/wait bookkeeping; the extra buffer is unused.
@@ -207,124 +202,139 @@ __global__ __launch_bounds__(512) void k_mfma(GemmArgs p, int ntn, int per) {
     const uint16_t *Ah = abuf(0, cur);
     const uint16_t *Al = abuf(1, AF32 ? cur : 0);
 
-    f32x16_t P[2][2];
+    // Four units s per K-step (k = 32 g + 8 s + 0..7 of this lane). A unit's
+    // B operand is 4 table lookups of code word s; its A operands are the
+    // four 32-row fragments. Unit s + 1's LDS reads are issued before unit
+    // s's MFMAs (fp32 A: only the lookups; its fragments would not fit).
+    constexpr int NA = AF32 ? 1 : 2;
+    uint2 t[2][4];
+    bf16x8_t ah[NA][4], al[NA][4];
+    auto read_a = [&](int sa, bf16x8_t *dh, bf16x8_t *dl) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) P[i][j][v] = 0.0f;
-
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      bf16x8_t ah[2], al[2];
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        const int row = wm * 64 + mb * 32 + l32;
-        const int col = 32 * g + 8 * s;
-        ah[mb] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4 *>(Ah + row * kApad + col));
-        if (AF32)
-          al[mb] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4 *>(Al + row * kApad + col));
+      for (int mb = 0; mb < 4; ++mb) {
+        const int row = mb * 32 + l32;
+        const int colk = 32 * g + 8 * sa;
+        dh[mb] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4 *>(Ah + row * kApad + colk));
+        if (AF32) dl[mb] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4 *>(Al + row * kApad + colk));
       }
+    };
 #pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        const uint32_t word = s == 0 ? bq[b].x : (s == 1 ? bq[b].y : (s == 2 ? bq[b].z : bq[b].w));
-        uint2 t[4];
+    for (int u = -1; u < 4; ++u) {
+      if (u + 1 < 4) {
+        const int sn = u + 1;
+        if (!AF32) read_a(sn, ah[sn & (NA - 1)], al[sn & (NA - 1)]);
+        const uint32_t word = sn == 0 ? bq.x : (sn == 1 ? bq.y : (sn == 2 ? bq.z : bq.w));
 #pragma unroll
-        for (int q = 0; q < 4; ++q) t[q] = *reinterpret_cast<const uint2 *>(smem + tab_offset(word, lanebyte, q));
+        for (int q = 0; q < 4; ++q)
+          t[sn & 1][q] = *reinterpret_cast<const uint2 *>(smem + tab_offset(word, lanebyte, q));
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if (u >= 0) {
+        const int s = u;
+        if (AF32) read_a(s, ah[0], al[0]);
+        const uint2 *tu = t[s & 1];
+        const bf16x8_t *ahs = ah[s & (NA - 1)];
+        const bf16x8_t *als = al[s & (NA - 1)];
         if (FMT == 0) {
-          const bf16x8_t bh = as_bf16x8(t[0].x, t[1].x, t[2].x, t[3].x);
-          const bf16x8_t bl = as_bf16x8(t[0].y, t[1].y, t[2].y, t[3].y);
+          const bf16x8_t bh = as_bf16x8(tu[0].x, tu[1].x, tu[2].x, tu[3].x);
+          const bf16x8_t bl = as_bf16x8(tu[0].y, tu[1].y, tu[2].y, tu[3].y);
 #pragma unroll
-          for (int mb = 0; mb < 2; ++mb) {
-            P[mb][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[mb], bh, P[mb][b], 0, 0, 0);
-            P[mb][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[mb], bl, P[mb][b], 0, 0, 0);
-            if (AF32)
-              P[mb][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[mb], bh, P[mb][b], 0, 0, 0);
+          for (int mb = 0; mb < 4; ++mb) {
+            P[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahs[mb], bh, s == 0 ? zero16 : P[mb], 0, 0, 0);
+            P[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahs[mb], bl, P[mb], 0, 0, 0);
+            if (AF32) P[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(als[mb], bh, P[mb], 0, 0, 0);
           }
         } else {
           uint32_t d[4];
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            const float ve = __uint_as_float(t[q].x) * bs[b];   // exact: power-of-two scale
-            const float vo = __uint_as_float(t[q].y) * bs[b];
+            const float ve = __uint_as_float(tu[q].x) * bs;   // exact: power-of-two scale
+            const float vo = __uint_as_float(tu[q].y) * bs;
             d[q] = (__float_as_uint(ve) >> 16) | (__float_as_uint(vo) & 0xffff0000u);
           }
           const bf16x8_t bv = as_bf16x8(d[0], d[1], d[2], d[3]);
 #pragma unroll
-          for (int mb = 0; mb < 2; ++mb) {
-            C[mb][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[mb], bv, C[mb][b], 0, 0, 0);
-            if (AF32)
-              C[mb][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[mb], bv, C[mb][b], 0, 0, 0);
+          for (int mb = 0; mb < 4; ++mb) {
+            C[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahs[mb], bv, C[mb], 0, 0, 0);
+            if (AF32) C[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(als[mb], bv, C[mb], 0, 0, 0);
           }
         }
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
-    if (FMT == 0) {
+    if (FMT == 0) {  // NF4: the block's absmax scales its partial product
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
+      for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) C[mb][b][v] = fmaf(bs[b], P[mb][b][v], C[mb][b][v]);
+        for (int v = 0; v < 16; ++v) C[mb][v] = fmaf(bs, P[mb][v], C[mb][v]);
     }
     __builtin_amdgcn_sched_barrier(0);  // the A store waits for its loads: keep it last
     store_a(cur ^ 1);
-    __syncthreads();
+    lds_barrier();
     return more;
   };
 
-  uint4 bq0[2], bq1[2];
-  uint32_t br0[2], br1[2];
-  bool bok0[2], bok1[2];
-  float bs0[2], bs1[2];
+  uint4 bq0, bq1;
+  uint32_t br0, br1;
+  bool bok0, bok1;
   load_a(0);
   load_b(0, bq0, br0, bok0);
   store_a(0);
-  __syncthreads();
-  bs0[0] = scale_of(br0[0], bok0[0]);
-  bs0[1] = scale_of(br0[1], bok0[1]);
+  lds_barrier();
+  float bs0 = scale_of(br0, bok0), bs1;
 
   // Unrolled by two so the register sets alternate without copies.
   for (int64_t k0 = 0;; k0 += 2 * kBK) {
     if (!step(k0, 0, bq0, bs0, bq1, br1, bok1)) break;
-    bs1[0] = scale_of(br1[0], bok1[0]);
-    bs1[1] = scale_of(br1[1], bok1[1]);
+    bs1 = scale_of(br1, bok1);
     if (!step(k0 + kBK, 1, bq1, bs1, bq0, br0, bok0)) break;
-    bs0[0] = scale_of(br0[0], bok0[0]);
-    bs0[1] = scale_of(br0[1], bok0[1]);
+    bs0 = scale_of(br0, bok0);
   }
 
   // ---- epilogue. 32x32 accumulator: lane holds column l32, rows
-  // 8 * (v / 4) + 4 * g + (v % 4) for v = 0..15.
+  // 8 * (v / 4) + 4 * g + (v % 4) for v = 0..15 of each 32-row block mb.
+  if (EPI == EPI_SWIGLU) {
+    // up waves hand their values to the gate waves through LDS (the table
+    // region: every lookup finished before the last step's barrier)
+    float *xch = reinterpret_cast<float *>(smem);
+    const int w4 = wave & 3;
+    if (wave >= 4) {
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb) {
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) xch[((w4 * 4 + mb) * 16 + v) * 64 + lane] = C[mb][v];
+    }
+    lds_barrier();
+    if (wave >= 4) return;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int m = mb * 32 + 8 * (v >> 2) + 4 * g + (v & 3);
+        const float up = xch[((w4 * 4 + mb) * 16 + v) * 64 + lane];
+        if (m >= trows || !nvalid) continue;
+        const float gt = C[mb][v];
+        reinterpret_cast<float *>(p.c)[(int64_t)(trow0 + m) * ncol + col] = gt / (1.0f + expf(-gt)) * up;
+      }
+    }
+    return;
+  }
+  if (!nvalid) return;
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb) {
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
-      const int m = wm * 64 + mb * 32 + 8 * (v >> 2) + 4 * g + (v & 3);
+      const int m = mb * 32 + 8 * (v >> 2) + 4 * g + (v & 3);
       if (m >= trows) continue;
       const int64_t r = trow0 + m;
-      if (EPI == EPI_SWIGLU) {
-        const int64_t col = colbase + l32;
-        if (col < ncol) {
-          const float gt = C[mb][0][v], up = C[mb][1][v];
-          reinterpret_cast<float *>(p.c)[r * ncol + col] = gt / (1.0f + expf(-gt)) * up;
-        }
+      const float y = C[mb][v];
+      if (EPI == EPI_PLAIN_F32) {
+        reinterpret_cast<float *>(p.c)[r * N + col] = y;
+      } else if (EPI == EPI_PLAIN_BF16) {
+        reinterpret_cast<uint16_t *>(p.c)[r * N + col] = (uint16_t)f32_to_bf16_rne(y);
       } else {
-#pragma unroll
-        for (int b = 0; b < 2; ++b) {
-          const int64_t col = nrow[b];
-          if (!nvalid[b]) continue;
-          const float y = C[mb][b][v];
-          if (EPI == EPI_PLAIN_F32) {
-            reinterpret_cast<float *>(p.c)[r * N + col] = y;
-          } else if (EPI == EPI_PLAIN_BF16) {
-            reinterpret_cast<uint16_t *>(p.c)[r * N + col] = (uint16_t)f32_to_bf16_rne(y);
-          } else {
-            const int64_t slot = p.slot_of[r];
-            reinterpret_cast<float *>(p.c)[slot * N + col] = p.slot_w[slot] * y;
-          }
-        }
+        const int64_t slot = p.slot_of[r];
+        reinterpret_cast<float *>(p.c)[slot * N + col] = p.slot_w[slot] * y;
       }
     }
   }
