@@ -62,7 +62,8 @@ def lib() -> ctypes.CDLL:
     sig = {
         "nf4moe_quantize": [ctypes.c_int, vp, i64, i64, vp, vp, vp],
         "nf4moe_dequantize": [ctypes.c_int, vp, vp, i64, i64, vp, vp],
-        "nf4moe_router_logits": [vp, i32, i32, vp, vp, i32, vp, vp],
+        "nf4moe_router_logits": [vp, i32, i32, vp, vp, i32, vp, vp, sz, vp],
+        "nf4moe_router_workspace_bytes": [i32, i32],
         "nf4moe_route_workspace_bytes": [i32, i32, i32],
         "nf4moe_route_permute": [vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp],
         "nf4moe_gemm_workspace_bytes": [i32, i32],
@@ -81,7 +82,8 @@ def lib() -> ctypes.CDLL:
         fn = getattr(L, name)
         fn.argtypes = args
         fn.restype = ctypes.c_int
-    for name in ("nf4moe_route_workspace_bytes", "nf4moe_gemm_workspace_bytes", "nf4moe_workspace_bytes"):
+    for name in ("nf4moe_route_workspace_bytes", "nf4moe_gemm_workspace_bytes", "nf4moe_workspace_bytes",
+                 "nf4moe_router_workspace_bytes"):
         getattr(L, name).restype = ctypes.c_size_t
     for name in ("nf4moe_status_string", "nf4moe_last_error", "nf4moe_version"):
         getattr(L, name).restype = ctypes.c_char_p
@@ -170,8 +172,10 @@ def dequantize(packed, scale, K: int, fmt: int = FMT_NF4):
     return out
 
 
-def router_logits(x, router_w, router_b=None):
-    """x bf16 [T, H], W_r fp32 [E, H] (+ b [E]) -> logits fp32 [T, E]."""
+def router_logits(x, router_w, router_b=None, matrix_cores: bool = True):
+    """x bf16 [T, H], W_r fp32 [E, H] (+ b [E]) -> logits fp32 [T, E].
+    matrix_cores: hand the library the workspace that enables its MFMA kernel
+    (used for T >= 32, H % 32 == 0); False keeps the vector-ALU kernels."""
     torch = _torch()
     _dev(x, "x", torch.bfloat16)
     _dev(router_w, "router_w", torch.float32)
@@ -180,8 +184,12 @@ def router_logits(x, router_w, router_b=None):
     T, H = x.shape
     E = router_w.shape[0]
     out = torch.empty(T, E, dtype=torch.float32, device=x.device)
+    ws, nb = None, 0
+    if matrix_cores:
+        nb = lib().nf4moe_router_workspace_bytes(E, H)
+        ws = torch.empty(nb, dtype=torch.uint8, device=x.device)
     _check(lib().nf4moe_router_logits(_ptr(x), T, H, _ptr(router_w), _ptr(router_b), E, _ptr(out),
-                                      _stream()))
+                                      _ptr(ws), nb, _stream()))
     return out
 
 

@@ -77,6 +77,7 @@ void carve_route_scratch(Carve &cv, const RoutePlan &rp, int E, RouteBufs &rb) {
 
 struct ForwardCarve {
   float *logits;
+  uint16_t *rsplit;  // router weight bf16 planes (T >= kMfmaLogitsT), else null
   RouteBufs rb;
   float *h;
   float *slotbuf;
@@ -95,6 +96,7 @@ ForwardCarve carve_forward(void *ws, const nf4moe_layer_t &L, int T) {
   carve_route_scratch(cv, rp, L.E, fc.rb);
   fc.h = cv.take<float>((size_t)(rp.R > 0 ? rp.R : 1) * L.I);
   fc.slotbuf = cv.take<float>((size_t)(rp.R > 0 ? rp.R : 1) * L.H);
+  fc.rsplit = T >= kMfmaLogitsT ? cv.take<uint16_t>(router_split_bytes(L.E, L.H) / sizeof(uint16_t)) : nullptr;
   fc.bytes = align_up(cv.off);
   return fc;
 }
@@ -189,9 +191,14 @@ nf4moe_status_t nf4moe_dequantize(nf4moe_format_t fmt, const uint8_t *packed, co
                     "dequantize launch");
 }
 
+size_t nf4moe_router_workspace_bytes(int32_t E, int32_t H) {
+  if (E < 1 || H <= 0) return 0;
+  return align_up(router_split_bytes(E, H));
+}
+
 nf4moe_status_t nf4moe_router_logits(const uint16_t *x, int32_t T, int32_t H,
                                      const float *router_w, const float *router_b, int32_t E,
-                                     float *logits, void *stream) {
+                                     float *logits, void *ws, size_t ws_bytes, void *stream) {
   if (T < 0) return fail(NF4MOE_ERR_INVALID_ARG, "T=%d < 0", T);
   if (E < 1 || E > kMaxE) return fail(NF4MOE_ERR_INVALID_ARG, "E=%d outside 1..%d", E, kMaxE);
   if (H <= 0 || H % 8) return fail(NF4MOE_ERR_INVALID_ARG, "H=%d must be a positive multiple of 8", H);
@@ -199,7 +206,12 @@ nf4moe_status_t nf4moe_router_logits(const uint16_t *x, int32_t T, int32_t H,
   if (!x || !router_w || !logits) return fail(NF4MOE_ERR_INVALID_ARG, "NULL pointer");
   if (!aligned(x, 16) || !aligned(router_w, 16) || !aligned(logits, 4))
     return fail(NF4MOE_ERR_INVALID_ARG, "misaligned pointer");
-  return hip_status(launch_router_logits(x, T, H, router_w, router_b, E, logits, (hipStream_t)stream),
+  if (ws) {
+    if (ws_bytes < router_split_bytes(E, H))
+      return fail(NF4MOE_ERR_WORKSPACE, "workspace %zu bytes < %zu required", ws_bytes, router_split_bytes(E, H));
+    if (!aligned(ws, 256)) return fail(NF4MOE_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  }
+  return hip_status(launch_router_logits(x, T, H, router_w, router_b, E, logits, ws, (hipStream_t)stream),
                     "router launch");
 }
 
@@ -359,7 +371,7 @@ static nf4moe_status_t forward_impl(const nf4moe_layer_t *layer, const uint16_t 
   };
   ForwardCarve fc = carve_forward(ws, L, T);
   if ((e = mark(0)) != hipSuccess) return hip_status(e, "event record");
-  e = launch_router_logits(x, T, L.H, L.router_w, L.router_b, L.E, fc.logits, s);
+  e = launch_router_logits(x, T, L.H, L.router_w, L.router_b, L.E, fc.logits, fc.rsplit, s);
   if (e != hipSuccess) return hip_status(e, "router launch");
   // One decode token on the small-M path: top-k and grouping happen inside the
   // gate_up kernel; otherwise they are their own launches.

@@ -35,8 +35,12 @@ hipError_t launch_quantize(int fmt, const float *w, int64_t rows, int64_t K, uin
 hipError_t launch_dequantize(int fmt, const uint8_t *packed, const void *scale, int64_t rows,
                              int64_t K, float *out, hipStream_t s);
 
+// Router logits. With split_ws (>= router_split_bytes(E, H) bytes, 256-byte
+// aligned) and T >= kMfmaLogitsT, H % 32 == 0: the matrix-core kernel.
+constexpr int kMfmaLogitsT = 32;
+size_t router_split_bytes(int E, int H);
 hipError_t launch_router_logits(const uint16_t *x, int T, int H, const float *W, const float *b,
-                                int E, float *logits, hipStream_t s);
+                                int E, float *logits, void *split_ws, hipStream_t s);
 // top-k + softmax, then grouping. Fills every RouteBufs field.
 hipError_t launch_route(const float *logits, int T, int E, int k, int renorm, const RouteBufs &rb,
                         int bm, hipStream_t s);

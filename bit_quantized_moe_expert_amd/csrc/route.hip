@@ -66,6 +66,92 @@ __global__ __launch_bounds__(256) void k_logits_rows(const uint16_t *__restrict_
 }
 
 // ---------------------------------------------------------------------------
+// Router logits, many tokens, on the matrix cores. x is bf16, an exact MFMA
+// operand. Each fp32 router weight is split exactly into three bf16 parts
+// w = w1 + w2 + w3 (w1 = w truncated to bf16, w2 = the remainder truncated,
+// w3 = what is left, at most 8 significant bits), so three bf16 products
+// accumulated in fp32 give the fp32 dot product.
+// k_split3: the three planes [3][E][H] (bf16 bits) from router_w.
+// k_logits_mfma: 32 tokens x 32 experts per workgroup, eight waves taking one
+// eighth of H each, loads issued eight k-steps ahead (their partial sums meet
+// in LDS, in a fixed order).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_split3(const float *__restrict__ W, int64_t n,
+                                                uint16_t *__restrict__ planes) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  const uint32_t w = __float_as_uint(W[i]);
+  const uint32_t p1 = w >> 16;
+  const float r1 = __uint_as_float(w) - __uint_as_float(p1 << 16);
+  const uint32_t p2 = __float_as_uint(r1) >> 16;
+  const float r2 = r1 - __uint_as_float(p2 << 16);
+  planes[i] = (uint16_t)p1;
+  planes[n + i] = (uint16_t)p2;
+  planes[2 * n + i] = (uint16_t)(__float_as_uint(r2) >> 16);
+}
+
+typedef __bf16 lg_bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float lg_f32x16_t __attribute__((ext_vector_type(16)));
+
+__global__ __launch_bounds__(512) void k_logits_mfma(const uint16_t *__restrict__ x, int T, int H,
+                                                     const uint16_t *__restrict__ planes,
+                                                     const float *__restrict__ b, int E,
+                                                     float *__restrict__ L) {
+  constexpr int NW = 8, BATCH = 8;
+  __shared__ float red[NW - 1][16][64];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int g = lane >> 5, l32 = lane & 31;
+  const int t = blockIdx.x * 32 + l32, e = blockIdx.y * 32 + l32;
+  const int64_t xrow = t < T ? t : 0, wrow = e < E ? e : 0;
+  const int64_t n = (int64_t)E * H;
+  // wave w takes k-steps [s0, s1) of 16 (H % 32 == 0)
+  const int nsteps = H / 16;
+  const int s0 = wave * nsteps / NW, s1 = (wave + 1) * nsteps / NW;
+  const uint16_t *xa = x + xrow * H + 8 * g;
+  const uint16_t *wa = planes + wrow * H + 8 * g;
+  lg_f32x16_t acc = {};
+  for (int sb = s0; sb < s1; sb += BATCH) {
+    uint4 a[BATCH], b1[BATCH], b2[BATCH], b3[BATCH];
+#pragma unroll
+    for (int i = 0; i < BATCH; ++i) {      // the batch's loads first (clamped to the range)
+      const int st = sb + i < s1 ? sb + i : s1 - 1;
+      a[i] = *reinterpret_cast<const uint4 *>(xa + 16 * st);
+      b1[i] = *reinterpret_cast<const uint4 *>(wa + 16 * st);
+      b2[i] = *reinterpret_cast<const uint4 *>(wa + n + 16 * st);
+      b3[i] = *reinterpret_cast<const uint4 *>(wa + 2 * n + 16 * st);
+    }
+#pragma unroll
+    for (int i = 0; i < BATCH; ++i) {
+      if (sb + i < s1) {
+        const lg_bf16x8_t av = __builtin_bit_cast(lg_bf16x8_t, a[i]);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, __builtin_bit_cast(lg_bf16x8_t, b1[i]), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, __builtin_bit_cast(lg_bf16x8_t, b2[i]), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, __builtin_bit_cast(lg_bf16x8_t, b3[i]), acc, 0, 0, 0);
+      }
+    }
+  }
+  // 32x32 accumulator: lane holds expert column l32, token rows
+  // 8 * (v / 4) + 4 * g + (v % 4). Partial sums meet in wave order.
+  if (wave > 0) {
+#pragma unroll
+    for (int v = 0; v < 16; ++v) red[wave - 1][v][lane] = acc[v];
+  }
+  __syncthreads();
+  if (wave > 0 || e >= E) return;
+  const float bias = b ? b[e] : 0.0f;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    float sum = acc[v];
+#pragma unroll
+    for (int w = 0; w < NW - 1; ++w) sum += red[w][v][lane];
+    const int tt = blockIdx.x * 32 + 8 * (v >> 2) + 4 * g + (v & 3);
+    if (tt < T) L[(int64_t)tt * E + e] = sum + bias;
+  }
+}
+
+size_t router_split_bytes(int E, int H) { return (size_t)3 * E * H * sizeof(uint16_t); }
+
+// ---------------------------------------------------------------------------
 // Router logits, many tokens: 32 tokens x 64 experts per workgroup, H in
 // steps of 64 through LDS; each thread owns 2 tokens x 4 experts.
 // ---------------------------------------------------------------------------
@@ -134,9 +220,15 @@ __global__ __launch_bounds__(256) void k_logits_tiled(const uint16_t *__restrict
 }
 
 hipError_t launch_router_logits(const uint16_t *x, int T, int H, const float *W, const float *b,
-                                int E, float *logits, hipStream_t s) {
+                                int E, float *logits, void *split_ws, hipStream_t s) {
   if (T <= 0) return hipSuccess;
-  if (T <= 8) {
+  if (split_ws && T >= kMfmaLogitsT && H % 32 == 0) {
+    uint16_t *planes = reinterpret_cast<uint16_t *>(split_ws);
+    const int64_t n = (int64_t)E * H;
+    hipLaunchKernelGGL(k_split3, dim3((unsigned)cdiv(n, 256)), dim3(256), 0, s, W, n, planes);
+    hipLaunchKernelGGL(k_logits_mfma, dim3((unsigned)cdiv(T, 32), (unsigned)cdiv(E, 32)), dim3(512), 0, s,
+                       x, T, H, planes, b, E, logits);
+  } else if (T <= 8) {
     hipLaunchKernelGGL(k_logits_rows<8>, dim3(E), dim3(256), 0, s, x, T, H, W, b, E, logits);
   } else {
     hipLaunchKernelGGL(k_logits_tiled, dim3((unsigned)cdiv(T, 32), (unsigned)cdiv(E, 64)),

@@ -108,14 +108,24 @@ nf4moe_status_t nf4moe_quantize(nf4moe_format_t fmt, const float *w, int64_t row
 nf4moe_status_t nf4moe_dequantize(nf4moe_format_t fmt, const uint8_t *packed, const void *scale,
                                   int64_t rows, int64_t K, float *w_out, void *stream);
 
+/* nf4moe_router_workspace_bytes -- workspace that lets nf4moe_router_logits use
+ * the matrix cores (3 * E * H * 2 bytes: router_w split exactly into three bf16
+ * planes); 0 for E < 1 or H <= 0. */
+size_t nf4moe_router_workspace_bytes(int32_t E, int32_t H);
+
 /* nf4moe_router_logits -- logits[t, e] = sum_h x[t, h] * router_w[e, h] (+ router_b[e]),
- * x bf16 [T, H], router_w fp32 [E, H], logits fp32 [T, E] (all device); fp32
- * accumulation. The first step of the routed layer (the router, outside the
- * kernel on the pages' "Why it happens" dataflow, inside this library).
- * Errors: INVALID_ARG for T < 0, E outside 1..1024, H <= 0 or H % 8, null pointers. */
+ * x bf16 [T, H], router_w fp32 [E, H], optional router_b fp32 [E], logits fp32
+ * [T, E] (all device); fp32-accurate accumulation. The first step of the routed
+ * layer (the router, outside the kernel on the pages' "Why it happens" dataflow,
+ * inside this library). ws (device, caller-owned, 256-byte aligned) may be NULL;
+ * with ws_bytes >= nf4moe_router_workspace_bytes(E, H), T >= 32 and H % 32 == 0
+ * the product runs on the matrix cores (x exact in bf16, each weight as the
+ * exact sum of three bf16 parts, fp32 accumulation), else on the vector ALUs.
+ * Errors: INVALID_ARG for T < 0, E outside 1..1024, H <= 0 or H % 8, null or
+ * misaligned pointers; WORKSPACE for a non-NULL ws smaller than required. */
 nf4moe_status_t nf4moe_router_logits(const uint16_t *x, int32_t T, int32_t H,
                                      const float *router_w, const float *router_b, int32_t E,
-                                     float *logits, void *stream);
+                                     float *logits, void *ws, size_t ws_bytes, void *stream);
 
 /* nf4moe_route_workspace_bytes -- workspace nf4moe_route_permute needs. */
 size_t nf4moe_route_workspace_bytes(int32_t T, int32_t E, int32_t top_k);

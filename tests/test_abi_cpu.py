@@ -66,10 +66,13 @@ def test_quantize_validation():
 
 
 def test_router_and_route_validation():
-    assert L.nf4moe_router_logits(FAKE, -1, 64, FAKE, None, 8, FAKE, STREAM) == INVALID
-    assert L.nf4moe_router_logits(FAKE, 1, 60, FAKE, None, 8, FAKE, STREAM) == INVALID
-    assert L.nf4moe_router_logits(FAKE, 1, 64, FAKE, None, 2000, FAKE, STREAM) == INVALID
-    assert L.nf4moe_router_logits(FAKE, 0, 64, FAKE, None, 8, FAKE, STREAM) == OK
+    assert L.nf4moe_router_logits(FAKE, -1, 64, FAKE, None, 8, FAKE, None, 0, STREAM) == INVALID
+    assert L.nf4moe_router_logits(FAKE, 1, 60, FAKE, None, 8, FAKE, None, 0, STREAM) == INVALID
+    assert L.nf4moe_router_logits(FAKE, 1, 64, FAKE, None, 2000, FAKE, None, 0, STREAM) == INVALID
+    assert L.nf4moe_router_logits(FAKE, 0, 64, FAKE, None, 8, FAKE, None, 0, STREAM) == OK
+    need = L.nf4moe_router_workspace_bytes(8, 64)
+    assert need >= 3 * 8 * 64 * 2
+    assert L.nf4moe_router_logits(FAKE, 64, 64, FAKE, None, 8, FAKE, FAKE, need - 1, STREAM) == 3  # WORKSPACE
     rp = L.nf4moe_route_permute
     need = L.nf4moe_route_workspace_bytes(16, 8, 2)
     assert need > 0

@@ -73,13 +73,17 @@ def test_quantize_large_stack_bitexact_sample():
 
 
 @pytest.mark.parametrize("T,E,H,bias", [(1, 64, 2048, False), (5, 8, 256, True),
-                                         (300, 128, 2048, True), (33, 100, 320, False)])
-def test_router_logits(T, E, H, bias):
+                                         (300, 128, 2048, True), (33, 100, 320, False),
+                                         (4097, 64, 2048, False), (45, 7, 64, True),
+                                         (64, 1000, 96, False), (32, 33, 2880, True)])
+@pytest.mark.parametrize("matrix_cores", [True, False])
+def test_router_logits(T, E, H, bias, matrix_cores):
     wl = S.custom(E=E, top_k=2, H=H, I=64, zipf_s=1.2 if bias else 0.0)
     xb = S.make_x(wl, T)
     W, b = S.make_router(wl)
     got = M.router_logits(bits_to_torch_bf16(xb), torch.from_numpy(W).to(DEV),
-                          None if b is None else torch.from_numpy(b).to(DEV)).cpu().numpy()
+                          None if b is None else torch.from_numpy(b).to(DEV),
+                          matrix_cores=matrix_cores).cpu().numpy()
     ref = O.router_logits(xb, W, b)
     mag = np.abs(O.bf16_bits_to_f64(xb)) @ np.abs(W.astype(np.float64)).T
     assert np.all(np.abs(got - ref) <= 2e-6 * mag + 1e-6)
