@@ -382,7 +382,8 @@ static nf4moe_status_t forward_impl(const nf4moe_layer_t *layer, const uint16_t 
   }
   if ((e = mark(1)) != hipSuccess) return hip_status(e, "event record");
 
-  // gate_up + SwiGLU -> h [R, I] fp32 in expert-sorted order
+  // gate_up + SwiGLU -> h [R, I] in expert-sorted order (fp32; on the MFMA
+  // path 32-bit (bf16 hi, bf16 lo) pairs)
   GemmArgs g = base_args(L.fmt);
   g.a = x;
   g.a_is_f32 = 0;
@@ -403,6 +404,7 @@ static nf4moe_status_t forward_impl(const nf4moe_layer_t *layer, const uint16_t 
   g.max_tiles = rp.max_tiles;
   g.epi = EPI_SWIGLU;
   g.c = fc.h;
+  if (use == NF4MOE_PATH_MFMA) g.c_split = 1;  // h as (bf16 hi, lo) pairs for the down MFMAs
   if (fused_route) {
     g.route_logits = fc.logits;
     g.route_E = L.E;
@@ -429,7 +431,8 @@ static nf4moe_status_t forward_impl(const nf4moe_layer_t *layer, const uint16_t 
     d.route_logits = nullptr;
     d.ev_start = d.ev_stop = nullptr;
     d.a = fc.h;
-    d.a_is_f32 = 1;
+    d.a_is_f32 = use == NF4MOE_PATH_MFMA ? 2 : 1;
+    d.c_split = 0;
     d.a_row_of = nullptr;
     d.a_div = 1;
     d.B = L.w2;

@@ -54,8 +54,8 @@ hipError_t launch_groups_from_offsets(const int32_t *goff, const int32_t *gexp, 
 enum Epi { EPI_SWIGLU = 0, EPI_PLAIN_F32 = 1, EPI_PLAIN_BF16 = 2, EPI_SLOT = 3 };
 struct GemmArgs {
   int fmt;
-  const void *a;            // bf16 [*, K] (a_is_f32 = 0) or fp32 [*, K]
-  int a_is_f32;
+  const void *a;            // bf16 [*, K] (a_is_f32 = 0), fp32 [*, K] (1), or 32-bit
+  int a_is_f32;             //   (bf16 hi, bf16 lo) pairs [*, K] (2: MFMA path only)
   const int32_t *a_row_of;  // row r reads a[a_row_of[r]] or, with a_div > 1, a[a_row_of[r] / a_div]
   int a_div;
   const uint8_t *B;         // [E, N, K/2]
@@ -69,6 +69,7 @@ struct GemmArgs {
   int max_tiles;
   int epi;
   void *c;                  // SwiGLU: fp32 [R, N/2]; plain: [R, N]; slot: fp32 [R_slots, N]
+  int c_split;              // MFMA SwiGLU: write h as 32-bit (bf16 hi, bf16 lo) pairs
   const int32_t *slot_of;   // EPI_SLOT: row r -> slot
   const float *slot_w;      // EPI_SLOT: weight of slot
   // One-token routing folded into the gate_up kernel: when route_logits is set

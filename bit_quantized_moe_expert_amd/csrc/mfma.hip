@@ -12,8 +12,8 @@
 //  - the activation tile is double-buffered in LDS and the next K-step's
 //    activation and weight loads are issued before the current step's MFMAs,
 //    so one barrier per step finds them mostly landed;
-//  - A rows are gathered (token of each routed slot) into LDS as bf16; fp32
-//    activations (h of the down projection) are split into bf16 hi + lo;
+//  - A rows are gathered (token of each routed slot) into LDS as bf16; the
+//    down projection's fp32 activation h arrives as (bf16 hi, bf16 lo) pairs;
 //  - each lane's B operand is 8 consecutive k of one weight row; the K order
 //    inside a 64-block is permuted the same way for A and B so that a lane's
 //    operands for all 4 K-steps come from one 16-byte load of codes;
@@ -71,8 +71,13 @@ __device__ inline void build_mfma_table(uint4 *tab) {
   }
 }
 
-template <int FMT, int EPI, int AF32>
+// AM: activation operand mode. 0: bf16 A; 2: an fp32 A given as 32-bit
+// (hi, lo) bf16 pairs, its truncated bf16 hi and the RNE bf16 of the rest
+// (the SwiGLU epilogue writes h so), each weight product taking three MFMAs.
+template <int FMT, int EPI, int AM>
 __global__ __launch_bounds__(512) void k_mfma(GemmArgs p, int ntn, int per) {
+  static_assert(AM == 0 || AM == 2, "operand mode");
+  constexpr bool AF32 = AM != 0;                      // a lo part exists
   constexpr int ABUF = kBM * kApad * 2;               // bytes per A buffer
   constexpr int NBUF = AF32 ? 4 : 2;                  // hi[2] (+ lo[2])
   __shared__ __attribute__((aligned(16))) uint8_t smem[kTabBytes + NBUF * ABUF];
@@ -137,27 +142,28 @@ __global__ __launch_bounds__(512) void k_mfma(GemmArgs p, int ntn, int per) {
     const int64_t kk = k0 + 16 * aq;
     a_ok = arow_ok && kk < K;
     const int64_t kc = kk < K ? kk : 0;
-    const uint4 *src = AF32 ? reinterpret_cast<const uint4 *>(reinterpret_cast<const float *>(p.a) + arow * K + kc)
-                            : reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(p.a) + arow * K + kc);
+    // AM 0: 16 bf16; AM 2: 16 (hi, lo) bf16 pairs, 4 bytes each
+    const uint4 *src = reinterpret_cast<const uint4 *>(reinterpret_cast<const uint8_t *>(p.a) +
+                                                       (arow * K + kc) * (AM == 2 ? 4 : 2));
 #pragma unroll
     for (int i = 0; i < AW; ++i) areg[i] = src[i];
   };
   auto store_a = [&](int buf) {
     uint16_t *dh = abuf(0, buf) + am * kApad + 16 * aq;
-    if (AF32) {
+    if (AM == 2) {  // de-interleave the pairs into the hi and lo tiles
       uint16_t *dl = abuf(1, buf) + am * kApad + 16 * aq;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint32_t f[4] = {areg[i].x, areg[i].y, areg[i].z, areg[i].w};
-        uint32_t hb[4], lb[4];
+      for (int i = 0; i < 2; ++i) {
+        const uint4 u = areg[2 * i], v = areg[2 * i + 1];
+        const uint32_t w[8] = {u.x, u.y, u.z, u.w, v.x, v.y, v.z, v.w};
+        uint32_t h4[4], l4[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const uint32_t hi = a_ok ? (f[q] & 0xffff0000u) : 0u;  // truncated hi
-          hb[q] = hi >> 16;
-          lb[q] = a_ok ? f32_to_bf16_rne(__uint_as_float(f[q]) - __uint_as_float(hi)) : 0u;
+          h4[q] = a_ok ? __builtin_amdgcn_perm(w[2 * q + 1], w[2 * q], 0x05040100u) : 0u;
+          l4[q] = a_ok ? __builtin_amdgcn_perm(w[2 * q + 1], w[2 * q], 0x07060302u) : 0u;
         }
-        *reinterpret_cast<uint2 *>(dh + 4 * i) = make_uint2(hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16));
-        *reinterpret_cast<uint2 *>(dl + 4 * i) = make_uint2(lb[0] | (lb[1] << 16), lb[2] | (lb[3] << 16));
+        *reinterpret_cast<uint4 *>(dh + 8 * i) = make_uint4(h4[0], h4[1], h4[2], h4[3]);
+        *reinterpret_cast<uint4 *>(dl + 8 * i) = make_uint4(l4[0], l4[1], l4[2], l4[3]);
       }
     } else {
 #pragma unroll
@@ -238,11 +244,18 @@ __global__ __launch_bounds__(512) void k_mfma(GemmArgs p, int ntn, int per) {
         if (FMT == 0) {
           const bf16x8_t bh = as_bf16x8(tu[0].x, tu[1].x, tu[2].x, tu[3].x);
           const bf16x8_t bl = as_bf16x8(tu[0].y, tu[1].y, tu[2].y, tu[3].y);
+          // passes over the four independent accumulators, so consecutive
+          // MFMAs never depend on each other
 #pragma unroll
-          for (int mb = 0; mb < 4; ++mb) {
+          for (int mb = 0; mb < 4; ++mb)
             P[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahs[mb], bh, s == 0 ? zero16 : P[mb], 0, 0, 0);
+#pragma unroll
+          for (int mb = 0; mb < 4; ++mb)
             P[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahs[mb], bl, P[mb], 0, 0, 0);
-            if (AF32) P[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(als[mb], bh, P[mb], 0, 0, 0);
+          if (AF32) {
+#pragma unroll
+            for (int mb = 0; mb < 4; ++mb)
+              P[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(als[mb], bh, P[mb], 0, 0, 0);
           }
         } else {
           uint32_t d[4];
@@ -254,9 +267,12 @@ __global__ __launch_bounds__(512) void k_mfma(GemmArgs p, int ntn, int per) {
           }
           const bf16x8_t bv = as_bf16x8(d[0], d[1], d[2], d[3]);
 #pragma unroll
-          for (int mb = 0; mb < 4; ++mb) {
+          for (int mb = 0; mb < 4; ++mb)
             C[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahs[mb], bv, C[mb], 0, 0, 0);
-            if (AF32) C[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(als[mb], bv, C[mb], 0, 0, 0);
+          if (AF32) {
+#pragma unroll
+            for (int mb = 0; mb < 4; ++mb)
+              C[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(als[mb], bv, C[mb], 0, 0, 0);
           }
         }
       }
@@ -314,7 +330,14 @@ __global__ __launch_bounds__(512) void k_mfma(GemmArgs p, int ntn, int per) {
         const float up = xch[((w4 * 4 + mb) * 16 + v) * 64 + lane];
         if (m >= trows || !nvalid) continue;
         const float gt = C[mb][v];
-        reinterpret_cast<float *>(p.c)[(int64_t)(trow0 + m) * ncol + col] = gt / (1.0f + expf(-gt)) * up;
+        const float h = gt / (1.0f + expf(-gt)) * up;
+        const int64_t o = (int64_t)(trow0 + m) * ncol + col;
+        if (p.c_split) {  // (truncated bf16 hi, RNE bf16 of the rest) in one word
+          const uint32_t hi = __float_as_uint(h) & 0xffff0000u;
+          reinterpret_cast<uint32_t *>(p.c)[o] = (hi >> 16) | (f32_to_bf16_rne(h - __uint_as_float(hi)) << 16);
+        } else {
+          reinterpret_cast<float *>(p.c)[o] = h;
+        }
       }
     }
     return;
@@ -340,28 +363,30 @@ __global__ __launch_bounds__(512) void k_mfma(GemmArgs p, int ntn, int per) {
   }
 }
 
-template <int FMT, int EPI, int AF32>
+template <int FMT, int EPI, int AM>
 static hipError_t launch_mfma_t(const GemmArgs &g, hipStream_t s) {
   const int64_t ncol = (EPI == EPI_SWIGLU) ? g.N / 2 : g.N;
   const int ntn = (int)((EPI == EPI_SWIGLU) ? cdiv(ncol, 128) : cdiv(ncol, 256));
   const int64_t total = (int64_t)g.max_tiles * ntn;
   const int64_t padded = cdiv(total, 8) * 8;
   const int per = (int)(padded / 8);
-  NF4MOE_LAUNCH(g, (k_mfma<FMT, EPI, AF32>), dim3((unsigned)padded), dim3(512), s, g, ntn, per);
+  NF4MOE_LAUNCH(g, (k_mfma<FMT, EPI, AM>), dim3((unsigned)padded), dim3(512), s, g, ntn, per);
   return hipGetLastError();
 }
 
+// Instantiated operand modes: SwiGLU (gate_up) and plain outputs bf16 A; slot
+// output (down projection) the pre-split planes.
 template <int FMT>
 static hipError_t mfma_pick(const GemmArgs &g, hipStream_t s) {
   switch (g.epi) {
     case EPI_SWIGLU:
-      return g.a_is_f32 ? launch_mfma_t<FMT, EPI_SWIGLU, 1>(g, s) : launch_mfma_t<FMT, EPI_SWIGLU, 0>(g, s);
+      return g.a_is_f32 == 0 ? launch_mfma_t<FMT, EPI_SWIGLU, 0>(g, s) : hipErrorInvalidValue;
     case EPI_PLAIN_F32:
-      return g.a_is_f32 ? launch_mfma_t<FMT, EPI_PLAIN_F32, 1>(g, s) : launch_mfma_t<FMT, EPI_PLAIN_F32, 0>(g, s);
+      return g.a_is_f32 == 0 ? launch_mfma_t<FMT, EPI_PLAIN_F32, 0>(g, s) : hipErrorInvalidValue;
     case EPI_PLAIN_BF16:
-      return g.a_is_f32 ? launch_mfma_t<FMT, EPI_PLAIN_BF16, 1>(g, s) : launch_mfma_t<FMT, EPI_PLAIN_BF16, 0>(g, s);
+      return g.a_is_f32 == 0 ? launch_mfma_t<FMT, EPI_PLAIN_BF16, 0>(g, s) : hipErrorInvalidValue;
     default:
-      return g.a_is_f32 ? launch_mfma_t<FMT, EPI_SLOT, 1>(g, s) : launch_mfma_t<FMT, EPI_SLOT, 0>(g, s);
+      return g.a_is_f32 == 2 ? launch_mfma_t<FMT, EPI_SLOT, 2>(g, s) : hipErrorInvalidValue;
   }
 }
 
