@@ -175,7 +175,7 @@ def dequantize(packed, scale, K: int, fmt: int = FMT_NF4):
 def router_logits(x, router_w, router_b=None, matrix_cores: bool = True):
     """x bf16 [T, H], W_r fp32 [E, H] (+ b [E]) -> logits fp32 [T, E].
     matrix_cores: hand the library the workspace that enables its MFMA kernel
-    (used for T >= 32, H % 32 == 0); False keeps the vector-ALU kernels."""
+    (used for T > 32, H % 32 == 0); False keeps the vector-ALU kernels."""
     torch = _torch()
     _dev(x, "x", torch.bfloat16)
     _dev(router_w, "router_w", torch.float32)

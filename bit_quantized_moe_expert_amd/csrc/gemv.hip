@@ -88,6 +88,10 @@ __device__ inline void chunk_dot(const char *tab, uint32_t lanebyte, uint4 q, co
 // built, so the table build overlaps their latency.
 constexpr int kGemvWaves = 8;
 constexpr int kGemvWavesRoute = kGemvWaves;  // waves sharing the one-token ranking
+// Grouped launches (many groups, several rounds of workgroups) use 4-wave
+// workgroups so two fit on a CU next to each other's 64 KB table.
+template <int ROUTE>
+constexpr int gemv_waves() { return ROUTE > 0 ? kGemvWaves : 4; }
 
 // Wave-loads (16 bytes per lane each) a wave keeps in flight: 8 / NJ, at most
 // 16 rows per wave, and 4 when four activation rows are held in registers.
@@ -219,7 +223,7 @@ __device__ inline void route_publish(const GemmArgs &p, const RouteToken<EPL> &r
         o.grp_expert[pos_e] = e;
         o.grp_row0[pos_e] = pos_e;
         o.grp_rows[pos_e] = 1;
-        o.tiles[pos_e] = make_int4(e, pos_e, 1, 0);
+        o.tiles[pos_e] = make_int4(e, pos_e, 1, 1);
       }
       bl += __popcll(sel[j]);
     }
@@ -238,7 +242,8 @@ __device__ inline void route_publish(const GemmArgs &p, const RouteToken<EPL> &r
 // and partial ranks come first, and the weight stream starts right after the
 // barrier, once every wave knows its expert.
 template <int FMT, int EPI, int AF32, int LPR, int NJ, int MS, int ROUTE>
-__global__ __launch_bounds__(kGemvWaves * 64) void k_gemv(GemmArgs p) {
+__global__ __launch_bounds__(gemv_waves<ROUTE>() * 64) void k_gemv(GemmArgs p) {
+  constexpr int NWV = gemv_waves<ROUTE>();
   constexpr int RPL = 64 / LPR;
   constexpr int NL = gemv_loads<LPR, NJ, MS>();
   constexpr int WR = NL * RPL;                       // weight rows per wave (<= 16)
@@ -267,12 +272,12 @@ __global__ __launch_bounds__(kGemvWaves * 64) void k_gemv(GemmArgs p) {
     row0 = p.grp_row0[gi];
   }
   const int64_t ncol = (EPI == EPI_SWIGLU) ? p.N / 2 : p.N;
-  const int64_t u0 = ((int64_t)blockIdx.x * kGemvWaves + wave) * UPW;
+  const int64_t u0 = ((int64_t)blockIdx.x * NWV + wave) * UPW;
   const bool wave_live = u0 < ncol;                  // uniform per wave
   if constexpr (ROUTE > 0) {
     // Table build and partial ranks while the logits load; one barrier; then
     // every wave knows its expert and starts the weight stream.
-    build_pair_table<FMT, kGemvRep>(tab_all, 0, kGemvWaves);
+    build_pair_table<FMT, kGemvRep>(tab_all, 0, NWV);
     route_partial<ROUTE>(p, rt, wave, s_rank);
     lds_barrier();
     e = route_finish<ROUTE>(p, rt, gi, s_rank);
@@ -393,7 +398,7 @@ __global__ __launch_bounds__(kGemvWaves * 64) void k_gemv(GemmArgs p) {
   if constexpr (ROUTE == 0) {
     // The table build overlaps the loads' latency; the barrier orders LDS
     // only, so the loads stay in flight through it.
-    build_pair_table<FMT, kGemvRep>(tab_all, 0, kGemvWaves);
+    build_pair_table<FMT, kGemvRep>(tab_all, 0, NWV);
     lds_barrier();
   }
   if (!wave_live) return;                            // no barrier follows
@@ -479,8 +484,9 @@ static void launch_gemv_t(const GemmArgs &g, hipStream_t s) {
   constexpr int WR = NL * RPL;
   constexpr int UPW = WR / ((EPI == EPI_SWIGLU) ? 2 : 1);
   const int64_t ncol = (EPI == EPI_SWIGLU) ? g.N / 2 : g.N;
-  const dim3 grid((unsigned)cdiv(ncol, kGemvWaves * UPW), (unsigned)(ROUTE > 0 ? g.route_k : g.max_grp));
-  NF4MOE_LAUNCH(g, (k_gemv<FMT, EPI, AF32, LPR, NJ, MS, ROUTE>), grid, dim3(kGemvWaves * 64), s, g);
+  constexpr int NWV = gemv_waves<ROUTE>();
+  const dim3 grid((unsigned)cdiv(ncol, NWV * UPW), (unsigned)(ROUTE > 0 ? g.route_k : g.max_grp));
+  NF4MOE_LAUNCH(g, (k_gemv<FMT, EPI, AF32, LPR, NJ, MS, ROUTE>), grid, dim3(NWV * 64), s, g);
 }
 
 template <int FMT, int EPI, int AF32, int LPR, int NJ>

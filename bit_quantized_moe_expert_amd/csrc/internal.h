@@ -37,7 +37,7 @@ hipError_t launch_dequantize(int fmt, const uint8_t *packed, const void *scale, 
 
 // Router logits. With split_ws (>= router_split_bytes(E, H) bytes, 256-byte
 // aligned) and T >= kMfmaLogitsT, H % 32 == 0: the matrix-core kernel.
-constexpr int kMfmaLogitsT = 32;
+constexpr int kMfmaLogitsT = 33;
 size_t router_split_bytes(int E, int H);
 hipError_t launch_router_logits(const uint16_t *x, int T, int H, const float *W, const float *b,
                                 int E, float *logits, void *split_ws, hipStream_t s);
@@ -64,7 +64,7 @@ struct GemmArgs {
   int R;                    // rows of the routed problem
   const int32_t *grp_expert, *grp_row0, *grp_rows, *n_grp;  // device group list
   int max_grp;
-  const int4 *tiles;        // MFMA path
+  const int4 *tiles;        // MFMA path: (expert, row0, rows, rows of the whole group)
   const int32_t *n_tiles;
   int max_tiles;
   int epi;

@@ -90,7 +90,7 @@ __global__ __launch_bounds__(512) void k_mfma(GemmArgs p, int ntn, int per) {
   if (Lp >= p.max_tiles * ntn) return;
   const int nt = Lp / p.max_tiles, ti = Lp % p.max_tiles;
   if (ti >= *p.n_tiles) return;
-  const int4 tile = p.tiles[ti];  // expert, row0, rows
+  const int4 tile = p.tiles[ti];  // expert, row0, rows, rows of the whole group
   const int e = tile.x, trow0 = tile.y, trows = tile.z;
 
   build_mfma_table<FMT>(reinterpret_cast<uint4 *>(smem));

@@ -230,6 +230,8 @@ hipError_t launch_router_logits(const uint16_t *x, int T, int H, const float *W,
                        x, T, H, planes, b, E, logits);
   } else if (T <= 8) {
     hipLaunchKernelGGL(k_logits_rows<8>, dim3(E), dim3(256), 0, s, x, T, H, W, b, E, logits);
+  } else if (T <= 32) {
+    hipLaunchKernelGGL(k_logits_rows<32>, dim3(E), dim3(256), 0, s, x, T, H, W, b, E, logits);
   } else {
     hipLaunchKernelGGL(k_logits_tiled, dim3((unsigned)cdiv(T, 32), (unsigned)cdiv(E, 64)),
                        dim3(256), 0, s, x, T, H, W, b, E, logits);
@@ -367,7 +369,7 @@ __device__ void build_tiles(const int32_t *grp_expert, const int32_t *grp_row0,
     const int base = s_carry + ex;
     for (int i = 0; i < nt && base + i < max_tiles; ++i) {
       const int r0 = i * bm;
-      tiles[base + i] = make_int4(grp_expert[g], grp_row0[g] + r0, min(bm, rows - r0), 0);
+      tiles[base + i] = make_int4(grp_expert[g], grp_row0[g] + r0, min(bm, rows - r0), rows);
     }
     __syncthreads();
     if (threadIdx.x == 0) s_carry += s_total;

@@ -118,7 +118,7 @@ size_t nf4moe_router_workspace_bytes(int32_t E, int32_t H);
  * [T, E] (all device); fp32-accurate accumulation. The first step of the routed
  * layer (the router, outside the kernel on the pages' "Why it happens" dataflow,
  * inside this library). ws (device, caller-owned, 256-byte aligned) may be NULL;
- * with ws_bytes >= nf4moe_router_workspace_bytes(E, H), T >= 32 and H % 32 == 0
+ * with ws_bytes >= nf4moe_router_workspace_bytes(E, H), T > 32 and H % 32 == 0
  * the product runs on the matrix cores (x exact in bf16, each weight as the
  * exact sum of three bf16 parts, fp32 accumulation), else on the vector ALUs.
  * Errors: INVALID_ARG for T < 0, E outside 1..1024, H <= 0 or H % 8, null or
