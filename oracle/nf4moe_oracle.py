@@ -51,7 +51,7 @@ __all__ = [
     "nf4_quantize", "nf4_dequantize", "mxfp4_quantize", "mxfp4_dequantize",
     "quantize", "dequantize", "block_size",
     "bf16_bits_to_f64", "router_logits", "topk_route", "topk_gap", "permute",
-    "grouped_gemm", "swiglu", "moe_forward", "rel_err",
+    "grouped_gemm", "grouped_dgrad", "swiglu", "moe_forward", "rel_err",
 ]
 
 FMT_NF4 = 0
@@ -330,6 +330,31 @@ def grouped_gemm(a: np.ndarray, a_row_of, fmt: int, B_packed, B_scale, N: int, K
         W = dequantize(fmt, B_packed[e], B_scale[e], N, K).astype(np.float64)
         c[r0:r1] = a[rows[r0:r1]] @ W.T
     return c
+
+
+def grouped_dgrad(dc: np.ndarray, fmt: int, B_packed, B_scale, N: int, K: int,
+                  group_offsets, group_experts=None) -> np.ndarray:
+    """da[r, :] = dc[r] . W[e(r)] in fp64: the input gradient of the grouped GEMM.
+
+    The pages' dgrad_4bit_grouped (page "grouped-nf4-gemm ...", section
+    "Training: the backward is a kernel too"): grad_out @ dequant(B) per
+    expert, decoding each weight exactly as the forward does. With the forward
+    c = a . W^T, dL/da = dL/dc . W, W the decoded [N, K] weights of the group's
+    expert. dc: float64 [R, N] in group order; output [R, K] in the same order.
+    """
+    off = np.asarray(group_offsets, dtype=np.int64)
+    G = off.size - 1
+    gexp = np.arange(G) if group_experts is None else np.asarray(group_experts, dtype=np.int64)
+    R = int(off[-1])
+    da = np.zeros((R, K), dtype=np.float64)
+    for g in range(G):
+        r0, r1 = int(off[g]), int(off[g + 1])
+        if r1 == r0:
+            continue
+        e = int(gexp[g])
+        W = dequantize(fmt, B_packed[e], B_scale[e], N, K).astype(np.float64)
+        da[r0:r1] = dc[r0:r1] @ W
+    return da
 
 
 def swiglu(g: np.ndarray, u: np.ndarray) -> np.ndarray:

@@ -291,6 +291,48 @@ def test_grouped_gemm_triple_loop(fmt):
                 assert abs(c[r, n] - ref) <= 1e-12 * (1 + abs(ref))
 
 
+@pytest.mark.parametrize("fmt", [O.FMT_NF4, O.FMT_MXFP4])
+def test_grouped_dgrad_triple_loop(fmt):
+    """dgrad (page "grouped-nf4-gemm ...", "Training: the backward is a kernel
+    too": grad_out @ dequant(B)) against explicit sums over n of the
+    pure-Python decode, groups with an empty one in the middle."""
+    rng = np.random.default_rng(14)
+    E, N, K = 3, 7, 128
+    Wf = rng.standard_normal((E, N, K)).astype(np.float32) * np.float32(0.02)
+    qs = [O.quantize(fmt, Wf[e]) for e in range(E)]
+    Bp = np.stack([q[0] for q in qs]); Bs = np.stack([q[1] for q in qs])
+    off, gexp = [0, 2, 2, 5], [2, 0, 1]
+    dc = rng.standard_normal((5, N))
+    da = O.grouped_dgrad(dc, fmt, Bp, Bs, N, K, off, gexp)
+    Wd = [_deq_py(fmt, Bp[e], Bs[e], N, K) for e in range(E)]
+    for g in range(3):
+        for r in range(off[g], off[g + 1]):
+            for kk in range(K):
+                ref = math.fsum(dc[r, n] * Wd[gexp[g]][n][kk] for n in range(N))
+                assert abs(da[r, kk] - ref) <= 1e-12 * (1 + abs(ref))
+
+
+def test_grouped_dgrad_is_the_adjoint_of_the_forward():
+    """<dc, a W^T> = <a, dc W> per group: the backward is the forward's adjoint
+    (a transposed or misindexed W in either would break the identity)."""
+    rng = np.random.default_rng(15)
+    E, N, K = 2, 96, 192
+    Wf = rng.standard_normal((E, N, K)).astype(np.float32) * np.float32(0.05)
+    qs = [O.nf4_quantize(Wf[e]) for e in range(E)]
+    Bp = np.stack([q[0] for q in qs]); Bs = np.stack([q[1] for q in qs])
+    off, gexp = [0, 3, 7], [1, 0]
+    a = rng.standard_normal((7, K))
+    dc = rng.standard_normal((7, N))
+    c = O.grouped_gemm(a, None, O.FMT_NF4, Bp, Bs, N, K, off, gexp)
+    da = O.grouped_dgrad(dc, O.FMT_NF4, Bp, Bs, N, K, off, gexp)
+    lhs, rhs = math.fsum((dc * c).ravel()), math.fsum((a * da).ravel())
+    assert abs(lhs - rhs) <= 1e-10 * (1 + abs(lhs))
+    # and a unit gradient row picks one decoded weight row
+    e1 = np.zeros((1, N)); e1[0, 11] = 1.0
+    row = O.grouped_dgrad(e1, O.FMT_NF4, Bp, Bs, N, K, [0, 1], [1])
+    assert np.array_equal(row[0], O.nf4_dequantize(Bp[1], Bs[1], N, K)[11].astype(np.float64))
+
+
 def test_unit_vector_picks_column():
     rng = np.random.default_rng(8)
     Wf = rng.standard_normal((1, 6, 64)).astype(np.float32)
