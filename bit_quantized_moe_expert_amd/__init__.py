@@ -70,6 +70,8 @@ def lib() -> ctypes.CDLL:
         "nf4moe_grouped_gemm": [ctypes.c_int, vp, vp, i32, vp, vp, i32, i64, i64, i32, vp, vp, i32,
                                 vp, ctypes.c_int, i32, vp, sz, vp],
         "nf4moe_workspace_bytes": [ctypes.POINTER(Layer), i32],
+        "nf4moe_grouped_dgrad": [ctypes.c_int, vp, vp, vp, i32, i64, i64, i32, vp, vp, i32, vp,
+                                 ctypes.c_int, vp, sz, vp],
         "nf4moe_moe_forward": [ctypes.POINTER(Layer), vp, i32, vp, vp, vp, vp, sz, vp],
         "nf4moe_moe_forward_profiled": [ctypes.POINTER(Layer), vp, i32, vp, vp, sz, vp,
                                         ctypes.POINTER(ctypes.c_void_p)],
@@ -236,6 +238,32 @@ def grouped_gemm(a, B, B_scale, group_offsets, K: int, R: int, group_experts=Non
                                      E, N, K, G, _ptr(group_offsets), _ptr(group_experts), R, _ptr(c),
                                      dt, path, wsp, nb, _stream()))
     return c
+
+
+def grouped_dgrad(dc, B, B_scale, group_offsets, K: int, group_experts=None, fmt: int = FMT_NF4,
+                  out_dtype=None):
+    """The pages' dgrad_4bit_grouped: da[r] = dc[r] . W[e(r)], W decoded from 4-bit
+    codes in registers (the input gradient of grouped_gemm). dc bf16 [R, N] in group
+    order; B [E, N, K/2] u8; group_offsets int32 [G+1] (device). Returns da [R, K]."""
+    torch = _torch()
+    out_dtype = out_dtype or torch.float32
+    _dev(dc, "dc", torch.bfloat16)
+    _dev(B, "B", torch.uint8)
+    _dev(B_scale, "B_scale", _scale_dtype(fmt))
+    _dev(group_offsets, "group_offsets", torch.int32)
+    if group_experts is not None:
+        _dev(group_experts, "group_experts", torch.int32)
+    R, N = dc.shape
+    E = B.shape[0]
+    G = group_offsets.numel() - 1
+    da = torch.empty(R, K, dtype=out_dtype, device=dc.device)
+    need = lib().nf4moe_gemm_workspace_bytes(G, R)
+    ws, wsp, nb = _workspace(need, dc.device)
+    dt = DT_F32 if out_dtype == torch.float32 else DT_BF16
+    _check(lib().nf4moe_grouped_dgrad(fmt, _ptr(dc), _ptr(B), _ptr(B_scale), E, N, K, G,
+                                      _ptr(group_offsets), _ptr(group_experts), R, _ptr(da), dt,
+                                      wsp, nb, _stream()))
+    return da
 
 
 @dataclass

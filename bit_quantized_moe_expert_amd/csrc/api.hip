@@ -7,6 +7,7 @@
 
 #include "../../include/nf4moe.h"
 #include "common.h"
+#include "dgrad.h"
 #include "internal.h"
 
 using namespace nf4moe;
@@ -334,6 +335,55 @@ nf4moe_status_t nf4moe_grouped_gemm(nf4moe_format_t fmt, const uint16_t *a, cons
   else
     e = launch_mfma_grouped(g, s);
   return hip_status(e, "grouped GEMM launch");
+}
+
+nf4moe_status_t nf4moe_grouped_dgrad(nf4moe_format_t fmt, const uint16_t *dc, const uint8_t *B,
+                                     const void *B_scale, int32_t E, int64_t N, int64_t K, int32_t G,
+                                     const int32_t *group_offsets, const int32_t *group_experts,
+                                     int32_t R, void *da, nf4moe_dtype_t da_dtype, void *ws,
+                                     size_t ws_bytes, void *stream) {
+  if (!fmt_ok(fmt)) return fail(NF4MOE_ERR_INVALID_ARG, "unknown format %d", (int)fmt);
+  const int blk = fmt_block(fmt);
+  if (K <= 0 || K % blk) return fail(NF4MOE_ERR_INVALID_ARG, "K=%lld must be a positive multiple of %d", (long long)K, blk);
+  if (N <= 0) return fail(NF4MOE_ERR_INVALID_ARG, "N=%lld must be positive", (long long)N);
+  if (N % 64) return fail(NF4MOE_ERR_UNSUPPORTED, "dgrad needs N %% 64 == 0 (N=%lld)", (long long)N);
+  if (E < 1) return fail(NF4MOE_ERR_INVALID_ARG, "E=%d must be positive", E);
+  if (G < 1 || G > 65536) return fail(NF4MOE_ERR_INVALID_ARG, "G=%d outside 1..65536", G);
+  if (R < 0) return fail(NF4MOE_ERR_INVALID_ARG, "R=%d < 0", R);
+  if (da_dtype != NF4MOE_DT_F32 && da_dtype != NF4MOE_DT_BF16)
+    return fail(NF4MOE_ERR_INVALID_ARG, "unknown output dtype %d", (int)da_dtype);
+  if (!group_offsets) return fail(NF4MOE_ERR_INVALID_ARG, "group_offsets is NULL");
+  if (R > 0 && (!dc || !B || !B_scale || !da)) return fail(NF4MOE_ERR_INVALID_ARG, "NULL pointer");
+  if (R > 0 && (!aligned(dc, 16) || !aligned(da, 4) || (fmt == NF4MOE_FMT_NF4_B64 && !aligned(B_scale, 4))))
+    return fail(NF4MOE_ERR_INVALID_ARG, "misaligned pointer");
+  const size_t need = nf4moe_gemm_workspace_bytes(G, R);
+  if (!ws || ws_bytes < need)
+    return fail(NF4MOE_ERR_WORKSPACE, "workspace %zu bytes < %zu required", ws_bytes, need);
+  if (!aligned(ws, 256)) return fail(NF4MOE_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  if (R == 0) return NF4MOE_OK;
+  hipStream_t s = (hipStream_t)stream;
+  Carve cv(ws);
+  RouteBufs rb;
+  rb.grp_expert = cv.take<int32_t>(G);
+  rb.grp_row0 = cv.take<int32_t>(G);
+  rb.grp_rows = cv.take<int32_t>(G);
+  rb.counters = cv.take<int32_t>(16);
+  rb.tiles = cv.take<int4>((size_t)cdiv(R, kMfmaBM) + G);
+  hipError_t e = launch_groups_from_offsets(group_offsets, group_experts, G, R, E, rb, kMfmaBM, s);
+  if (e != hipSuccess) return hip_status(e, "group table launch");
+  DgradArgs a;
+  a.fmt = (int)fmt;
+  a.dc = dc;
+  a.B = B;
+  a.B_scale = B_scale;
+  a.N = N;
+  a.K = K;
+  a.tiles = rb.tiles;
+  a.n_tiles = rb.counters + 1;
+  a.max_tiles = (int)(cdiv(R, kMfmaBM) + G);
+  a.da = da;
+  a.da_bf16 = da_dtype == NF4MOE_DT_BF16;
+  return hip_status(launch_dgrad(a, s), "dgrad launch");
 }
 
 size_t nf4moe_workspace_bytes(const nf4moe_layer_t *layer, int32_t T_max) {

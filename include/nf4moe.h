@@ -174,6 +174,26 @@ nf4moe_status_t nf4moe_grouped_gemm(nf4moe_format_t fmt, const uint16_t *a, cons
                                     nf4moe_dtype_t c_dtype, int32_t path, void *ws, size_t ws_bytes,
                                     void *stream);
 
+/* nf4moe_grouped_dgrad -- the pages' dgrad_4bit_grouped (grouped-nf4-gemm page,
+ * "Training: the backward is a kernel too"): the input gradient of
+ * nf4moe_grouped_gemm, da[r, :] = dc[r, :] . W[e(r)] over routed groups, W the
+ * [N, K] weights decoded from 4-bit codes exactly as the forward decodes them
+ * (never written out), fp32 accumulation.
+ *   dc       bf16 [R, N] gradient of the GEMM output, rows in group order (device,
+ *            16-byte aligned)
+ *   B, B_scale  expert stack [E, N, K/2] + scales in `fmt` (device)
+ *   G, group_offsets, group_experts  as nf4moe_grouped_gemm (empty groups allowed)
+ *   da       [R, K] fp32 or bf16 (RNE), same row order (device)
+ *   ws       nf4moe_gemm_workspace_bytes(G, R) bytes, 256-byte aligned (device)
+ * Matrix-core kernel for every R (tiles of 128 rows x 128 columns).
+ * Errors: INVALID_ARG (K not a multiple of the format block, bad sizes, null or
+ * misaligned pointers), UNSUPPORTED (N % 64 != 0), WORKSPACE. */
+nf4moe_status_t nf4moe_grouped_dgrad(nf4moe_format_t fmt, const uint16_t *dc, const uint8_t *B,
+                                     const void *B_scale, int32_t E, int64_t N, int64_t K, int32_t G,
+                                     const int32_t *group_offsets, const int32_t *group_experts,
+                                     int32_t R, void *da, nf4moe_dtype_t da_dtype, void *ws,
+                                     size_t ws_bytes, void *stream);
+
 /* nf4moe_workspace_bytes -- workspace nf4moe_moe_forward needs for T <= T_max. */
 size_t nf4moe_workspace_bytes(const nf4moe_layer_t *layer, int32_t T_max);
 

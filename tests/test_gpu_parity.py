@@ -161,6 +161,47 @@ def test_grouped_gemm_ragged(fmt, N, K, path):
     check_bound(got, ref, f"ragged fmt={fmt} N={N} K={K} path={path}")
 
 
+# --------------------------------------------------------------------- grouped dgrad
+def _dgrad_case(fmt, N, K, E, sizes, experts, out_dtype, seed):
+    rng = np.random.default_rng(seed)
+    Wf = (rng.standard_normal((E, N, K)) * 0.02).astype(np.float32)
+    pk, sc = M.quantize(torch.from_numpy(Wf).to(DEV), fmt)
+    qs = [O.quantize(fmt, Wf[e]) for e in range(E)]
+    Bp = np.stack([q[0] for q in qs]); Bs = np.stack([q[1] for q in qs])
+    R = int(sum(sizes))
+    off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    dcb = S.f32_to_bf16_bits(rng.standard_normal((R, N)).astype(np.float32))
+    da = M.grouped_dgrad(bits_to_torch_bf16(dcb), pk, sc, torch.from_numpy(off).to(DEV), K,
+                         group_experts=torch.from_numpy(np.array(experts, np.int32)).to(DEV),
+                         fmt=fmt, out_dtype=out_dtype)
+    got = bf16_to_np(da) if out_dtype == torch.bfloat16 else da.cpu().numpy().astype(np.float64)
+    ref = O.grouped_dgrad(O.bf16_bits_to_f64(dcb), fmt, Bp, Bs, N, K, off, experts)
+    return got, ref
+
+
+@pytest.mark.parametrize("fmt,N,K,sizes", [
+    (O.FMT_NF4, 256, 512, [3, 1, 4]),                    # the page example's shapes
+    (O.FMT_NF4, 192, 320, [1, 130, 0, 169, 2]),          # ragged rows, a ragged column tile
+    (O.FMT_MXFP4, 320, 288, [5, 0, 129, 7]),             # MXFP4, K % 128 != 0
+    (O.FMT_NF4, 2048, 1024, [257, 3, 0, 64]),            # OLMoE-shaped gate_up dgrad
+    (O.FMT_MXFP4, 2880, 2880, [40, 131]),                # gpt-oss-shaped
+])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_grouped_dgrad(fmt, N, K, sizes, dtype):
+    od = torch.float32 if dtype == "f32" else torch.bfloat16
+    experts = [(3 * i + 1) % 6 for i in range(len(sizes))]
+    got, ref = _dgrad_case(fmt, N, K, 6, sizes, experts, od, seed=N + K + len(sizes))
+    check_bound(got, ref, f"dgrad fmt={fmt} N={N} K={K}")
+
+
+def test_grouped_dgrad_rejects_unsupported_n():
+    pk = torch.zeros(1, 96, 32, dtype=torch.uint8, device=DEV)
+    sc = torch.ones(1, 96, 1, dtype=torch.float32, device=DEV)
+    dc = torch.zeros(2, 96, dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(M.Nf4MoeError, match="UNSUPPORTED"):
+        M.grouped_dgrad(dc, pk, sc, torch.tensor([0, 2], dtype=torch.int32, device=DEV), 64)
+
+
 # --------------------------------------------------------------------- full forward
 def _forward_case(wl, T, path=0, on_device_rng=False, sample=None):
     dev_layer, o_layer, _ = build_layers(wl, 0, DEV, on_device_rng=on_device_rng, path=path)
