@@ -35,6 +35,10 @@ def parse():
     ap.add_argument("--graph", type=int, default=1, help="1: time HIP-graph replays as well")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--op", default="forward", choices=["forward", "dgrad"],
+                    help="forward: the routed MoE layer (default). dgrad: the input gradients "
+                         "of the layer's two grouped GEMMs (gate_up and down) on the forward's "
+                         "routing, for training-shaped token counts")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain elementwise copy of MIB MiB (read + write once) five "
                          "times, for scaling the FETCH_SIZE / WRITE_SIZE counters, and exit")
@@ -104,6 +108,9 @@ def main():
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE={world}); "
               "this build has no multi-GPU path.", file=sys.stderr)
         sys.exit(2)
+    if args.op == "dgrad":
+        bench_dgrad(args)
+        return
 
     import numpy as np
     import torch
@@ -271,6 +278,109 @@ def main():
                             "down_combine": down_ms},
         "roofline": roof,
         "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def bench_dgrad(args):
+    """One step = the input gradients of one layer's two grouped GEMMs
+    (grouped_dgrad through gate_up [E, 2I, H] and down [E, H, I]) on the routing
+    the forward computes for a synthetic batch, with random bf16 output
+    gradients, rotating over independently seeded layers."""
+    import ctypes
+    import numpy as np
+    import torch
+    import moe_synth as S
+    import bit_quantized_moe_expert_amd as M
+
+    wl = S.WORKLOADS[args.workload if args.workload != "olmoe_decode" else "olmoe_prefill"]
+    T = args.tokens or wl.tokens[-1]
+    nlayers = args.layers or wl.layers
+    steps = args.steps or 4 * nlayers
+    warmup = args.warmup if args.warmup is not None else nlayers
+    dev = torch.device("cuda", 0)
+    R = T * wl.top_k
+    L = M.lib()
+    setups = []
+    for l in range(nlayers):
+        W_r, b_r = S.make_router(wl, l)
+        w13 = S.make_stack_torch(wl, l, "w13", dev)
+        p13, s13 = M.quantize(w13, wl.fmt)
+        del w13
+        w2 = S.make_stack_torch(wl, l, "w2", dev)
+        p2, s2 = M.quantize(w2, wl.fmt)
+        del w2
+        xb = S.make_x(wl, T, l)
+        x = torch.from_numpy(xb.view(np.int16)).to(dev).view(torch.bfloat16)
+        logits = M.router_logits(x, torch.from_numpy(W_r).to(dev),
+                                 None if b_r is None else torch.from_numpy(b_r).to(dev))
+        off = M.route_permute(logits, wl.top_k, bool(wl.renormalize))["expert_offsets"]
+        g = torch.Generator(device=dev).manual_seed(7000 + l)
+        dc13 = torch.randn(R, 2 * wl.I, generator=g, device=dev).to(torch.bfloat16)
+        dc2 = torch.randn(R, wl.H, generator=g, device=dev).to(torch.bfloat16)
+        setups.append((p13, s13, p2, s2, off, dc13, dc2))
+    G = wl.E
+    need = L.nf4moe_gemm_workspace_bytes(G, R)
+    ws = torch.empty(need + 256, dtype=torch.uint8, device=dev)
+    wsp = ctypes.c_void_p((ws.data_ptr() + 255) // 256 * 256)
+    da13 = torch.empty(R, wl.H, dtype=torch.float32, device=dev)
+    da2 = torch.empty(R, wl.I, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    p = M._ptr
+
+    def call(i, which):
+        p13, s13, p2, s2, off, dc13, dc2 = setups[i % nlayers]
+        if which == 0:
+            st = L.nf4moe_grouped_dgrad(wl.fmt, p(dc13), p(p13), p(s13), wl.E, 2 * wl.I, wl.H, G, p(off),
+                                        None, R, p(da13), M.DT_F32, wsp, need, sp)
+        else:
+            st = L.nf4moe_grouped_dgrad(wl.fmt, p(dc2), p(p2), p(s2), wl.E, wl.H, wl.I, G, p(off),
+                                        None, R, p(da2), M.DT_F32, wsp, need, sp)
+        if st != 0:
+            M._check(st)
+
+    for i in range(warmup):
+        call(i, 0)
+        call(i, 1)
+    torch.cuda.synchronize()
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    t_gu, t_dn = 0.0, 0.0
+    e[0].record(stream)
+    for i in range(steps):
+        call(i, 0)
+        call(i, 1)
+    e[1].record(stream)
+    torch.cuda.synchronize()
+    ms = e[0].elapsed_time(e[1]) / steps
+    # per-GEMM split on a second pass
+    per = [[], []]
+    for i in range(min(steps, 4 * nlayers)):
+        for which in (0, 1):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            call(i, which)
+            b.record(stream)
+            per[which].append((a, b))
+    torch.cuda.synchronize()
+    gu_ms = float(np.mean([a.elapsed_time(b) for a, b in per[0]]))
+    dn_ms = float(np.mean([a.elapsed_time(b) for a, b in per[1]]))
+    flops = 6.0 * R * wl.H * wl.I
+    gu_flops = 4.0 * R * wl.H * wl.I
+    line = {
+        "metric": "grouped dgrad TFLOP/s (input gradients of gate_up and down on 4-bit weights)",
+        "value": flops / (ms * 1e-3) / 1e12, "unit": "TFLOP/s", "n_gpus": 1, "steps": steps,
+        "warmup": warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (forward routing of seeded N(0,1) tokens, N(0,1) bf16 output gradients)",
+        "config": {"workload": wl.name + "_dgrad", "format": "nf4_b64" if wl.fmt == 0 else "mxfp4_b32",
+                   "E": wl.E, "top_k": wl.top_k, "H": wl.H, "I": wl.I, "T": T, "R": R, "layers": nlayers,
+                   "timing": "eager"},
+        "gate_up_dgrad_ms_mean": gu_ms, "down_dgrad_ms_mean": dn_ms,
+        "roofline": {"bound": "mfma", "achieved": gu_flops / (gu_ms * 1e-3) / 1e12, "peak": BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": gu_flops / (gu_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+                     "traffic": None, "kernel": "k_dgrad (gate_up, events around the call)"},
+        "cpu_baseline": None,
     }
     print(json.dumps(line), flush=True)
 
