@@ -421,7 +421,10 @@ static nf4moe_status_t forward_impl(const nf4moe_layer_t *layer, const uint16_t 
   };
   ForwardCarve fc = carve_forward(ws, L, T);
   if ((e = mark(0)) != hipSuccess) return hip_status(e, "event record");
-  e = launch_router_logits(x, T, L.H, L.router_w, L.router_b, L.E, fc.logits, fc.rsplit, s);
+  // The small-M path keeps each token's bits independent of T: per-token
+  // router logits for every T, and kernels whose per-row order is fixed.
+  const bool small = use == NF4MOE_PATH_SMALL_M;
+  e = launch_router_logits(x, T, L.H, L.router_w, L.router_b, L.E, fc.logits, fc.rsplit, s, small);
   if (e != hipSuccess) return hip_status(e, "router launch");
   // One decode token on the small-M path: top-k and grouping happen inside the
   // gate_up kernel; otherwise they are their own launches.
@@ -472,7 +475,7 @@ static nf4moe_status_t forward_impl(const nf4moe_layer_t *layer, const uint16_t 
   if ((e = mark(2)) != hipSuccess) return hip_status(e, "event record");
 
   // down projection + router-weighted combine
-  if (use == NF4MOE_PATH_SMALL_M && T <= kTokenCentricT) {
+  if (small && T <= kTokenCentricT && down_combine_supported(L.I, L.top_k)) {
     e = launch_gemv_down_combine((int)L.fmt, fc.h, fc.rb.slot_pos, fc.rb.topk_ids, fc.rb.topk_w, T,
                                  L.top_k, L.w2, L.w2_scale, L.H, L.I, out, s);
     if (e != hipSuccess) return hip_status(e, "down launch");

@@ -193,19 +193,30 @@ __device__ inline void route_publish(const GemmArgs &p, const RouteToken<EPL> &r
   const int *rank = r.rank;
   const uint64_t *sel = r.sel;
   {
-    float vmax = -__builtin_inff(), part = 0.0f, full = 0.0f;
+    float vmax = -__builtin_inff();
 #pragma unroll
     for (int j = 0; j < EPL; ++j)
       if (lane + 64 * j < E && rank[j] == 0) vmax = r.v[j];
     vmax = wave_max(vmax);
+    // The denominator in the routing kernels' one order: selected experts by
+    // rank, or every expert by id.
+    float ex[EPL];
 #pragma unroll
-    for (int j = 0; j < EPL; ++j) {
-      const bool chosen = (sel[j] >> lane) & 1;
-      const float ex = lane + 64 * j < E ? expf(r.v[j] - vmax) : 0.0f;
-      part += chosen ? ex : 0.0f;
-      full += ex;
+    for (int j = 0; j < EPL; ++j) ex[j] = lane + 64 * j < E ? expf(r.v[j] - vmax) : 0.0f;
+    float denom = 0.0f;
+    if (p.route_renorm) {
+      for (int q = 0; q < k; ++q) {
+#pragma unroll
+        for (int j = 0; j < EPL; ++j) {
+          const uint64_t hit = __ballot(lane + 64 * j < E && rank[j] == q);
+          if (hit) denom += __shfl(ex[j], (int)__builtin_ctzll(hit), kWave);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < EPL; ++j)
+        for (int l = 0; l < 64 && 64 * j + l < E; ++l) denom += __shfl(ex[j], l, kWave);
     }
-    const float denom = wave_sum(p.route_renorm ? part : full);
     const RouteBufs &o = p.route_out;
     int bl = 0;
 #pragma unroll
@@ -568,12 +579,15 @@ hipError_t launch_gemv_grouped(const GemmArgs &g, int ms_hint, hipStream_t s) {
 // ---------------------------------------------------------------------------
 // Token-centric down projection fused with the router-weighted combine, for a
 // handful of tokens: out[t, n] = bf16( sum_j w[t,j] * h[pos(t,j)] . W2[e_j][n] ).
-// A workgroup owns RB output rows of one token; the k (slot, chunk) pairs of a
-// row are spread over the 4 waves, each lane keeping its slot's activations
-// (already multiplied by the routing weight) in registers; the four wave
-// partials of a row are added in wave order, so the result is deterministic.
+// It takes the same arithmetic steps, in the same order, as the grouped GEMV
+// (slot output) followed by k_combine, so a token gets the same bits from
+// either pair of kernels: per slot j, each of LPR lanes sums its chunks
+// c = li + LPR * jj (jj < NJ; a chunk's 32-term dot times its block scale), the
+// lanes meet in seg_sum<LPR>, s_j = w_j * y_j, and out = bf16 of the fp32 sum
+// of s_0, s_1, ... from 0. A workgroup owns RB output rows of one token; its 4
+// waves hold 4 * 64 / LPR lane segments, one slot each per pass (NP passes).
 // ---------------------------------------------------------------------------
-template <int FMT, int NQ, int RB>
+template <int FMT, int LPR, int NJ, int NP, int RB>
 __global__ __launch_bounds__(256) void k_down_combine(const float *__restrict__ h,
                                                       const int32_t *__restrict__ slot_pos,
                                                       const int32_t *__restrict__ topk_ids,
@@ -581,132 +595,169 @@ __global__ __launch_bounds__(256) void k_down_combine(const float *__restrict__ 
                                                       int k, const uint8_t *__restrict__ w2,
                                                       const void *__restrict__ w2s, int H, int I,
                                                       uint16_t *__restrict__ out) {
+  constexpr int SPW = 64 / LPR;      // lane segments per wave
+  constexpr int NSEG = 4 * SPW;      // slots per pass
   __shared__ float2 tab_all[256 * kGemvRep];
-  __shared__ float red[4][RB];
+  __shared__ float red[kMaxTopK][RB];
   const int t = blockIdx.y;
   const int n0 = blockIdx.x * RB;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int seg = wave * SPW + lane / LPR, li = lane % LPR;
   const int nch = I / 32;
-  const int Q = k * nch;
-  const int QW = (Q + 3) / 4;
   const int64_t rowbytes = I / 2;
   const int64_t sc_per_row = I / Fmt<FMT>::kBlock;
 
-  // (slot, chunk) pairs of this lane: routing metadata first (written by the
-  // previous kernel), the LDS table built while it arrives, then addresses.
-  bool live[NQ];
-  int cq[NQ], eraw[NQ], praw[NQ];
-  float wj[NQ];
+  // Routing metadata first (written by the previous kernel), the LDS table
+  // built while it arrives, then addresses.
+  bool live[NP];
+  int eraw[NP], praw[NP];
+  float wj[NP];
 #pragma unroll
-  for (int qi = 0; qi < NQ; ++qi) {
-    const int ql = qi * 64 + lane;
-    const int q = wave * QW + ql;
-    live[qi] = ql < QW && q < Q;
-    const int j = live[qi] ? q / nch : 0;
-    cq[qi] = live[qi] ? q % nch : 0;
-    const int slot = t * k + j;
-    eraw[qi] = topk_ids[slot];
-    wj[qi] = topk_w[slot];
-    praw[qi] = slot_pos[slot];
+  for (int q = 0; q < NP; ++q) {
+    const int j = q * NSEG + seg;
+    live[q] = j < k;
+    const int slot = t * k + (live[q] ? j : 0);
+    eraw[q] = topk_ids[slot];
+    wj[q] = topk_w[slot];
+    praw[q] = slot_pos[slot];
   }
   __builtin_amdgcn_sched_barrier(0);
   build_pair_table<FMT, kGemvRep>(tab_all, 0, 4);
   __builtin_amdgcn_sched_barrier(0);
-  const uint8_t *wbase[NQ];
-  int64_t sbase[NQ];
-  int64_t hoff[NQ];
+  // Chunks past the row end read chunk 0 and get scale 0, as in the GEMV.
+  bool cok[NJ];
+  int64_t cc[NJ];
 #pragma unroll
-  for (int qi = 0; qi < NQ; ++qi) {
-    const int c = cq[qi];
-    hoff[qi] = (int64_t)praw[qi] * I + (int64_t)c * 32;
-    wbase[qi] = w2 + (int64_t)eraw[qi] * H * rowbytes + (int64_t)c * 16;
-    sbase[qi] = (int64_t)eraw[qi] * H * sc_per_row + (FMT == 0 ? (c >> 1) : c);
+  for (int jj = 0; jj < NJ; ++jj) {
+    const int c = li + LPR * jj;
+    cok[jj] = c < nch;
+    cc[jj] = cok[jj] ? c : 0;
   }
   // Loads: activations first, then weights in row order (vector loads retire
   // in issue order, so row n waits only for its own data); all unconditional
-  // from clamped addresses. An idle lane gets weight 0, a row past H scale 0.
-  uint4 hraw[NQ][8];
+  // from clamped addresses.
+  uint4 hraw[NP][NJ][8];
 #pragma unroll
-  for (int qi = 0; qi < NQ; ++qi) {
-    const uint4 *src = reinterpret_cast<const uint4 *>(h + hoff[qi]);
+  for (int q = 0; q < NP; ++q)
 #pragma unroll
-    for (int w = 0; w < 8; ++w) hraw[qi][w] = src[w];
-  }
-  uint4 wq[RB][NQ];
-  float sc[RB][NQ];
+    for (int jj = 0; jj < NJ; ++jj) {
+      const uint4 *src = reinterpret_cast<const uint4 *>(h + (int64_t)praw[q] * I + cc[jj] * 32);
+#pragma unroll
+      for (int w = 0; w < 8; ++w) hraw[q][jj][w] = src[w];
+    }
+  uint4 wq[RB][NP][NJ];
+  float sc[RB][NP][NJ];
 #pragma unroll
   for (int n = 0; n < RB; ++n) {
+    const int row = n0 + n;
+    const int64_t rc = row < H ? row : H - 1;
 #pragma unroll
-    for (int qi = 0; qi < NQ; ++qi) {
-      const int row = n0 + n;
-      const int64_t rc = row < H ? row : H - 1;
-      wq[n][qi] = *reinterpret_cast<const uint4 *>(wbase[qi] + rc * rowbytes);
-      sc[n][qi] = block_scale<FMT>(w2s, sbase[qi] + rc * sc_per_row);
-    }
+    for (int q = 0; q < NP; ++q)
+#pragma unroll
+      for (int jj = 0; jj < NJ; ++jj) {
+        const int64_t eb = (int64_t)eraw[q] * H;
+        wq[n][q][jj] = *reinterpret_cast<const uint4 *>(w2 + (eb + rc) * rowbytes + cc[jj] * 16);
+        sc[n][q][jj] = block_scale<FMT>(w2s, (eb + rc) * sc_per_row + (FMT == 0 ? (cc[jj] >> 1) : cc[jj]));
+      }
   }
   __builtin_amdgcn_sched_barrier(0);  // every load is in flight before any wait
   lds_barrier();                      // the table is complete; the loads stay in flight
-  float hv[NQ][32];
-#pragma unroll
-  for (int qi = 0; qi < NQ; ++qi) {
-    const float wv = live[qi] ? wj[qi] : 0.0f;
-#pragma unroll
-    for (int w = 0; w < 8; ++w) {
-      hv[qi][4 * w + 0] = __uint_as_float(hraw[qi][w].x) * wv;
-      hv[qi][4 * w + 1] = __uint_as_float(hraw[qi][w].y) * wv;
-      hv[qi][4 * w + 2] = __uint_as_float(hraw[qi][w].z) * wv;
-      hv[qi][4 * w + 3] = __uint_as_float(hraw[qi][w].w) * wv;
-    }
-  }
   const char *tab = reinterpret_cast<const char *>(tab_all);
   const uint32_t lanebyte = (uint32_t)(lane & (kGemvRep - 1)) * 8u;
 #pragma unroll
   for (int n = 0; n < RB; ++n) {
-    float acc = 0.0f;
 #pragma unroll
-    for (int qi = 0; qi < NQ; ++qi) {
-      float dot = 0.0f;
-      float xj[1][32];
+    for (int q = 0; q < NP; ++q) {
+      float acc = 0.0f;
 #pragma unroll
-      for (int i = 0; i < 32; ++i) xj[0][i] = hv[qi][i];
-      chunk_dot<1>(tab, lanebyte, wq[n][qi], xj, &dot);
-      acc = fmaf((n0 + n < H) ? sc[n][qi] : 0.0f, dot, acc);
+      for (int jj = 0; jj < NJ; ++jj) {
+        float xj[1][32];
+#pragma unroll
+        for (int w = 0; w < 8; ++w) {
+          xj[0][4 * w + 0] = __uint_as_float(hraw[q][jj][w].x);
+          xj[0][4 * w + 1] = __uint_as_float(hraw[q][jj][w].y);
+          xj[0][4 * w + 2] = __uint_as_float(hraw[q][jj][w].z);
+          xj[0][4 * w + 3] = __uint_as_float(hraw[q][jj][w].w);
+        }
+        float dot = 0.0f;
+        chunk_dot<1>(tab, lanebyte, wq[n][q][jj], xj, &dot);
+        acc = fmaf((cok[jj] && n0 + n < H) ? sc[n][q][jj] : 0.0f, dot, acc);
+      }
+      acc = seg_sum<LPR>(acc);
+      if (li == 0 && live[q]) red[q * NSEG + seg][n] = wj[q] * acc;
     }
-    acc = wave_sum(acc);
-    if (lane == 0) red[wave][n] = acc;
   }
   lds_barrier();
   if (threadIdx.x < RB && n0 + (int)threadIdx.x < H) {
     const int n = threadIdx.x;
-    const float v = ((red[0][n] + red[1][n]) + red[2][n]) + red[3][n];
+    float v = 0.0f;
+    for (int j = 0; j < k; ++j) v += red[j][n];
     out[(int64_t)t * H + n0 + n] = (uint16_t)f32_to_bf16_rne(v);
   }
+}
+
+template <int FMT, int LPR, int NJ, int NP>
+static void launch_down_combine_t(const float *h, const int32_t *slot_pos, const int32_t *topk_ids,
+                                  const float *topk_w, int T, int k, const uint8_t *w2,
+                                  const void *w2_scale, int H, int I, uint16_t *out, hipStream_t s) {
+  constexpr int RB = 8;
+  const dim3 grid((unsigned)cdiv(H, RB), (unsigned)T);
+  hipLaunchKernelGGL((k_down_combine<FMT, LPR, NJ, NP, RB>), grid, dim3(256), 0, s, h, slot_pos, topk_ids,
+                     topk_w, T, k, w2, w2_scale, H, I, out);
+}
+
+// Lane-segment shape of the grouped GEMV for K = I (pick_shape's rule): LPR
+// lanes per row, NJ chunks per lane.
+static void gemv_segment_shape(int64_t nch, int *lpr, int *nj) {
+  *nj = nch > 64 ? 2 : 1;
+  *lpr = nch > 32 ? 64 : (nch > 16 ? 32 : 16);
+}
+
+bool down_combine_supported(int I, int k) {
+  const int64_t nch = I / 32;
+  if (nch > 128 || k > kMaxTopK) return false;
+  int lpr, nj;
+  gemv_segment_shape(nch, &lpr, &nj);
+  const int np = (k + 4 * (64 / lpr) - 1) / (4 * (64 / lpr));
+  return np * nj <= 2;  // activation and weight registers of at most two chunk passes
+}
+
+template <int FMT, int LPR, int NJ>
+static void down_combine_passes(const float *h, const int32_t *slot_pos, const int32_t *topk_ids,
+                                const float *topk_w, int T, int k, const uint8_t *w2,
+                                const void *w2_scale, int H, int I, uint16_t *out, hipStream_t s) {
+  constexpr int NSEG = 4 * (64 / LPR);
+  if (NJ == 1 && k > NSEG)
+    launch_down_combine_t<FMT, LPR, 1, 2>(h, slot_pos, topk_ids, topk_w, T, k, w2, w2_scale, H, I, out, s);
+  else
+    launch_down_combine_t<FMT, LPR, NJ, 1>(h, slot_pos, topk_ids, topk_w, T, k, w2, w2_scale, H, I, out, s);
+}
+
+template <int FMT>
+static void down_combine_shape(const float *h, const int32_t *slot_pos, const int32_t *topk_ids,
+                               const float *topk_w, int T, int k, const uint8_t *w2,
+                               const void *w2_scale, int H, int I, uint16_t *out, hipStream_t s) {
+  int lpr, nj;
+  gemv_segment_shape(I / 32, &lpr, &nj);
+  if (nj == 2)
+    down_combine_passes<FMT, 64, 2>(h, slot_pos, topk_ids, topk_w, T, k, w2, w2_scale, H, I, out, s);
+  else if (lpr == 64)
+    down_combine_passes<FMT, 64, 1>(h, slot_pos, topk_ids, topk_w, T, k, w2, w2_scale, H, I, out, s);
+  else if (lpr == 32)
+    down_combine_passes<FMT, 32, 1>(h, slot_pos, topk_ids, topk_w, T, k, w2, w2_scale, H, I, out, s);
+  else
+    down_combine_passes<FMT, 16, 1>(h, slot_pos, topk_ids, topk_w, T, k, w2, w2_scale, H, I, out, s);
 }
 
 hipError_t launch_gemv_down_combine(int fmt, const float *h, const int32_t *slot_pos,
                                     const int32_t *topk_ids, const float *topk_w, int T, int k,
                                     const uint8_t *w2, const void *w2_scale, int H, int I,
                                     uint16_t *out, hipStream_t s) {
-  constexpr int RB = 8;
-  const int Q = k * (I / 32);
-  const int QW = (Q + 3) / 4;
-  const dim3 grid((unsigned)cdiv(H, RB), (unsigned)T);
-  if (QW > 128) return hipErrorInvalidValue;
-  if (QW > 64) {
-    if (fmt == 0)
-      hipLaunchKernelGGL((k_down_combine<0, 2, RB>), grid, dim3(256), 0, s, h, slot_pos, topk_ids,
-                         topk_w, T, k, w2, w2_scale, H, I, out);
-    else
-      hipLaunchKernelGGL((k_down_combine<1, 2, RB>), grid, dim3(256), 0, s, h, slot_pos, topk_ids,
-                         topk_w, T, k, w2, w2_scale, H, I, out);
-  } else {
-    if (fmt == 0)
-      hipLaunchKernelGGL((k_down_combine<0, 1, RB>), grid, dim3(256), 0, s, h, slot_pos, topk_ids,
-                         topk_w, T, k, w2, w2_scale, H, I, out);
-    else
-      hipLaunchKernelGGL((k_down_combine<1, 1, RB>), grid, dim3(256), 0, s, h, slot_pos, topk_ids,
-                         topk_w, T, k, w2, w2_scale, H, I, out);
-  }
+  if (!down_combine_supported(I, k)) return hipErrorInvalidValue;
+  if (fmt == 0)
+    down_combine_shape<0>(h, slot_pos, topk_ids, topk_w, T, k, w2, w2_scale, H, I, out, s);
+  else
+    down_combine_shape<1>(h, slot_pos, topk_ids, topk_w, T, k, w2, w2_scale, H, I, out, s);
   return hipGetLastError();
 }
 

@@ -37,10 +37,13 @@ hipError_t launch_dequantize(int fmt, const uint8_t *packed, const void *scale, 
 
 // Router logits. With split_ws (>= router_split_bytes(E, H) bytes, 256-byte
 // aligned) and T >= kMfmaLogitsT, H % 32 == 0: the matrix-core kernel.
+// rows_only: the one-workgroup-per-expert kernel for every T, so each token's
+// logits have the same bits whatever T (the small-M path's contract).
 constexpr int kMfmaLogitsT = 33;
 size_t router_split_bytes(int E, int H);
 hipError_t launch_router_logits(const uint16_t *x, int T, int H, const float *W, const float *b,
-                                int E, float *logits, void *split_ws, hipStream_t s);
+                                int E, float *logits, void *split_ws, hipStream_t s,
+                                bool rows_only = false);
 // top-k + softmax, then grouping. Fills every RouteBufs field.
 hipError_t launch_route(const float *logits, int T, int E, int k, int renorm, const RouteBufs &rb,
                         int bm, hipStream_t s);
@@ -96,7 +99,10 @@ struct GemmArgs {
 hipError_t launch_gemv_grouped(const GemmArgs &g, int ms_hint, hipStream_t s);
 hipError_t launch_mfma_grouped(const GemmArgs &g, hipStream_t s);
 
-// Token-centric down projection + combine for a handful of tokens.
+// Token-centric down projection + combine for a handful of tokens; the same
+// bits as the grouped GEMV's slot output followed by launch_combine. Shapes:
+// down_combine_supported(I, k).
+bool down_combine_supported(int I, int k);
 hipError_t launch_gemv_down_combine(int fmt, const float *h, const int32_t *slot_pos,
                                     const int32_t *topk_ids, const float *topk_w, int T, int k,
                                     const uint8_t *w2, const void *w2_scale, int H, int I,

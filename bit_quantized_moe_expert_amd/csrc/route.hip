@@ -17,7 +17,9 @@
 namespace nf4moe {
 
 // ---------------------------------------------------------------------------
-// Router logits, few tokens: one workgroup per expert, threads stride over H.
+// Router logits, few tokens: one workgroup per (expert, chunk of TMAX tokens),
+// threads stride over H. A token's logit is summed in the same order whatever
+// TMAX, the chunk it falls in and the other tokens of the call.
 // ---------------------------------------------------------------------------
 template <int TMAX>
 __global__ __launch_bounds__(256) void k_logits_rows(const uint16_t *__restrict__ x, int T, int H,
@@ -25,6 +27,10 @@ __global__ __launch_bounds__(256) void k_logits_rows(const uint16_t *__restrict_
                                                      const float *__restrict__ b, int E,
                                                      float *__restrict__ L) {
   const int e = blockIdx.x;
+  const int64_t t0 = (int64_t)blockIdx.y * TMAX;
+  x += t0 * H;
+  L += t0 * E;
+  T = (int)((int64_t)T - t0 < TMAX ? (int64_t)T - t0 : TMAX);
   const float *w = W + (int64_t)e * H;
   float acc[TMAX];
 #pragma unroll
@@ -220,9 +226,15 @@ __global__ __launch_bounds__(256) void k_logits_tiled(const uint16_t *__restrict
 }
 
 hipError_t launch_router_logits(const uint16_t *x, int T, int H, const float *W, const float *b,
-                                int E, float *logits, void *split_ws, hipStream_t s) {
+                                int E, float *logits, void *split_ws, hipStream_t s, bool rows_only) {
   if (T <= 0) return hipSuccess;
-  if (split_ws && T >= kMfmaLogitsT && H % 32 == 0) {
+  if (rows_only) {  // the per-token order of k_logits_rows for every T
+    if (T <= 8)
+      hipLaunchKernelGGL(k_logits_rows<8>, dim3(E), dim3(256), 0, s, x, T, H, W, b, E, logits);
+    else
+      hipLaunchKernelGGL(k_logits_rows<32>, dim3(E, (unsigned)cdiv(T, 32)), dim3(256), 0, s, x, T, H, W,
+                         b, E, logits);
+  } else if (split_ws && T >= kMfmaLogitsT && H % 32 == 0) {
     uint16_t *planes = reinterpret_cast<uint16_t *>(split_ws);
     const int64_t n = (int64_t)E * H;
     hipLaunchKernelGGL(k_split3, dim3((unsigned)cdiv(n, 256)), dim3(256), 0, s, W, n, planes);
@@ -290,17 +302,20 @@ __global__ __launch_bounds__(256) void k_topk(const float *__restrict__ L, int T
     }
   }
   const float v0 = __shfl(my_v, 0, kWave);  // the largest logit
-  float wgt;
+  // Denominator summed in one fixed order (selected experts by rank, or all
+  // experts by id), the order every routing kernel here uses.
+  float den = 0.0f;
   if (renorm) {
     const float ex = lane < k ? expf(my_v - v0) : 0.0f;
-    wgt = ex / wave_sum(ex);
+    for (int q = 0; q < k; ++q) den += __shfl(ex, q, kWave);
   } else {
-    float part = 0.0f;
 #pragma unroll
-    for (int j = 0; j < EPL; ++j)
-      if (lane + 64 * j < E) part += expf(v[j] - v0);
-    wgt = expf(my_v - v0) / wave_sum(part);
+    for (int j = 0; j < EPL; ++j) {
+      const float ex = lane + 64 * j < E ? expf(v[j] - v0) : 0.0f;
+      for (int l = 0; l < 64 && 64 * j + l < E; ++l) den += __shfl(ex, l, kWave);
+    }
   }
+  const float wgt = expf(my_v - v0) / den;
   if (lane < k) {
     ids[(int64_t)t * k + lane] = my_id;
     wts[(int64_t)t * k + lane] = wgt;
