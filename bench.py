@@ -35,6 +35,9 @@ def parse():
     ap.add_argument("--graph", type=int, default=1, help="1: time HIP-graph replays as well")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--gptoss-form", action="store_true",
+                    help="the gpt-oss expert form: clamped GLU (alpha 1.702, limit 7), per-expert "
+                         "biases, interleaved gate / up rows")
     ap.add_argument("--op", default="forward", choices=["forward", "dgrad"],
                     help="forward: the routed MoE layer (default). dgrad: the input gradients "
                          "of the layer's two grouped GEMMs (gate_up and down) on the forward's "
@@ -139,11 +142,16 @@ def main():
         w2 = S.make_stack_torch(wl, l, "w2", dev)
         p2, s2 = M.quantize(w2, wl.fmt)
         del w2
+        form = {}
+        if args.gptoss_form:
+            b13, b2 = S.make_biases(wl, l)
+            form = dict(glu=M.GLU_CLAMPED, glu_alpha=GPTOSS_ALPHA, glu_limit=GPTOSS_LIMIT, glu_interleaved=1,
+                        b13=torch.from_numpy(b13).to(dev), b2=torch.from_numpy(b2).to(dev))
         layers.append(M.MoELayer(
             fmt=wl.fmt, E=wl.E, H=wl.H, I=wl.I, top_k=wl.top_k, w13=p13, w13_scale=s13, w2=p2,
             w2_scale=s2, router_w=torch.from_numpy(W_r).to(dev),
             router_b=None if b_r is None else torch.from_numpy(b_r).to(dev),
-            renormalize=wl.renormalize, path=path))
+            renormalize=wl.renormalize, path=path, **form))
         xb = S.make_x(wl, T, l)
         xs.append(torch.from_numpy(xb.view(np.int16)).to(dev).view(torch.bfloat16))
     torch.cuda.synchronize()
@@ -260,7 +268,7 @@ def main():
     # ---- CPU baseline: the fp64 oracle on a bounded sample of the same workload
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(wl, T, layers, xs, dev, args.cpu_seconds)
+        cpu = cpu_baseline(wl, T, layers, xs, dev, args.cpu_seconds, args.gptoss_form)
 
     line = {
         "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": steps,
@@ -269,7 +277,8 @@ def main():
         "data": "synthetic (seeded N(0,1) activations, N(0,0.02) weights quantized on device)",
         "config": {"workload": wl.name, "format": "nf4_b64" if wl.fmt == 0 else "mxfp4_b32",
                    "E": wl.E, "top_k": wl.top_k, "H": wl.H, "I": wl.I, "T": T, "layers": nlayers,
-                   "path": "small_m" if small else "mfma", "timing": "hip_graph" if graph_ms else "eager"},
+                   "path": "small_m" if small else "mfma", "timing": "hip_graph" if graph_ms else "eager",
+                   "epilogue": "clamped_glu+biases" if args.gptoss_form else "swiglu"},
         "eager_ms_per_step": eager_ms, "graph_ms_per_step": graph_ms,
         "effective_packed_GBps": step_bytes / (ms * 1e-3) / 1e9,
         "algorithmic_TFLOPs": flops / (ms * 1e-3) / 1e12,
@@ -385,7 +394,11 @@ def bench_dgrad(args):
     print(json.dumps(line), flush=True)
 
 
-def cpu_baseline(wl, T, layers, xs, dev, seconds):
+# gpt-oss's published clamped-GLU constants
+GPTOSS_ALPHA, GPTOSS_LIMIT = 1.702, 7.0
+
+
+def cpu_baseline(wl, T, layers, xs, dev, seconds, gptoss_form=False):
     """Time oracle.moe_forward (fp64, numpy) on host cores for a bounded sample:
     whole layer calls of this workload, one token batch each, until `seconds`."""
     import numpy as np
@@ -426,6 +439,10 @@ def cpu_baseline(wl, T, layers, xs, dev, seconds):
             layer = dict(fmt=wl.fmt, E=E, H=wl.H, I=wl.I, top_k=wl.top_k, renormalize=wl.renormalize,
                          w13=Pick(q13, 0), w13_scale=Pick(q13, 1), w2=Pick(q2, 0), w2_scale=Pick(q2, 1),
                          router_w=W_r, router_b=b_r)
+            if gptoss_form:
+                b13, b2 = S.make_biases(wl, l)
+                layer.update(glu=O.GLU_CLAMPED, glu_alpha=GPTOSS_ALPHA, glu_limit=GPTOSS_LIMIT,
+                             glu_interleaved=1, b13=b13, b2=b2)
             t = time.perf_counter()
             O.moe_forward(layer, xb)
             total += time.perf_counter() - t

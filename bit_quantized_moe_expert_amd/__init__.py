@@ -16,6 +16,7 @@ FMT_NF4 = 0
 FMT_MXFP4 = 1
 PATH_AUTO, PATH_SMALL_M, PATH_MFMA = 0, 1, 2
 DT_F32, DT_BF16 = 0, 1
+GLU_SWIGLU, GLU_CLAMPED = 0, 1
 BLOCK = {FMT_NF4: 64, FMT_MXFP4: 32}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -39,6 +40,8 @@ class Layer(ctypes.Structure):
         ("w13", ctypes.c_void_p), ("w13_scale", ctypes.c_void_p),
         ("w2", ctypes.c_void_p), ("w2_scale", ctypes.c_void_p),
         ("router_w", ctypes.c_void_p), ("router_b", ctypes.c_void_p),
+        ("glu", ctypes.c_int32), ("glu_alpha", ctypes.c_float), ("glu_limit", ctypes.c_float),
+        ("glu_interleaved", ctypes.c_int32), ("b13", ctypes.c_void_p), ("b2", ctypes.c_void_p),
     ]
 
 
@@ -270,8 +273,10 @@ def grouped_dgrad(dc, B, B_scale, group_offsets, K: int, group_experts=None, fmt
 class MoELayer:
     """One routed MoE layer held on the device in 4-bit form.
 
-    w13 [E, 2I, H/2] u8 (rows [0, I) gate, [I, 2I) up), w13_scale, w2 [E, H, I/2] u8,
-    w2_scale, router_w fp32 [E, H], router_b fp32 [E] or None."""
+    w13 [E, 2I, H/2] u8 (rows [0, I) gate, [I, 2I) up; with glu_interleaved rows 2c
+    gate, 2c + 1 up), w13_scale, w2 [E, H, I/2] u8, w2_scale, router_w fp32 [E, H],
+    router_b fp32 [E] or None. glu: GLU_SWIGLU or GLU_CLAMPED (glu_alpha, glu_limit);
+    b13 fp32 [E, 2I] and b2 fp32 [E, H] per-expert biases or None."""
     fmt: int
     E: int
     H: int
@@ -285,6 +290,12 @@ class MoELayer:
     router_b: object = None
     renormalize: int = 1
     path: int = PATH_AUTO
+    glu: int = 0
+    glu_alpha: float = 0.0
+    glu_limit: float = 0.0
+    glu_interleaved: int = 0
+    b13: object = None
+    b2: object = None
 
     def struct(self) -> Layer:
         torch = _torch()
@@ -296,10 +307,15 @@ class MoELayer:
         _dev(self.router_w, "router_w", torch.float32)
         if self.router_b is not None:
             _dev(self.router_b, "router_b", torch.float32)
+        for name in ("b13", "b2"):
+            if getattr(self, name) is not None:
+                _dev(getattr(self, name), name, torch.float32)
+        ptr = lambda t: None if t is None else t.data_ptr()
         return Layer(self.fmt, self.E, self.H, self.I, self.top_k, self.renormalize, self.path,
                      self.w13.data_ptr(), self.w13_scale.data_ptr(), self.w2.data_ptr(),
-                     self.w2_scale.data_ptr(), self.router_w.data_ptr(),
-                     None if self.router_b is None else self.router_b.data_ptr())
+                     self.w2_scale.data_ptr(), self.router_w.data_ptr(), ptr(self.router_b),
+                     self.glu, self.glu_alpha, self.glu_limit, self.glu_interleaved,
+                     ptr(self.b13), ptr(self.b2))
 
     def workspace_bytes(self, T: int) -> int:
         return int(lib().nf4moe_workspace_bytes(ctypes.byref(self.struct()), T))

@@ -126,6 +126,15 @@ nf4moe_status_t check_layer(const nf4moe_layer_t *L) {
     return fail(NF4MOE_ERR_INVALID_ARG, "NF4 absmax must be 4-byte aligned");
   if (L->router_b && !aligned(L->router_b, 4))
     return fail(NF4MOE_ERR_INVALID_ARG, "router_b must be 4-byte aligned");
+  if (L->glu != NF4MOE_GLU_SWIGLU && L->glu != NF4MOE_GLU_CLAMPED)
+    return fail(NF4MOE_ERR_INVALID_ARG, "unknown glu %d", L->glu);
+  if (L->glu == NF4MOE_GLU_CLAMPED &&
+      !(L->glu_alpha > 0.0f && L->glu_alpha < 1e30f && L->glu_limit > 0.0f && L->glu_limit < 1e30f))
+    return fail(NF4MOE_ERR_INVALID_ARG, "clamped GLU needs finite alpha > 0 and limit > 0");
+  if (L->glu_interleaved != 0 && L->glu_interleaved != 1)
+    return fail(NF4MOE_ERR_INVALID_ARG, "glu_interleaved must be 0 or 1");
+  if ((L->b13 && !aligned(L->b13, 4)) || (L->b2 && !aligned(L->b2, 4)))
+    return fail(NF4MOE_ERR_INVALID_ARG, "b13/b2 must be 4-byte aligned");
   return NF4MOE_OK;
 }
 
@@ -456,6 +465,11 @@ static nf4moe_status_t forward_impl(const nf4moe_layer_t *layer, const uint16_t 
   g.n_tiles = fc.rb.counters + 1;
   g.max_tiles = rp.max_tiles;
   g.epi = EPI_SWIGLU;
+  g.glu = L.glu;
+  g.glu_alpha = L.glu_alpha;
+  g.glu_limit = L.glu_limit;
+  g.glu_inter = L.glu_interleaved;
+  g.bias = L.b13;
   g.c = fc.h;
   if (use == NF4MOE_PATH_MFMA) g.c_split = 1;  // h as (bf16 hi, lo) pairs for the down MFMAs
   if (fused_route) {
@@ -477,7 +491,7 @@ static nf4moe_status_t forward_impl(const nf4moe_layer_t *layer, const uint16_t 
   // down projection + router-weighted combine
   if (small && T <= kTokenCentricT && down_combine_supported(L.I, L.top_k)) {
     e = launch_gemv_down_combine((int)L.fmt, fc.h, fc.rb.slot_pos, fc.rb.topk_ids, fc.rb.topk_w, T,
-                                 L.top_k, L.w2, L.w2_scale, L.H, L.I, out, s);
+                                 L.top_k, L.w2, L.w2_scale, L.b2, L.H, L.I, out, s);
     if (e != hipSuccess) return hip_status(e, "down launch");
   } else {
     GemmArgs d = g;
@@ -493,6 +507,8 @@ static nf4moe_status_t forward_impl(const nf4moe_layer_t *layer, const uint16_t 
     d.N = L.H;
     d.K = L.I;
     d.epi = EPI_SLOT;
+    d.glu_inter = 0;
+    d.bias = L.b2;
     d.c = fc.slotbuf;
     d.slot_of = fc.rb.sorted_slots;
     d.slot_w = fc.rb.topk_w;

@@ -157,6 +157,18 @@ __device__ inline float2 pair_gather(float cb_lane, uint32_t b) {
                   : make_float2(codebook_gather(cb_lane, b & 15), codebook_gather(cb_lane, b >> 4));
 }
 
+// Gate_up epilogue: glu 0 is SwiGLU, silu(g) * u; glu 1 the clamped GLU,
+// (u' + 1) * g' / (1 + exp(-alpha g')) with g' = min(g, limit) and
+// u' = clamp(u, -limit, limit).
+__device__ inline float glu_value(int glu, float alpha, float limit, float g, float u) {
+  if (glu == 1) {
+    g = fminf(g, limit);
+    u = fminf(fmaxf(u, -limit), limit);
+    return (u + 1.0f) * (g / (1.0f + expf(-alpha * g)));
+  }
+  return g / (1.0f + expf(-g)) * u;
+}
+
 // Barrier that orders LDS only: global loads (and stores) issued before it
 // stay in flight, unlike __syncthreads(), whose workgroup fence also covers
 // global memory and so waits for every outstanding vector memory operation.

@@ -252,7 +252,9 @@ __device__ inline void route_publish(const GemmArgs &p, const RouteToken<EPL> &r
 // after it orders LDS only. One token (ROUTE > 0): the logits load, table build
 // and partial ranks come first, and the weight stream starts right after the
 // barrier, once every wave knows its expert.
-template <int FMT, int EPI, int AF32, int LPR, int NJ, int MS, int ROUTE>
+// XF: the extended gate_up / down epilogue (clamped GLU, interleaved gate and
+// up rows, per-expert biases); XF = 0 instantiates the plain SwiGLU kernel.
+template <int FMT, int EPI, int AF32, int LPR, int NJ, int MS, int ROUTE, int XF>
 __global__ __launch_bounds__(gemv_waves<ROUTE>() * 64) void k_gemv(GemmArgs p) {
   constexpr int NWV = gemv_waves<ROUTE>();
   constexpr int RPL = 64 / LPR;
@@ -371,7 +373,7 @@ __global__ __launch_bounds__(gemv_waves<ROUTE>() * 64) void k_gemv(GemmArgs p) {
     int64_t col, wrow;
     if (EPI == EPI_SWIGLU) {
       col = u0 + (q >> 1);
-      wrow = (q & 1) ? col + ncol : col;
+      wrow = (XF && p.glu_inter) ? 2 * col + (q & 1) : ((q & 1) ? col + ncol : col);
     } else {
       col = u0 + q;
       wrow = col;
@@ -473,7 +475,18 @@ __global__ __launch_bounds__(gemv_waves<ROUTE>() * 64) void k_gemv(GemmArgs p) {
       if (mm < rows && col < ncol) {
         const int64_t r = row0 + mm;
         if (EPI == EPI_SWIGLU) {
-          const float hval = v0 / (1.0f + expf(-v0)) * v1;
+          float hval;
+          if constexpr (XF) {
+            float gv = v0, uv = v1;
+            if (p.bias) {
+              const float *bb = p.bias + (int64_t)e * p.N;
+              gv += bb[p.glu_inter ? 2 * col : col];
+              uv += bb[p.glu_inter ? 2 * col + 1 : col + ncol];
+            }
+            hval = glu_value(p.glu, p.glu_alpha, p.glu_limit, gv, uv);
+          } else {
+            hval = v0 / (1.0f + expf(-v0)) * v1;
+          }
           reinterpret_cast<float *>(p.c)[r * ncol + col] = hval;
         } else if (EPI == EPI_PLAIN_F32) {
           reinterpret_cast<float *>(p.c)[r * ncol + col] = v0;
@@ -481,14 +494,15 @@ __global__ __launch_bounds__(gemv_waves<ROUTE>() * 64) void k_gemv(GemmArgs p) {
           reinterpret_cast<uint16_t *>(p.c)[r * ncol + col] = (uint16_t)f32_to_bf16_rne(v0);
         } else {
           const int64_t slot = p.slot_of[r];
-          reinterpret_cast<float *>(p.c)[slot * ncol + col] = p.slot_w[slot] * v0;
+          const float y = (XF && p.bias) ? v0 + p.bias[(int64_t)e * p.N + col] : v0;
+          reinterpret_cast<float *>(p.c)[slot * ncol + col] = p.slot_w[slot] * y;
         }
       }
     }
   }
 }
 
-template <int FMT, int EPI, int AF32, int LPR, int NJ, int MS, int ROUTE = 0>
+template <int FMT, int EPI, int AF32, int LPR, int NJ, int MS, int ROUTE = 0, int XF = 0>
 static void launch_gemv_t(const GemmArgs &g, hipStream_t s) {
   constexpr int RPL = 64 / LPR;
   constexpr int NL = gemv_loads<LPR, NJ, MS>();
@@ -497,71 +511,80 @@ static void launch_gemv_t(const GemmArgs &g, hipStream_t s) {
   const int64_t ncol = (EPI == EPI_SWIGLU) ? g.N / 2 : g.N;
   constexpr int NWV = gemv_waves<ROUTE>();
   const dim3 grid((unsigned)cdiv(ncol, NWV * UPW), (unsigned)(ROUTE > 0 ? g.route_k : g.max_grp));
-  NF4MOE_LAUNCH(g, (k_gemv<FMT, EPI, AF32, LPR, NJ, MS, ROUTE>), grid, dim3(NWV * 64), s, g);
+  NF4MOE_LAUNCH(g, (k_gemv<FMT, EPI, AF32, LPR, NJ, MS, ROUTE, XF>), grid, dim3(NWV * 64), s, g);
 }
 
-template <int FMT, int EPI, int AF32, int LPR, int NJ>
+template <int FMT, int EPI, int AF32, int LPR, int NJ, int XF>
 static hipError_t pick_ms(const GemmArgs &g, int ms, hipStream_t s) {
   if constexpr (NJ == 2) {
-    launch_gemv_t<FMT, EPI, AF32, LPR, NJ, 1>(g, s);  // two chunks per lane: one row at a time
+    launch_gemv_t<FMT, EPI, AF32, LPR, NJ, 1, 0, XF>(g, s);  // two chunks per lane: one row at a time
   } else {
     if (ms <= 1)
-      launch_gemv_t<FMT, EPI, AF32, LPR, NJ, 1>(g, s);
+      launch_gemv_t<FMT, EPI, AF32, LPR, NJ, 1, 0, XF>(g, s);
     else if (ms == 2)
-      launch_gemv_t<FMT, EPI, AF32, LPR, NJ, 2>(g, s);
+      launch_gemv_t<FMT, EPI, AF32, LPR, NJ, 2, 0, XF>(g, s);
     else
-      launch_gemv_t<FMT, EPI, AF32, LPR, NJ, 4>(g, s);
+      launch_gemv_t<FMT, EPI, AF32, LPR, NJ, 4, 0, XF>(g, s);
   }
   return hipGetLastError();
 }
 
-template <int FMT, int EPI, int AF32>
+template <int FMT, int EPI, int AF32, int XF = 0>
 static hipError_t pick_shape(const GemmArgs &g, int ms, hipStream_t s) {
   const int64_t nch = g.K / 32;
   if (nch > 64) {
     if (nch > 128) return hipErrorInvalidValue;
-    return pick_ms<FMT, EPI, AF32, 64, 2>(g, ms, s);
+    return pick_ms<FMT, EPI, AF32, 64, 2, XF>(g, ms, s);
   }
-  if (nch > 32) return pick_ms<FMT, EPI, AF32, 64, 1>(g, ms, s);
-  if (nch > 16) return pick_ms<FMT, EPI, AF32, 32, 1>(g, ms, s);
-  return pick_ms<FMT, EPI, AF32, 16, 1>(g, ms, s);
+  if (nch > 32) return pick_ms<FMT, EPI, AF32, 64, 1, XF>(g, ms, s);
+  if (nch > 16) return pick_ms<FMT, EPI, AF32, 32, 1, XF>(g, ms, s);
+  return pick_ms<FMT, EPI, AF32, 16, 1, XF>(g, ms, s);
 }
+
+// The extended epilogue is instantiated where the forward uses it: SwiGLU on
+// bf16 activations (gate_up) and the slot output on fp32 ones (down).
+inline bool extended_epilogue(const GemmArgs &g) { return g.glu != 0 || g.glu_inter != 0 || g.bias != nullptr; }
 
 template <int FMT>
 static hipError_t pick_epi(const GemmArgs &g, int ms, hipStream_t s) {
+  const bool xf = extended_epilogue(g);
   switch (g.epi) {
     case EPI_SWIGLU:
+      if (xf) return g.a_is_f32 ? hipErrorInvalidValue : pick_shape<FMT, EPI_SWIGLU, 0, 1>(g, ms, s);
       return g.a_is_f32 ? pick_shape<FMT, EPI_SWIGLU, 1>(g, ms, s)
                         : pick_shape<FMT, EPI_SWIGLU, 0>(g, ms, s);
     case EPI_PLAIN_F32:
+      if (xf) return hipErrorInvalidValue;
       return g.a_is_f32 ? pick_shape<FMT, EPI_PLAIN_F32, 1>(g, ms, s)
                         : pick_shape<FMT, EPI_PLAIN_F32, 0>(g, ms, s);
     case EPI_PLAIN_BF16:
+      if (xf) return hipErrorInvalidValue;
       return g.a_is_f32 ? pick_shape<FMT, EPI_PLAIN_BF16, 1>(g, ms, s)
                         : pick_shape<FMT, EPI_PLAIN_BF16, 0>(g, ms, s);
     default:
+      if (xf) return g.a_is_f32 ? pick_shape<FMT, EPI_SLOT, 1, 1>(g, ms, s) : hipErrorInvalidValue;
       return g.a_is_f32 ? pick_shape<FMT, EPI_SLOT, 1>(g, ms, s)
                         : pick_shape<FMT, EPI_SLOT, 0>(g, ms, s);
   }
 }
 
-template <int FMT>
+template <int FMT, int XF>
 static hipError_t launch_routed(const GemmArgs &g, hipStream_t s) {
   const int64_t nch = g.K / 32;
   const bool two = g.route_E > 64;
   if (nch > 128) return hipErrorInvalidValue;
   if (nch > 64) {
-    if (two) launch_gemv_t<FMT, EPI_SWIGLU, 0, 64, 2, 1, 2>(g, s);
-    else launch_gemv_t<FMT, EPI_SWIGLU, 0, 64, 2, 1, 1>(g, s);
+    if (two) launch_gemv_t<FMT, EPI_SWIGLU, 0, 64, 2, 1, 2, XF>(g, s);
+    else launch_gemv_t<FMT, EPI_SWIGLU, 0, 64, 2, 1, 1, XF>(g, s);
   } else if (nch > 32) {
-    if (two) launch_gemv_t<FMT, EPI_SWIGLU, 0, 64, 1, 1, 2>(g, s);
-    else launch_gemv_t<FMT, EPI_SWIGLU, 0, 64, 1, 1, 1>(g, s);
+    if (two) launch_gemv_t<FMT, EPI_SWIGLU, 0, 64, 1, 1, 2, XF>(g, s);
+    else launch_gemv_t<FMT, EPI_SWIGLU, 0, 64, 1, 1, 1, XF>(g, s);
   } else if (nch > 16) {
-    if (two) launch_gemv_t<FMT, EPI_SWIGLU, 0, 32, 1, 1, 2>(g, s);
-    else launch_gemv_t<FMT, EPI_SWIGLU, 0, 32, 1, 1, 1>(g, s);
+    if (two) launch_gemv_t<FMT, EPI_SWIGLU, 0, 32, 1, 1, 2, XF>(g, s);
+    else launch_gemv_t<FMT, EPI_SWIGLU, 0, 32, 1, 1, 1, XF>(g, s);
   } else {
-    if (two) launch_gemv_t<FMT, EPI_SWIGLU, 0, 16, 1, 1, 2>(g, s);
-    else launch_gemv_t<FMT, EPI_SWIGLU, 0, 16, 1, 1, 1>(g, s);
+    if (two) launch_gemv_t<FMT, EPI_SWIGLU, 0, 16, 1, 1, 2, XF>(g, s);
+    else launch_gemv_t<FMT, EPI_SWIGLU, 0, 16, 1, 1, 1, XF>(g, s);
   }
   return hipGetLastError();
 }
@@ -570,7 +593,9 @@ hipError_t launch_gemv_grouped(const GemmArgs &g, int ms_hint, hipStream_t s) {
   if (g.route_logits) {
     if (g.epi != EPI_SWIGLU || g.a_is_f32 || g.route_E > 128 || g.route_k > kMaxTopK)
       return hipErrorInvalidValue;
-    return g.fmt == 0 ? launch_routed<0>(g, s) : launch_routed<1>(g, s);
+    if (extended_epilogue(g))
+      return g.fmt == 0 ? launch_routed<0, 1>(g, s) : launch_routed<1, 1>(g, s);
+    return g.fmt == 0 ? launch_routed<0, 0>(g, s) : launch_routed<1, 0>(g, s);
   }
   if (g.max_grp <= 0) return hipSuccess;
   return g.fmt == 0 ? pick_epi<0>(g, ms_hint, s) : pick_epi<1>(g, ms_hint, s);
@@ -587,14 +612,15 @@ hipError_t launch_gemv_grouped(const GemmArgs &g, int ms_hint, hipStream_t s) {
 // of s_0, s_1, ... from 0. A workgroup owns RB output rows of one token; its 4
 // waves hold 4 * 64 / LPR lane segments, one slot each per pass (NP passes).
 // ---------------------------------------------------------------------------
-template <int FMT, int LPR, int NJ, int NP, int RB>
+template <int FMT, int LPR, int NJ, int NP, int RB, int XF>
 __global__ __launch_bounds__(256) void k_down_combine(const float *__restrict__ h,
                                                       const int32_t *__restrict__ slot_pos,
                                                       const int32_t *__restrict__ topk_ids,
                                                       const float *__restrict__ topk_w, int T,
                                                       int k, const uint8_t *__restrict__ w2,
                                                       const void *__restrict__ w2s, int H, int I,
-                                                      uint16_t *__restrict__ out) {
+                                                      uint16_t *__restrict__ out,
+                                                      const float *__restrict__ b2) {
   constexpr int SPW = 64 / LPR;      // lane segments per wave
   constexpr int NSEG = 4 * SPW;      // slots per pass
   __shared__ float2 tab_all[256 * kGemvRep];
@@ -684,6 +710,7 @@ __global__ __launch_bounds__(256) void k_down_combine(const float *__restrict__ 
         acc = fmaf((cok[jj] && n0 + n < H) ? sc[n][q][jj] : 0.0f, dot, acc);
       }
       acc = seg_sum<LPR>(acc);
+      if constexpr (XF) acc += b2[(int64_t)eraw[q] * H + (n0 + n < H ? n0 + n : H - 1)];
       if (li == 0 && live[q]) red[q * NSEG + seg][n] = wj[q] * acc;
     }
   }
@@ -699,11 +726,16 @@ __global__ __launch_bounds__(256) void k_down_combine(const float *__restrict__ 
 template <int FMT, int LPR, int NJ, int NP>
 static void launch_down_combine_t(const float *h, const int32_t *slot_pos, const int32_t *topk_ids,
                                   const float *topk_w, int T, int k, const uint8_t *w2,
-                                  const void *w2_scale, int H, int I, uint16_t *out, hipStream_t s) {
+                                  const void *w2_scale, const float *b2, int H, int I, uint16_t *out,
+                                  hipStream_t s) {
   constexpr int RB = 8;
   const dim3 grid((unsigned)cdiv(H, RB), (unsigned)T);
-  hipLaunchKernelGGL((k_down_combine<FMT, LPR, NJ, NP, RB>), grid, dim3(256), 0, s, h, slot_pos, topk_ids,
-                     topk_w, T, k, w2, w2_scale, H, I, out);
+  if (b2)
+    hipLaunchKernelGGL((k_down_combine<FMT, LPR, NJ, NP, RB, 1>), grid, dim3(256), 0, s, h, slot_pos, topk_ids,
+                       topk_w, T, k, w2, w2_scale, H, I, out, b2);
+  else
+    hipLaunchKernelGGL((k_down_combine<FMT, LPR, NJ, NP, RB, 0>), grid, dim3(256), 0, s, h, slot_pos, topk_ids,
+                       topk_w, T, k, w2, w2_scale, H, I, out, b2);
 }
 
 // Lane-segment shape of the grouped GEMV for K = I (pick_shape's rule): LPR
@@ -725,39 +757,41 @@ bool down_combine_supported(int I, int k) {
 template <int FMT, int LPR, int NJ>
 static void down_combine_passes(const float *h, const int32_t *slot_pos, const int32_t *topk_ids,
                                 const float *topk_w, int T, int k, const uint8_t *w2,
-                                const void *w2_scale, int H, int I, uint16_t *out, hipStream_t s) {
+                                const void *w2_scale, const float *b2, int H, int I, uint16_t *out,
+                                hipStream_t s) {
   constexpr int NSEG = 4 * (64 / LPR);
   if (NJ == 1 && k > NSEG)
-    launch_down_combine_t<FMT, LPR, 1, 2>(h, slot_pos, topk_ids, topk_w, T, k, w2, w2_scale, H, I, out, s);
+    launch_down_combine_t<FMT, LPR, 1, 2>(h, slot_pos, topk_ids, topk_w, T, k, w2, w2_scale, b2, H, I, out, s);
   else
-    launch_down_combine_t<FMT, LPR, NJ, 1>(h, slot_pos, topk_ids, topk_w, T, k, w2, w2_scale, H, I, out, s);
+    launch_down_combine_t<FMT, LPR, NJ, 1>(h, slot_pos, topk_ids, topk_w, T, k, w2, w2_scale, b2, H, I, out, s);
 }
 
 template <int FMT>
 static void down_combine_shape(const float *h, const int32_t *slot_pos, const int32_t *topk_ids,
                                const float *topk_w, int T, int k, const uint8_t *w2,
-                               const void *w2_scale, int H, int I, uint16_t *out, hipStream_t s) {
+                               const void *w2_scale, const float *b2, int H, int I, uint16_t *out,
+                               hipStream_t s) {
   int lpr, nj;
   gemv_segment_shape(I / 32, &lpr, &nj);
   if (nj == 2)
-    down_combine_passes<FMT, 64, 2>(h, slot_pos, topk_ids, topk_w, T, k, w2, w2_scale, H, I, out, s);
+    down_combine_passes<FMT, 64, 2>(h, slot_pos, topk_ids, topk_w, T, k, w2, w2_scale, b2, H, I, out, s);
   else if (lpr == 64)
-    down_combine_passes<FMT, 64, 1>(h, slot_pos, topk_ids, topk_w, T, k, w2, w2_scale, H, I, out, s);
+    down_combine_passes<FMT, 64, 1>(h, slot_pos, topk_ids, topk_w, T, k, w2, w2_scale, b2, H, I, out, s);
   else if (lpr == 32)
-    down_combine_passes<FMT, 32, 1>(h, slot_pos, topk_ids, topk_w, T, k, w2, w2_scale, H, I, out, s);
+    down_combine_passes<FMT, 32, 1>(h, slot_pos, topk_ids, topk_w, T, k, w2, w2_scale, b2, H, I, out, s);
   else
-    down_combine_passes<FMT, 16, 1>(h, slot_pos, topk_ids, topk_w, T, k, w2, w2_scale, H, I, out, s);
+    down_combine_passes<FMT, 16, 1>(h, slot_pos, topk_ids, topk_w, T, k, w2, w2_scale, b2, H, I, out, s);
 }
 
 hipError_t launch_gemv_down_combine(int fmt, const float *h, const int32_t *slot_pos,
                                     const int32_t *topk_ids, const float *topk_w, int T, int k,
-                                    const uint8_t *w2, const void *w2_scale, int H, int I,
-                                    uint16_t *out, hipStream_t s) {
+                                    const uint8_t *w2, const void *w2_scale, const float *b2, int H,
+                                    int I, uint16_t *out, hipStream_t s) {
   if (!down_combine_supported(I, k)) return hipErrorInvalidValue;
   if (fmt == 0)
-    down_combine_shape<0>(h, slot_pos, topk_ids, topk_w, T, k, w2, w2_scale, H, I, out, s);
+    down_combine_shape<0>(h, slot_pos, topk_ids, topk_w, T, k, w2, w2_scale, b2, H, I, out, s);
   else
-    down_combine_shape<1>(h, slot_pos, topk_ids, topk_w, T, k, w2, w2_scale, H, I, out, s);
+    down_combine_shape<1>(h, slot_pos, topk_ids, topk_w, T, k, w2, w2_scale, b2, H, I, out, s);
   return hipGetLastError();
 }
 

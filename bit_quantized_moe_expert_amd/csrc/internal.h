@@ -85,6 +85,14 @@ struct GemmArgs {
   // Optional timing: when set, the kernel is launched with these two HIP
   // events, which take the kernel's own start and end timestamps.
   void *ev_start, *ev_stop;
+  // EPI_SWIGLU: glu 0 = silu(g) * u, 1 = clamped GLU (glu_alpha, glu_limit);
+  // glu_inter: gate / up weight rows 2c, 2c + 1 instead of c, c + N/2.
+  int glu;
+  float glu_alpha, glu_limit;
+  int glu_inter;
+  // Per-expert bias [E, N] added to the product (by weight row) before the
+  // epilogue: SwiGLU before the activation, slot before the routing weight.
+  const float *bias;
 };
 
 // Launch through hipExtLaunchKernelGGL when the arguments carry events.
@@ -105,8 +113,8 @@ hipError_t launch_mfma_grouped(const GemmArgs &g, hipStream_t s);
 bool down_combine_supported(int I, int k);
 hipError_t launch_gemv_down_combine(int fmt, const float *h, const int32_t *slot_pos,
                                     const int32_t *topk_ids, const float *topk_w, int T, int k,
-                                    const uint8_t *w2, const void *w2_scale, int H, int I,
-                                    uint16_t *out, hipStream_t s);
+                                    const uint8_t *w2, const void *w2_scale, const float *b2, int H,
+                                    int I, uint16_t *out, hipStream_t s);
 // out[t] = bf16(sum_j slotbuf[t*k + j]) in j order.
 hipError_t launch_combine(const float *slotbuf, int T, int k, int H, uint16_t *out, hipStream_t s);
 

@@ -112,7 +112,7 @@ __global__ __launch_bounds__(512) void k_mfma(GemmArgs p, int ntn, int per) {
   int64_t col, nrow;
   if (EPI == EPI_SWIGLU) {
     col = (int64_t)nt * 128 + 32 * (wave & 3) + l32;
-    nrow = col + (wave >> 2) * ncol;
+    nrow = p.glu_inter ? 2 * col + (wave >> 2) : col + (wave >> 2) * ncol;
   } else {
     col = (int64_t)nt * 256 + 32 * wave + l32;
     nrow = col;
@@ -322,6 +322,12 @@ __global__ __launch_bounds__(512) void k_mfma(GemmArgs p, int ntn, int per) {
     }
     lds_barrier();
     if (wave >= 4) return;
+    float bg = 0.0f, bu = 0.0f;  // this column's gate and up biases
+    if (p.bias && nvalid) {
+      const float *bb = p.bias + (int64_t)e * N;
+      bg = bb[nrow];
+      bu = bb[p.glu_inter ? nrow + 1 : nrow + ncol];
+    }
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) {
 #pragma unroll
@@ -329,8 +335,12 @@ __global__ __launch_bounds__(512) void k_mfma(GemmArgs p, int ntn, int per) {
         const int m = mb * 32 + 8 * (v >> 2) + 4 * g + (v & 3);
         const float up = xch[((w4 * 4 + mb) * 16 + v) * 64 + lane];
         if (m >= trows || !nvalid) continue;
-        const float gt = C[mb][v];
-        const float h = gt / (1.0f + expf(-gt)) * up;
+        float gt = C[mb][v], ut = up;
+        if (p.bias) {
+          gt += bg;
+          ut += bu;
+        }
+        const float h = glu_value(p.glu, p.glu_alpha, p.glu_limit, gt, ut);
         const int64_t o = (int64_t)(trow0 + m) * ncol + col;
         if (p.c_split) {  // (truncated bf16 hi, RNE bf16 of the rest) in one word
           const uint32_t hi = __float_as_uint(h) & 0xffff0000u;
@@ -343,6 +353,7 @@ __global__ __launch_bounds__(512) void k_mfma(GemmArgs p, int ntn, int per) {
     return;
   }
   if (!nvalid) return;
+  const float yb = (EPI == EPI_SLOT && p.bias) ? p.bias[(int64_t)e * N + col] : 0.0f;
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb) {
 #pragma unroll
@@ -357,7 +368,7 @@ __global__ __launch_bounds__(512) void k_mfma(GemmArgs p, int ntn, int per) {
         reinterpret_cast<uint16_t *>(p.c)[r * N + col] = (uint16_t)f32_to_bf16_rne(y);
       } else {
         const int64_t slot = p.slot_of[r];
-        reinterpret_cast<float *>(p.c)[slot * N + col] = p.slot_w[slot] * y;
+        reinterpret_cast<float *>(p.c)[slot * N + col] = p.slot_w[slot] * (p.bias ? y + yb : y);
       }
     }
   }

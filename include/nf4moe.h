@@ -64,10 +64,23 @@ typedef enum { NF4MOE_DT_F32 = 0, NF4MOE_DT_BF16 = 1 } nf4moe_dtype_t;
  * A/B measurement and tests); the result must satisfy the same tolerance. */
 typedef enum { NF4MOE_PATH_AUTO = 0, NF4MOE_PATH_SMALL_M = 1, NF4MOE_PATH_MFMA = 2 } nf4moe_path_t;
 
+/* The gate_up epilogue. SWIGLU: h = silu(g) * u, silu(g) = g / (1 + exp(-g)).
+ * CLAMPED: the gpt-oss expert form the experts4bit-qlora page names without
+ * defining it ("Scope": MXFP4 experts with per-expert biases and a clamped-GLU
+ * epilogue); read here as g' = min(g, limit), u' = clamp(u, -limit, limit),
+ * h = (u' + 1) * g' / (1 + exp(-alpha * g')), alpha and limit given by the
+ * caller (gpt-oss publishes alpha = 1.702, limit = 7). */
+typedef enum { NF4MOE_GLU_SWIGLU = 0, NF4MOE_GLU_CLAMPED = 1 } nf4moe_glu_t;
+
 /* One MoE layer. All pointers are device memory owned by the caller.
- * The fused gate_up stack is [E, 2I, H] (rows [0, I) gate, [I, 2I) up) and the
- * down stack [E, H, I] -- the experts4bit-qlora README's fused expert-stack
- * convention ("Quickstart") -- each stored in `fmt`. */
+ * The fused gate_up stack is [E, 2I, H] (rows [0, I) gate, [I, 2I) up, or with
+ * glu_interleaved rows 2c gate and 2c + 1 up) and the down stack [E, H, I] --
+ * the experts4bit-qlora README's fused expert-stack convention ("Quickstart")
+ * -- each stored in `fmt`. Optional per-expert biases (the gpt-oss form):
+ * b13 [E, 2I] fp32 added to the gate_up product row by row (same row order as
+ * w13) before the epilogue, b2 [E, H] fp32 added to each expert's down output
+ * before its routing weight. A zero-filled struct tail (glu 0, biases NULL)
+ * is the plain SwiGLU layer. */
 typedef struct {
   nf4moe_format_t fmt;
   int32_t E;           /* experts, 1..1024                                   */
@@ -82,6 +95,12 @@ typedef struct {
   const void *w2_scale;  /* NF4: float [E, H, I/64];  MXFP4: uint8 [E, H, I/32]  */
   const float *router_w; /* [E, H] fp32                                        */
   const float *router_b; /* [E] fp32 added to the logits, or NULL              */
+  int32_t glu;           /* nf4moe_glu_t                                        */
+  float glu_alpha;       /* CLAMPED only: > 0, finite                           */
+  float glu_limit;       /* CLAMPED only: > 0, finite                           */
+  int32_t glu_interleaved; /* 0: gate rows [0, I), up [I, 2I); 1: gate 2c, up 2c + 1 */
+  const float *b13;      /* [E, 2I] fp32 or NULL                                */
+  const float *b2;       /* [E, H] fp32 or NULL                                 */
 } nf4moe_layer_t;
 
 /* ---------------------------------------------------------------------------

@@ -9,6 +9,7 @@ for the pages' real-text workloads (no dataset or checkpoint is used):
   b_r    per-expert prior log p_e (Zipf s=1.2 over a seeded rank order) or none
   w13    ~ N(0, 0.02) fp32, [E, 2I, H]   (rows [0, I) gate, [I, 2I) up)
   w2     ~ N(0, 0.02) fp32, [E, H, I]
+  b13, b2 (the gpt-oss expert form only) ~ N(0, 0.1) fp32, [E, 2I] and [E, H]
 Layer l of workload c uses seed 1000*c + l; each tensor draws from its own
 stream, and each expert of a weight stack from its own sub-stream so any
 single expert can be regenerated alone.
@@ -22,7 +23,7 @@ import numpy as np
 FMT_NF4 = 0
 FMT_MXFP4 = 1
 
-_STREAM = {"x": 1, "router_w": 2, "router_b": 3, "w13": 4, "w2": 5}
+_STREAM = {"x": 1, "router_w": 2, "router_b": 3, "w13": 4, "w2": 5, "b13": 6, "b2": 7}
 
 
 @dataclass(frozen=True)
@@ -96,6 +97,13 @@ def make_stack(wl: Workload, layer: int, which: str, experts=None) -> np.ndarray
     """fp32 weight stack [E, N, K] (or only the listed experts, in order)."""
     ids = range(wl.E) if experts is None else experts
     return np.stack([make_expert(wl, layer, which, int(e)) for e in ids])
+
+
+def make_biases(wl: Workload, layer: int = 0):
+    """Per-expert biases of the gpt-oss expert form: (b13 fp32 [E, 2I], b2 fp32 [E, H])."""
+    b13 = _rng(wl, layer, "b13").standard_normal((wl.E, 2 * wl.I), dtype=np.float32) * np.float32(0.1)
+    b2 = _rng(wl, layer, "b2").standard_normal((wl.E, wl.H), dtype=np.float32) * np.float32(0.1)
+    return b13.astype(np.float32), b2.astype(np.float32)
 
 
 def make_stack_torch(wl: Workload, layer: int, which: str, device):

@@ -38,6 +38,13 @@ Readings of points the pages leave open (each listed in the design doc):
     (renormalize=0).
   * Grouping: stable counting sort of slots s = t*k + j by expert.
   * gate_up rows [0, I) are gate, [I, 2I) are up; SwiGLU = silu(gate) * up.
+  * The gpt-oss expert form, which the experts4bit-qlora page names ("Scope":
+    per-expert biases and a clamped-GLU epilogue) without defining: optional
+    biases b13 [E, 2I] (added to the gate_up product, row order of w13) and
+    b2 [E, H] (added to each expert's down output before its routing weight);
+    optional interleaved gate/up rows (2c gate, 2c + 1 up); clamped GLU
+    g' = min(g, limit), u' = clamp(u, -limit, limit),
+    h = (u' + 1) * g' * sigmoid(alpha * g'), alpha and limit parameters.
   * Combine: out[t] = sum_j w[t, j] * y[t*k + j] in fp64, not rounded.
 """
 from __future__ import annotations
@@ -51,11 +58,14 @@ __all__ = [
     "nf4_quantize", "nf4_dequantize", "mxfp4_quantize", "mxfp4_dequantize",
     "quantize", "dequantize", "block_size",
     "bf16_bits_to_f64", "router_logits", "topk_route", "topk_gap", "permute",
-    "grouped_gemm", "grouped_dgrad", "swiglu", "moe_forward", "rel_err",
+    "grouped_gemm", "grouped_dgrad", "swiglu", "clamped_glu", "GLU_SWIGLU", "GLU_CLAMPED",
+    "moe_forward", "rel_err",
 ]
 
 FMT_NF4 = 0
 FMT_MXFP4 = 1
+GLU_SWIGLU = 0
+GLU_CLAMPED = 1
 NF4_BLOCK = 64
 MXFP4_BLOCK = 32
 
@@ -362,11 +372,23 @@ def swiglu(g: np.ndarray, u: np.ndarray) -> np.ndarray:
     return g / (1.0 + np.exp(-g)) * u
 
 
+def clamped_glu(g: np.ndarray, u: np.ndarray, alpha: float, limit: float) -> np.ndarray:
+    """The clamped GLU epilogue of the gpt-oss expert form (a reading: the
+    experts4bit-qlora page, "Scope", names it without defining it):
+    g' = min(g, limit), u' = clamp(u, -limit, limit),
+    h = (u' + 1) * g' * sigmoid(alpha * g')."""
+    g = np.minimum(g, limit)
+    u = np.clip(u, -limit, limit)
+    return (u + 1.0) * (g / (1.0 + np.exp(-alpha * g)))
+
+
 def moe_forward(layer: dict, x_bits: np.ndarray, topk_ids_override=None, return_all=False):
     """One routed MoE layer on 4-bit weights, fp64, unrounded output [T, H].
 
     layer: fmt, E, H, I, top_k, renormalize, w13 [E, 2I, H/2] u8, w13_scale,
-    w2 [E, H, I/2] u8, w2_scale, router_w [E, H] f32, router_b [E] or None.
+    w2 [E, H, I/2] u8, w2_scale, router_w [E, H] f32, router_b [E] or None;
+    optional: glu (GLU_SWIGLU / GLU_CLAMPED), glu_alpha, glu_limit,
+    glu_interleaved, b13 [E, 2I] f32, b2 [E, H] f32 (the gpt-oss expert form).
     Steps (page "How do I run a grouped GEMM ...", "Why it happens" dataflow,
     and grouped-nf4-gemm PKG-INFO "The NVMe tier": gate -> GLU -> down):
     router logits, top-k + softmax, grouping, gate_up, SwiGLU, down, weighted
@@ -393,9 +415,21 @@ def moe_forward(layer: dict, x_bits: np.ndarray, topk_ids_override=None, return_
                 w[t] = full[ids[t]] / full.sum()
     off, slots = permute(ids, E)
     tok = slots // k
+    expert_of_row = np.repeat(np.arange(E), np.diff(off))    # expert of each sorted row
     gu = grouped_gemm(x, tok, fmt, layer["w13"], layer["w13_scale"], 2 * I, H, off)
-    h = swiglu(gu[:, :I], gu[:, I:])
+    if layer.get("b13") is not None:
+        gu = gu + np.asarray(layer["b13"], np.float64)[expert_of_row]
+    if layer.get("glu_interleaved", 0):
+        g, u = gu[:, 0::2], gu[:, 1::2]
+    else:
+        g, u = gu[:, :I], gu[:, I:]
+    if layer.get("glu", GLU_SWIGLU) == GLU_CLAMPED:
+        h = clamped_glu(g, u, float(layer["glu_alpha"]), float(layer["glu_limit"]))
+    else:
+        h = swiglu(g, u)
     y = grouped_gemm(h, None, fmt, layer["w2"], layer["w2_scale"], H, I, off)
+    if layer.get("b2") is not None:
+        y = y + np.asarray(layer["b2"], np.float64)[expert_of_row]
     y_slot = np.empty_like(y)
     y_slot[slots] = y                                  # back to slot order s = t*k + j
     out = np.zeros((T, H))

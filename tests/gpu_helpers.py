@@ -68,8 +68,11 @@ class _Proj:
         return self.st._get(int(e))[self.i]
 
 
-def build_layers(wl: S.Workload, layer=0, device="cuda", on_device_rng=False, path=0):
-    """Returns (device MoELayer, oracle layer dict, fp32 sources)."""
+def build_layers(wl: S.Workload, layer=0, device="cuda", on_device_rng=False, path=0, gptoss=None):
+    """Returns (device MoELayer, oracle layer dict, fp32 sources).
+
+    gptoss: None, or dict(alpha, limit, interleaved) for the gpt-oss expert form
+    (clamped GLU, per-expert biases; interleaved gate / up rows)."""
     import torch
     import bit_quantized_moe_expert_amd as M
     W_r, b_r = S.make_router(wl, layer)
@@ -82,6 +85,25 @@ def build_layers(wl: S.Workload, layer=0, device="cuda", on_device_rng=False, pa
         w2 = S.make_stack(wl, layer, "w2")
         w13_d = torch.from_numpy(w13).to(device)
         w2_d = torch.from_numpy(w2).to(device)
+    extra, o_extra = {}, {}
+    if gptoss is not None:
+        b13, b2 = S.make_biases(wl, layer)
+        if gptoss.get("interleaved"):
+            perm = np.empty(2 * wl.I, np.int64)
+            perm[0::2] = np.arange(wl.I)
+            perm[1::2] = wl.I + np.arange(wl.I)
+            b13 = np.ascontiguousarray(b13[:, perm])
+            if on_device_rng:
+                w13 = w13[:, torch.from_numpy(perm).to(device)].contiguous()
+                w13_d = w13
+            else:
+                w13 = np.ascontiguousarray(w13[:, perm])
+                w13_d = torch.from_numpy(w13).to(device)
+        extra = dict(glu=M.GLU_CLAMPED, glu_alpha=float(gptoss["alpha"]), glu_limit=float(gptoss["limit"]),
+                     glu_interleaved=int(bool(gptoss.get("interleaved"))),
+                     b13=torch.from_numpy(b13).to(device), b2=torch.from_numpy(b2).to(device))
+        o_extra = dict(glu=O.GLU_CLAMPED, glu_alpha=float(gptoss["alpha"]), glu_limit=float(gptoss["limit"]),
+                       glu_interleaved=int(bool(gptoss.get("interleaved"))), b13=b13, b2=b2)
     p13, s13 = M.quantize(w13_d, wl.fmt)
     p2, s2 = M.quantize(w2_d, wl.fmt)
     dev_layer = M.MoELayer(
@@ -89,11 +111,11 @@ def build_layers(wl: S.Workload, layer=0, device="cuda", on_device_rng=False, pa
         w13=p13, w13_scale=s13, w2=p2, w2_scale=s2,
         router_w=torch.from_numpy(W_r).to(device),
         router_b=None if b_r is None else torch.from_numpy(b_r).to(device),
-        renormalize=wl.renormalize, path=path)
+        renormalize=wl.renormalize, path=path, **extra)
     st13, st2 = LazyStack(wl.fmt, w13), LazyStack(wl.fmt, w2)
     o_layer = dict(fmt=wl.fmt, E=wl.E, H=wl.H, I=wl.I, top_k=wl.top_k, renormalize=wl.renormalize,
                    w13=st13.packed(), w13_scale=st13.scale(), w2=st2.packed(), w2_scale=st2.scale(),
-                   router_w=W_r, router_b=b_r)
+                   router_w=W_r, router_b=b_r, **o_extra)
     return dev_layer, o_layer, (w13, w2)
 
 

@@ -54,8 +54,8 @@ def _same(a, b, what):
         assert bad.size == 0, f"{what}: {name} differs first at {bad[0].tolist()} ({bad.shape[0]} elements)"
 
 
-def _check_invariance(wl, path, Ts, singles, n_all, on_device_rng=False):
-    layer, o_layer, _ = build_layers(wl, 0, DEV, on_device_rng=on_device_rng, path=path)
+def _check_invariance(wl, path, Ts, singles, n_all, on_device_rng=False, gptoss=None):
+    layer, o_layer, _ = build_layers(wl, 0, DEV, on_device_rng=on_device_rng, path=path, gptoss=gptoss)
     X = S.make_x(wl, n_all)
     full = _run(layer, X)
     rows = [0, n_all - 1]
@@ -84,6 +84,14 @@ def test_auto_decode_sizes_row_count_invariance(wl):
     """AUTO picks the small-M path while T * top_k <= 64: every such T agrees."""
     tmax = 64 // wl.top_k
     _check_invariance(wl, M.PATH_AUTO, list(range(1, tmax)), [1, tmax - 1], tmax)
+
+
+def test_gptoss_form_row_count_invariance():
+    """Clamped GLU with per-expert biases (the down bias enters the token-centric
+    kernel and the GEMV slot output the same way)."""
+    wl = S.custom(E=16, top_k=4, H=256, I=2880, fmt=O.FMT_MXFP4, wid=36)
+    _check_invariance(wl, M.PATH_SMALL_M, [1, 2, 3, 16], [1, 15], 17,
+                      gptoss=dict(alpha=1.702, limit=1.0, interleaved=True))
 
 
 def test_olmoe_shape_row_count_invariance():

@@ -203,8 +203,8 @@ def test_grouped_dgrad_rejects_unsupported_n():
 
 
 # --------------------------------------------------------------------- full forward
-def _forward_case(wl, T, path=0, on_device_rng=False, sample=None):
-    dev_layer, o_layer, _ = build_layers(wl, 0, DEV, on_device_rng=on_device_rng, path=path)
+def _forward_case(wl, T, path=0, on_device_rng=False, sample=None, gptoss=None):
+    dev_layer, o_layer, _ = build_layers(wl, 0, DEV, on_device_rng=on_device_rng, path=path, gptoss=gptoss)
     xb = S.make_x(wl, T)
     x = bits_to_torch_bf16(xb)
     out, ids, _w = M.moe_forward(dev_layer, x, return_routing=True)
@@ -233,6 +233,35 @@ SMALL = [
 @pytest.mark.parametrize("path", [M.PATH_AUTO, M.PATH_SMALL_M, M.PATH_MFMA])
 def test_forward_small_shapes(wl, T, path):
     _forward_case(wl, T, path)
+
+
+# The gpt-oss expert form: clamped GLU (a small limit, so the clamps act),
+# per-expert biases, halves or interleaved gate / up rows.
+GPTOSS_SMALL = [
+    (S.custom(E=16, top_k=4, H=512, I=256, wid=51), dict(alpha=1.702, limit=1.0, interleaved=False)),
+    (S.custom(E=8, top_k=2, H=320, I=288, fmt=O.FMT_MXFP4, wid=52), dict(alpha=1.702, limit=0.75, interleaved=True)),
+    (S.custom(E=12, top_k=3, H=384, I=192, wid=53), dict(alpha=1.0, limit=2.0, interleaved=True)),
+]
+
+
+@pytest.mark.parametrize("case", GPTOSS_SMALL, ids=lambda c: c[0].name)
+@pytest.mark.parametrize("T", [1, 2, 5, 40, 333])
+@pytest.mark.parametrize("path", [M.PATH_AUTO, M.PATH_SMALL_M, M.PATH_MFMA])
+def test_forward_gptoss_form(case, T, path):
+    wl, opts = case
+    _forward_case(wl, T, path, gptoss=opts)
+
+
+def test_forward_rejects_bad_glu():
+    wl = S.WORKLOADS["tiny"]
+    dev_layer, _, _ = build_layers(wl)
+    x = torch.zeros(1, wl.H, dtype=torch.bfloat16, device=DEV)
+    dev_layer.glu = 7
+    with pytest.raises(M.Nf4MoeError, match="INVALID_ARG"):
+        M.moe_forward(dev_layer, x)
+    dev_layer.glu, dev_layer.glu_alpha, dev_layer.glu_limit = M.GLU_CLAMPED, 1.702, 0.0
+    with pytest.raises(M.Nf4MoeError, match="INVALID_ARG"):
+        M.moe_forward(dev_layer, x)
 
 
 def test_forward_deterministic():
@@ -291,3 +320,12 @@ def test_full_qwen3_zipf(T, sample):
 @pytest.mark.parametrize("T,sample", [(1, None), (2048, [2047])])
 def test_full_gptoss_mxfp4(T, sample):
     _forward_case(S.WORKLOADS["gptoss_mxfp4"], T, on_device_rng=True, sample=sample)
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("T,sample", [(1, None), (2048, [0, 2047])])
+def test_full_gptoss_mxfp4_clamped_glu(T, sample):
+    """The gpt-oss-120b-shaped MXFP4 layer in its own expert form: clamped GLU
+    (alpha 1.702, limit 7), per-expert biases, interleaved gate / up rows."""
+    _forward_case(S.WORKLOADS["gptoss_mxfp4"], T, on_device_rng=True, sample=sample,
+                  gptoss=dict(alpha=1.702, limit=7.0, interleaved=True))

@@ -419,3 +419,107 @@ def test_gate_up_halves_matter():
     a = O.moe_forward(build(w13), xb)
     b = O.moe_forward(build(np.concatenate([w13[:, 64:], w13[:, :64]], axis=1)), xb)
     assert not np.allclose(a, b)
+
+
+# ----------------------------------------------------------------------------
+# The gpt-oss expert form (experts4bit-qlora page, "Scope": per-expert biases and
+# a clamped-GLU epilogue; the formula is this build's reading, a parameterised
+# clamp of the gate and up values around a GLU with sigmoid(alpha * g)).
+def test_clamped_glu_special_values():
+    a, lim = 1.702, 7.0
+    g = np.array([0.0, 0.0, 2.0, -3.0, 7.0, 50.0, 50.0, 1.0, 1.0])
+    u = np.array([5.0, -9.0, -1.0, -1.0, 0.5, 0.5, 100.0, 7.0, 1e9])
+    h = O.clamped_glu(g, u, a, lim)
+    assert h[0] == 0.0 and h[1] == 0.0          # g = 0
+    assert h[2] == 0.0 and h[3] == 0.0          # u = -1 (the +1 offset)
+    assert h[5] == h[4]                          # g clamps at the limit from above
+    assert h[6] == O.clamped_glu(np.array([7.0]), np.array([7.0]), a, lim)[0]   # both clamp
+    assert h[8] == h[7]                          # u clamps at the limit
+    # negative gates are not clamped: a large negative gate gives ~0 (sigmoid -> 0)
+    assert abs(O.clamped_glu(np.array([-60.0]), np.array([0.0]), a, lim)[0]) < 1e-40
+    # alpha = 1 and a limit no value reaches: (u + 1) * silu(g), the SwiGLU with up + 1
+    g2 = np.linspace(-5, 5, 11); u2 = np.linspace(-3, 4, 11)
+    assert np.allclose(O.clamped_glu(g2, u2, 1.0, 1e300), O.swiglu(g2, u2 + 1.0), rtol=1e-15, atol=0)
+
+
+def _gptoss_layer(fmt, E, H, I, k, interleaved, alpha=1.702, limit=1.0, zero_weights=False, seed=0):
+    wl = S.custom(E=E, top_k=k, H=H, I=I, fmt=fmt, wid=40 + seed)
+    W_r, _ = S.make_router(wl)
+    w13, w2 = S.make_stack(wl, 0, "w13"), S.make_stack(wl, 0, "w2")
+    b13, b2 = S.make_biases(wl)
+    if zero_weights:
+        w13, w2 = np.zeros_like(w13), np.zeros_like(w2)
+    if interleaved:   # the same gate and up rows, stored as 2c / 2c + 1
+        perm = np.empty(2 * I, np.int64); perm[0::2] = np.arange(I); perm[1::2] = I + np.arange(I)
+        w13, b13 = w13[:, perm], b13[:, perm]
+    q13 = [O.quantize(fmt, w13[e]) for e in range(E)]
+    q2 = [O.quantize(fmt, w2[e]) for e in range(E)]
+    return wl, dict(fmt=fmt, E=E, H=H, I=I, top_k=k, renormalize=1, router_w=W_r, router_b=None,
+                    w13=np.stack([q[0] for q in q13]), w13_scale=np.stack([q[1] for q in q13]),
+                    w2=np.stack([q[0] for q in q2]), w2_scale=np.stack([q[1] for q in q2]),
+                    glu=O.GLU_CLAMPED, glu_alpha=alpha, glu_limit=limit, glu_interleaved=int(interleaved),
+                    b13=b13, b2=b2)
+
+
+def _gptoss_forward_py(layer, xb):
+    """Pure-Python forward of the gpt-oss form: loops, math.exp, min/max."""
+    fmt, E, H, I, k = layer["fmt"], layer["E"], layer["H"], layer["I"], layer["top_k"]
+    a, lim, inter = layer["glu_alpha"], layer["glu_limit"], layer["glu_interleaved"]
+    W13 = [_deq_py(fmt, layer["w13"][e], layer["w13_scale"][e], 2 * I, H) for e in range(E)]
+    W2 = [_deq_py(fmt, layer["w2"][e], layer["w2_scale"][e], H, I) for e in range(E)]
+    out = []
+    for t in range(xb.shape[0]):
+        x = [float(np.array([int(v) << 16], np.uint32).view(np.float32)[0]) for v in xb[t]]
+        L = [math.fsum(x[h] * float(layer["router_w"][e, h]) for h in range(H)) for e in range(E)]
+        order = sorted(range(E), key=lambda e: (-L[e], e))[:k]
+        ex = [math.exp(L[e] - L[order[0]]) for e in order]
+        ws = [v / math.fsum(ex) for v in ex]
+        o = [0.0] * H
+        for wj, e in zip(ws, order):
+            gu = [math.fsum(x[h] * W13[e][n][h] for h in range(H)) + float(layer["b13"][e][n])
+                  for n in range(2 * I)]
+            hh = []
+            for i in range(I):
+                g = gu[2 * i] if inter else gu[i]
+                u = gu[2 * i + 1] if inter else gu[I + i]
+                g = min(g, lim)
+                u = max(-lim, min(u, lim))
+                hh.append((u + 1.0) * g / (1.0 + math.exp(-a * g)))
+            for n in range(H):
+                o[n] += wj * (math.fsum(hh[i] * W2[e][n][i] for i in range(I)) + float(layer["b2"][e][n]))
+        out.append(o)
+    return np.array(out)
+
+
+@pytest.mark.parametrize("fmt,interleaved", [(O.FMT_NF4, False), (O.FMT_MXFP4, True)])
+def test_gptoss_form_bruteforce(fmt, interleaved):
+    wl, layer = _gptoss_layer(fmt, 4, 64, 64, 2, interleaved, limit=0.5)
+    xb = S.make_x(wl, 3)
+    out, inner = O.moe_forward(layer, xb, return_all=True)
+    assert np.allclose(out, _gptoss_forward_py(layer, xb), rtol=1e-10, atol=1e-14)
+    assert np.mean(np.abs(inner["h"]) > 0) > 0.5     # the epilogue saw nonzero inputs
+
+
+def test_gptoss_interleaved_is_a_row_permutation():
+    """Interleaved storage of the same gate / up rows gives the same layer."""
+    wl, a = _gptoss_layer(O.FMT_NF4, 4, 64, 128, 2, False, limit=0.7, seed=1)
+    _, b = _gptoss_layer(O.FMT_NF4, 4, 64, 128, 2, True, limit=0.7, seed=1)
+    xb = S.make_x(wl, 5)
+    assert np.array_equal(O.moe_forward(a, xb), O.moe_forward(b, xb))
+
+
+def test_gptoss_zero_weights_leave_the_biases():
+    """With every weight 0: h = clamped_glu(b13 gate, b13 up) of the row's expert,
+    and out[t] = sum_j w[t, j] * b2[e_j] exactly."""
+    wl, layer = _gptoss_layer(O.FMT_NF4, 4, 64, 64, 2, False, limit=0.05, zero_weights=True, seed=2)
+    xb = S.make_x(wl, 4)
+    out, inner = O.moe_forward(layer, xb, return_all=True)
+    ids, w = inner["topk_ids"], inner["topk_w"]
+    b13, b2 = layer["b13"].astype(np.float64), layer["b2"].astype(np.float64)
+    for s, r in enumerate(np.argsort(inner["sorted_slots"])):     # slot s sits at sorted row r
+        e = ids[s // 2, s % 2]
+        assert np.array_equal(inner["h"][r], O.clamped_glu(b13[e, :64], b13[e, 64:], 1.702, 0.05))
+    ref = np.zeros((4, 64))
+    for j in range(2):
+        ref += w[:, j:j + 1] * b2[ids[:, j]]
+    assert np.allclose(out, ref, rtol=1e-15, atol=0)
