@@ -35,6 +35,8 @@ def parse():
     ap.add_argument("--graph", type=int, default=1, help="1: time HIP-graph replays as well")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--absmax-bf16", action="store_true",
+                    help="NF4 workloads: bf16-source weights stored with bf16 absmax")
     ap.add_argument("--gptoss-form", action="store_true",
                     help="the gpt-oss expert form: clamped GLU (alpha 1.702, limit 7), per-expert "
                          "biases, interleaved gate / up rows")
@@ -92,10 +94,27 @@ def measured_traffic(workload, kind):
     return float(rec["hbm_bytes_per_launch"])
 
 
+def workload(args):
+    import moe_synth as S
+    wl = S.WORKLOADS[args.workload]
+    if args.absmax_bf16:
+        if wl.fmt != 0:
+            raise SystemExit("--absmax-bf16 applies to NF4 workloads")
+        import dataclasses
+        wl = dataclasses.replace(wl, fmt=2, name=wl.name + "_bf16abs")
+    return wl
+
+
+def bf16_source(w, wl):
+    """The bf16-absmax workloads stand for a bf16 checkpoint: weights rounded to bf16."""
+    import torch
+    return w.to(torch.bfloat16).to(torch.float32) if wl.fmt == 2 else w
+
+
 def packed_bytes_per_expert(wl):
     """Algorithmic bytes of one expert: codes + scales of gate_up and down."""
-    blk = 64 if wl.fmt == 0 else 32
-    sbytes = 4 if wl.fmt == 0 else 1
+    blk = 32 if wl.fmt == 1 else 64
+    sbytes = {0: 4, 1: 1, 2: 2}[wl.fmt]
     g = 2 * wl.I * (wl.H // 2 + (wl.H // blk) * sbytes)
     d = wl.H * (wl.I // 2 + (wl.I // blk) * sbytes)
     return g, d
@@ -120,7 +139,7 @@ def main():
     import moe_synth as S
     import bit_quantized_moe_expert_amd as M
 
-    wl = S.WORKLOADS[args.workload]
+    wl = workload(args)
     T = args.tokens or wl.tokens[0]
     nlayers = args.layers or wl.layers
     path = {"auto": M.PATH_AUTO, "small": M.PATH_SMALL_M, "mfma": M.PATH_MFMA}[args.path]
@@ -136,10 +155,10 @@ def main():
     t0 = time.time()
     for l in range(nlayers):
         W_r, b_r = S.make_router(wl, l)
-        w13 = S.make_stack_torch(wl, l, "w13", dev)
+        w13 = bf16_source(S.make_stack_torch(wl, l, "w13", dev), wl)
         p13, s13 = M.quantize(w13, wl.fmt)
         del w13
-        w2 = S.make_stack_torch(wl, l, "w2", dev)
+        w2 = bf16_source(S.make_stack_torch(wl, l, "w2", dev), wl)
         p2, s2 = M.quantize(w2, wl.fmt)
         del w2
         form = {}
@@ -275,7 +294,7 @@ def main():
         "warmup": warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f32" if small else "bf16",
         "data": "synthetic (seeded N(0,1) activations, N(0,0.02) weights quantized on device)",
-        "config": {"workload": wl.name, "format": "nf4_b64" if wl.fmt == 0 else "mxfp4_b32",
+        "config": {"workload": wl.name, "format": {0: "nf4_b64", 1: "mxfp4_b32", 2: "nf4_b64_bf16abs"}[wl.fmt],
                    "E": wl.E, "top_k": wl.top_k, "H": wl.H, "I": wl.I, "T": T, "layers": nlayers,
                    "path": "small_m" if small else "mfma", "timing": "hip_graph" if graph_ms else "eager",
                    "epilogue": "clamped_glu+biases" if args.gptoss_form else "swiglu"},
@@ -313,10 +332,10 @@ def bench_dgrad(args):
     setups = []
     for l in range(nlayers):
         W_r, b_r = S.make_router(wl, l)
-        w13 = S.make_stack_torch(wl, l, "w13", dev)
+        w13 = bf16_source(S.make_stack_torch(wl, l, "w13", dev), wl)
         p13, s13 = M.quantize(w13, wl.fmt)
         del w13
-        w2 = S.make_stack_torch(wl, l, "w2", dev)
+        w2 = bf16_source(S.make_stack_torch(wl, l, "w2", dev), wl)
         p2, s2 = M.quantize(w2, wl.fmt)
         del w2
         xb = S.make_x(wl, T, l)
@@ -382,7 +401,7 @@ def bench_dgrad(args):
         "warmup": warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (forward routing of seeded N(0,1) tokens, N(0,1) bf16 output gradients)",
-        "config": {"workload": wl.name + "_dgrad", "format": "nf4_b64" if wl.fmt == 0 else "mxfp4_b32",
+        "config": {"workload": wl.name + "_dgrad", "format": {0: "nf4_b64", 1: "mxfp4_b32", 2: "nf4_b64_bf16abs"}[wl.fmt],
                    "E": wl.E, "top_k": wl.top_k, "H": wl.H, "I": wl.I, "T": T, "R": R, "layers": nlayers,
                    "timing": "eager"},
         "gate_up_dgrad_ms_mean": gu_ms, "down_dgrad_ms_mean": dn_ms,
@@ -422,8 +441,8 @@ def cpu_baseline(wl, T, layers, xs, dev, seconds, gptoss_form=False):
             L64 = O.router_logits(xb, W_r, b_r)
             ids, _ = O.topk_route(L64, wl.top_k, bool(wl.renormalize))
             need = sorted(set(ids.reshape(-1).tolist()))
-            w13 = S.make_stack_torch(wl, l, "w13", dev)
-            w2 = S.make_stack_torch(wl, l, "w2", dev)
+            w13 = bf16_source(S.make_stack_torch(wl, l, "w13", dev), wl)
+            w2 = bf16_source(S.make_stack_torch(wl, l, "w2", dev), wl)
             E = wl.E
             q13 = {e: O.quantize(wl.fmt, w13[e].cpu().numpy()) for e in need}
             q2 = {e: O.quantize(wl.fmt, w2[e].cpu().numpy()) for e in need}

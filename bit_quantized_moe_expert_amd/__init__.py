@@ -14,10 +14,11 @@ from dataclasses import dataclass
 
 FMT_NF4 = 0
 FMT_MXFP4 = 1
+FMT_NF4_BF16ABS = 2   # NF4 b64 with the absmax stored as bf16
 PATH_AUTO, PATH_SMALL_M, PATH_MFMA = 0, 1, 2
 DT_F32, DT_BF16 = 0, 1
 GLU_SWIGLU, GLU_CLAMPED = 0, 1
-BLOCK = {FMT_NF4: 64, FMT_MXFP4: 32}
+BLOCK = {FMT_NF4: 64, FMT_MXFP4: 32, FMT_NF4_BF16ABS: 64}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libnf4moe.so")
@@ -65,6 +66,7 @@ def lib() -> ctypes.CDLL:
     sig = {
         "nf4moe_quantize": [ctypes.c_int, vp, i64, i64, vp, vp, vp],
         "nf4moe_dequantize": [ctypes.c_int, vp, vp, i64, i64, vp, vp],
+        "nf4moe_absmax_to_bf16": [vp, i64, vp, vp, vp],
         "nf4moe_router_logits": [vp, i32, i32, vp, vp, i32, vp, vp, sz, vp],
         "nf4moe_router_workspace_bytes": [i32, i32],
         "nf4moe_route_workspace_bytes": [i32, i32, i32],
@@ -151,7 +153,7 @@ def _workspace(nbytes: int, device):
 
 def _scale_dtype(fmt):
     torch = _torch()
-    return torch.float32 if fmt == FMT_NF4 else torch.uint8
+    return {FMT_NF4: torch.float32, FMT_MXFP4: torch.uint8, FMT_NF4_BF16ABS: torch.int16}[fmt]
 
 
 def quantize(w, fmt: int = FMT_NF4):
@@ -175,6 +177,18 @@ def dequantize(packed, scale, K: int, fmt: int = FMT_NF4):
     out = torch.empty(*packed.shape[:-1], K, dtype=torch.float32, device=packed.device)
     _check(lib().nf4moe_dequantize(fmt, _ptr(packed), _ptr(scale), rows, K, _ptr(out), _stream()))
     return out
+
+
+def absmax_to_bf16(absmax):
+    """The bf16 absmax cast of an NF4 fp32 scale tensor (device): returns
+    (bf16 bits as int16, same shape; number of entries that were not bf16 values
+    and were rounded up). The cast is lossless only when that number is 0."""
+    torch = _torch()
+    _dev(absmax, "absmax", torch.float32)
+    out = torch.empty(absmax.shape, dtype=torch.int16, device=absmax.device)
+    bad = torch.zeros(1, dtype=torch.int32, device=absmax.device)
+    _check(lib().nf4moe_absmax_to_bf16(_ptr(absmax), absmax.numel(), _ptr(out), _ptr(bad), _stream()))
+    return out, int(bad.item())
 
 
 def router_logits(x, router_w, router_b=None, matrix_cores: bool = True):

@@ -31,8 +31,10 @@ nf4moe_status_t hip_status(hipError_t e, const char *what) {
 
 bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
-int fmt_block(nf4moe_format_t f) { return f == NF4MOE_FMT_NF4_B64 ? 64 : 32; }
-bool fmt_ok(nf4moe_format_t f) { return f == NF4MOE_FMT_NF4_B64 || f == NF4MOE_FMT_MXFP4_B32; }
+bool fmt_nf4(nf4moe_format_t f) { return f == NF4MOE_FMT_NF4_B64 || f == NF4MOE_FMT_NF4_B64_BF16ABS; }
+int fmt_block(nf4moe_format_t f) { return fmt_nf4(f) ? 64 : 32; }
+bool fmt_ok(nf4moe_format_t f) { return fmt_nf4(f) || f == NF4MOE_FMT_MXFP4_B32; }
+int scale_align(nf4moe_format_t f) { return f == NF4MOE_FMT_NF4_B64 ? 4 : f == NF4MOE_FMT_NF4_B64_BF16ABS ? 2 : 1; }
 
 constexpr int kSmallR = 64;        // routed rows up to which AUTO picks the small-M kernels
 constexpr int kTokenCentricT = 2;  // tokens up to which the down projection is token-centric
@@ -122,8 +124,8 @@ nf4moe_status_t check_layer(const nf4moe_layer_t *L) {
     return fail(NF4MOE_ERR_INVALID_ARG, "layer weight pointer is NULL");
   if (!aligned(L->w13, 16) || !aligned(L->w2, 16) || !aligned(L->router_w, 16))
     return fail(NF4MOE_ERR_INVALID_ARG, "layer weights must be 16-byte aligned");
-  if (L->fmt == NF4MOE_FMT_NF4_B64 && (!aligned(L->w13_scale, 4) || !aligned(L->w2_scale, 4)))
-    return fail(NF4MOE_ERR_INVALID_ARG, "NF4 absmax must be 4-byte aligned");
+  if (!aligned(L->w13_scale, scale_align(L->fmt)) || !aligned(L->w2_scale, scale_align(L->fmt)))
+    return fail(NF4MOE_ERR_INVALID_ARG, "scales must be aligned to their element size");
   if (L->router_b && !aligned(L->router_b, 4))
     return fail(NF4MOE_ERR_INVALID_ARG, "router_b must be 4-byte aligned");
   if (L->glu != NF4MOE_GLU_SWIGLU && L->glu != NF4MOE_GLU_CLAMPED)
@@ -168,7 +170,7 @@ const char *nf4moe_last_error(void) { return g_err; }
 nf4moe_status_t nf4moe_codebook(nf4moe_format_t fmt, float out[16]) {
   if (!fmt_ok(fmt)) return fail(NF4MOE_ERR_INVALID_ARG, "unknown format %d", (int)fmt);
   if (!out) return fail(NF4MOE_ERR_INVALID_ARG, "out is NULL");
-  for (int i = 0; i < 16; ++i) out[i] = fmt == NF4MOE_FMT_NF4_B64 ? nf4_value(i) : e2m1_value(i);
+  for (int i = 0; i < 16; ++i) out[i] = fmt_nf4(fmt) ? nf4_value(i) : e2m1_value(i);
   return NF4MOE_OK;
 }
 
@@ -180,7 +182,7 @@ static nf4moe_status_t check_quant_args(nf4moe_format_t fmt, const void *dense, 
   if (K <= 0 || K % blk) return fail(NF4MOE_ERR_INVALID_ARG, "K=%lld must be a positive multiple of %d", (long long)K, blk);
   if (rows == 0) return NF4MOE_OK;
   if (!dense || !packed || !scale) return fail(NF4MOE_ERR_INVALID_ARG, "NULL pointer");
-  if (!aligned(dense, 8) || !aligned(packed, 4) || !aligned(scale, fmt == NF4MOE_FMT_NF4_B64 ? 4 : 1))
+  if (!aligned(dense, 8) || !aligned(packed, 4) || !aligned(scale, scale_align(fmt)))
     return fail(NF4MOE_ERR_INVALID_ARG, "misaligned pointer");
   return NF4MOE_OK;
 }
@@ -191,6 +193,16 @@ nf4moe_status_t nf4moe_quantize(nf4moe_format_t fmt, const float *w, int64_t row
   if (st != NF4MOE_OK || rows == 0) return st;
   return hip_status(launch_quantize((int)fmt, w, rows, K, packed, scale, (hipStream_t)stream),
                     "quantize launch");
+}
+
+nf4moe_status_t nf4moe_absmax_to_bf16(const float *absmax, int64_t n, uint16_t *out, int32_t *n_inexact,
+                                      void *stream) {
+  if (n < 0) return fail(NF4MOE_ERR_INVALID_ARG, "n=%lld < 0", (long long)n);
+  if (n == 0) return NF4MOE_OK;
+  if (!absmax || !out || !n_inexact) return fail(NF4MOE_ERR_INVALID_ARG, "NULL pointer");
+  if (!aligned(absmax, 4) || !aligned(out, 2) || !aligned(n_inexact, 4))
+    return fail(NF4MOE_ERR_INVALID_ARG, "misaligned pointer");
+  return hip_status(launch_absmax_bf16(absmax, n, out, n_inexact, (hipStream_t)stream), "absmax cast launch");
 }
 
 nf4moe_status_t nf4moe_dequantize(nf4moe_format_t fmt, const uint8_t *packed, const void *scale,
@@ -299,7 +311,7 @@ nf4moe_status_t nf4moe_grouped_gemm(nf4moe_format_t fmt, const uint16_t *a, cons
   if (!group_offsets) return fail(NF4MOE_ERR_INVALID_ARG, "group_offsets is NULL");
   if (R > 0 && (!a || !B || !B_scale || !c)) return fail(NF4MOE_ERR_INVALID_ARG, "NULL pointer");
   if (R > 0 && (!aligned(a, 16) || !aligned(B, 16) || !aligned(c, 4) ||
-                (fmt == NF4MOE_FMT_NF4_B64 && !aligned(B_scale, 4))))
+                !aligned(B_scale, scale_align(fmt))))
     return fail(NF4MOE_ERR_INVALID_ARG, "misaligned pointer");
   const size_t need = nf4moe_gemm_workspace_bytes(G, R);
   if (!ws || ws_bytes < need)
@@ -363,7 +375,7 @@ nf4moe_status_t nf4moe_grouped_dgrad(nf4moe_format_t fmt, const uint16_t *dc, co
     return fail(NF4MOE_ERR_INVALID_ARG, "unknown output dtype %d", (int)da_dtype);
   if (!group_offsets) return fail(NF4MOE_ERR_INVALID_ARG, "group_offsets is NULL");
   if (R > 0 && (!dc || !B || !B_scale || !da)) return fail(NF4MOE_ERR_INVALID_ARG, "NULL pointer");
-  if (R > 0 && (!aligned(dc, 16) || !aligned(da, 4) || (fmt == NF4MOE_FMT_NF4_B64 && !aligned(B_scale, 4))))
+  if (R > 0 && (!aligned(dc, 16) || !aligned(da, 4) || !aligned(B_scale, scale_align(fmt))))
     return fail(NF4MOE_ERR_INVALID_ARG, "misaligned pointer");
   const size_t need = nf4moe_gemm_workspace_bytes(G, R);
   if (!ws || ws_bytes < need)

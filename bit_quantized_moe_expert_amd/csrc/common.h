@@ -33,19 +33,39 @@ __host__ __device__ constexpr float e2m1_value(int code) {
 
 // Value of the code stored at even k (first) and odd k (second) of a byte.
 // NF4 keeps the even-k code in the high nibble, MXFP4 in the low nibble.
+// Formats: 0 NF4 with fp32 absmax per 64; 1 MXFP4 (e8m0 per 32); 2 NF4 with
+// the absmax stored as bf16 (the same codes and decode, 2 bytes per block).
+// Fmt<FMT>: kNF4 (NF4 codebook, nibble order and absmax semantics), kBlock
+// (K elements per scale), raw(scale, idx) (the stored scale as 32 bits) and
+// value(raw) (the fp32 multiplier).
+template <int FMT> struct Fmt;
+template <> struct Fmt<0> {
+  static constexpr bool kNF4 = true;
+  static constexpr int kBlock = 64;
+  __device__ static uint32_t raw(const void *s, int64_t i) { return reinterpret_cast<const uint32_t *>(s)[i]; }
+  __device__ static float value(uint32_t r) { return __uint_as_float(r); }
+};
+template <> struct Fmt<1> {
+  static constexpr bool kNF4 = false;
+  static constexpr int kBlock = 32;
+  __device__ static uint32_t raw(const void *s, int64_t i) { return reinterpret_cast<const uint8_t *>(s)[i]; }
+  __device__ static float value(uint32_t r);
+};
+template <> struct Fmt<2> {
+  static constexpr bool kNF4 = true;
+  static constexpr int kBlock = 64;
+  __device__ static uint32_t raw(const void *s, int64_t i) { return reinterpret_cast<const uint16_t *>(s)[i]; }
+  __device__ static float value(uint32_t r) { return __uint_as_float(r << 16); }
+};
+
 template <int FMT>
 __host__ __device__ constexpr float even_value(uint32_t byte) {
-  return FMT == 0 ? nf4_value(byte >> 4) : e2m1_value(byte & 15);
+  return Fmt<FMT>::kNF4 ? nf4_value(byte >> 4) : e2m1_value(byte & 15);
 }
 template <int FMT>
 __host__ __device__ constexpr float odd_value(uint32_t byte) {
-  return FMT == 0 ? nf4_value(byte & 15) : e2m1_value(byte >> 4);
+  return Fmt<FMT>::kNF4 ? nf4_value(byte & 15) : e2m1_value(byte >> 4);
 }
-
-// Block size of the scale along K and bytes per scale.
-template <int FMT> struct Fmt;
-template <> struct Fmt<0> { static constexpr int kBlock = 64; };
-template <> struct Fmt<1> { static constexpr int kBlock = 32; };
 
 // Scale of one block as an fp32 multiplier. NF4: the stored fp32 absmax.
 // MXFP4: 2^(e8m0 - 127), e8m0 = 255 -> NaN.
@@ -54,10 +74,16 @@ __device__ inline float e8m0_to_f32(uint32_t e) {
   if (e == 0u) return 0x1p-127f;               // the one subnormal power of two
   return __uint_as_float(e << 23);
 }
+__device__ inline float Fmt<1>::value(uint32_t r) { return e8m0_to_f32(r); }
 
 // ---------------------------------------------------------------------------
 // bf16 helpers (bf16 tensors cross the ABI as uint16 bit patterns)
 // ---------------------------------------------------------------------------
+// The smallest bf16 value >= the non-negative finite fp32 value with bits b,
+// as bf16 bits (b itself when it is a bf16 value).
+__host__ __device__ inline uint32_t bf16_round_up_bits(uint32_t b) {
+  return ((b & 0xffffu) ? b + 0x10000u : b) >> 16;
+}
 __device__ inline float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
 __device__ inline float bf16lo_to_f32(uint32_t packed) { return __uint_as_float(packed << 16); }
 __device__ inline float bf16hi_to_f32(uint32_t packed) { return __uint_as_float(packed & 0xffff0000u); }
@@ -88,7 +114,7 @@ __device__ inline float e2m1_value_sel(uint32_t c) {
 }
 template <int FMT>
 __device__ inline float2 pair_value(uint32_t b) {
-  return FMT == 0 ? make_float2(nf4_value_sel(b >> 4), nf4_value_sel(b & 15))
+  return Fmt<FMT>::kNF4 ? make_float2(nf4_value_sel(b >> 4), nf4_value_sel(b & 15))
                   : make_float2(e2m1_value_sel(b & 15), e2m1_value_sel(b >> 4));
 }
 
@@ -145,7 +171,7 @@ __device__ inline uint64_t lanemask_lt() {
 template <int FMT>
 __device__ inline float codebook_lane() {
   const uint32_t c = threadIdx.x & 15;
-  return FMT == 0 ? nf4_value_sel(c) : e2m1_value_sel(c);
+  return Fmt<FMT>::kNF4 ? nf4_value_sel(c) : e2m1_value_sel(c);
 }
 __device__ inline float codebook_gather(float cb_lane, uint32_t code) {
   return __int_as_float(__builtin_amdgcn_ds_bpermute((int)(code << 2), __float_as_int(cb_lane)));
@@ -153,7 +179,7 @@ __device__ inline float codebook_gather(float cb_lane, uint32_t code) {
 // (value of the even-k code, value of the odd-k code) of a packed byte.
 template <int FMT>
 __device__ inline float2 pair_gather(float cb_lane, uint32_t b) {
-  return FMT == 0 ? make_float2(codebook_gather(cb_lane, b >> 4), codebook_gather(cb_lane, b & 15))
+  return Fmt<FMT>::kNF4 ? make_float2(codebook_gather(cb_lane, b >> 4), codebook_gather(cb_lane, b & 15))
                   : make_float2(codebook_gather(cb_lane, b & 15), codebook_gather(cb_lane, b >> 4));
 }
 

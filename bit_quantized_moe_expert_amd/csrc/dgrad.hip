@@ -95,10 +95,7 @@ __global__ __launch_bounds__(512) void k_dgrad(DgradArgs p, int ktn, int per) {
     for (int i = 0; i < 8; ++i) {
       const int64_t n = n0 + 8 * ng + i;
       braw[i] = Be[n * rowbytes + kbyte];
-      if (FMT == 0)
-        sraw[i] = reinterpret_cast<const uint32_t *>(p.B_scale)[sc_base + n * sc_per_row + sidx];
-      else
-        sraw[i] = reinterpret_cast<const uint8_t *>(p.B_scale)[sc_base + n * sc_per_row + sidx];
+      sraw[i] = Fmt<FMT>::raw(p.B_scale, sc_base + n * sc_per_row + sidx);
     }
   };
   const uint32_t lanerep = (uint32_t)(lane & (kDRep - 1));
@@ -110,7 +107,7 @@ __global__ __launch_bounds__(512) void k_dgrad(DgradArgs p, int ktn, int per) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const float2 v = tab[braw[i] * kDRep + lanerep];
-      const float s = kok ? (FMT == 0 ? __uint_as_float(sraw[i]) : e8m0_to_f32(sraw[i])) : 0.0f;
+      const float s = kok ? Fmt<FMT>::value(sraw[i]) : 0.0f;
       const float we = v.x * s, wo = v.y * s;
       const uint32_t hbe = __float_as_uint(we) & 0xffff0000u, hbo = __float_as_uint(wo) & 0xffff0000u;
       const uint32_t lbe = f32_to_bf16_rne(we - __uint_as_float(hbe));
@@ -207,6 +204,7 @@ hipError_t launch_dgrad_t(const DgradArgs &a, hipStream_t s) {
 hipError_t launch_dgrad(const DgradArgs &a, hipStream_t s) {
   if (a.max_tiles <= 0) return hipSuccess;
   if (a.fmt == 0) return a.da_bf16 ? launch_dgrad_t<0, 1>(a, s) : launch_dgrad_t<0, 0>(a, s);
+  if (a.fmt == 2) return a.da_bf16 ? launch_dgrad_t<2, 1>(a, s) : launch_dgrad_t<2, 0>(a, s);
   return a.da_bf16 ? launch_dgrad_t<1, 1>(a, s) : launch_dgrad_t<1, 0>(a, s);
 }
 

@@ -24,8 +24,7 @@ constexpr int kGemvRep = 32;  // LDS table replicas
 
 template <int FMT>
 __device__ inline float block_scale(const void *scale, int64_t idx) {
-  if (FMT == 0) return reinterpret_cast<const float *>(scale)[idx];
-  return e8m0_to_f32(reinterpret_cast<const uint8_t *>(scale)[idx]);
+  return Fmt<FMT>::value(Fmt<FMT>::raw(scale, idx));
 }
 
 // Load 32 activations (one 16-byte weight chunk's K range) as fp32.
@@ -391,7 +390,7 @@ __global__ __launch_bounds__(gemv_waves<ROUTE>() * 64) void k_gemv(GemmArgs p) {
     for (int j = 0; j < NJ; ++j) {
       const int64_t c = li + (int64_t)LPR * j;
       const int64_t cc = c < nch ? c : 0;
-      const int64_t sidx = FMT == 0 ? (cc >> 1) : cc;
+      const int64_t sidx = Fmt<FMT>::kBlock == 64 ? (cc >> 1) : cc;
       sc[i][j] = block_scale<FMT>(p.B_scale, sc_base + wrow_of[i] * sc_per_row + sidx);
     }
   __builtin_amdgcn_sched_barrier(0);
@@ -594,11 +593,11 @@ hipError_t launch_gemv_grouped(const GemmArgs &g, int ms_hint, hipStream_t s) {
     if (g.epi != EPI_SWIGLU || g.a_is_f32 || g.route_E > 128 || g.route_k > kMaxTopK)
       return hipErrorInvalidValue;
     if (extended_epilogue(g))
-      return g.fmt == 0 ? launch_routed<0, 1>(g, s) : launch_routed<1, 1>(g, s);
-    return g.fmt == 0 ? launch_routed<0, 0>(g, s) : launch_routed<1, 0>(g, s);
+      return g.fmt == 0 ? launch_routed<0, 1>(g, s) : g.fmt == 2 ? launch_routed<2, 1>(g, s) : launch_routed<1, 1>(g, s);
+    return g.fmt == 0 ? launch_routed<0, 0>(g, s) : g.fmt == 2 ? launch_routed<2, 0>(g, s) : launch_routed<1, 0>(g, s);
   }
   if (g.max_grp <= 0) return hipSuccess;
-  return g.fmt == 0 ? pick_epi<0>(g, ms_hint, s) : pick_epi<1>(g, ms_hint, s);
+  return g.fmt == 0 ? pick_epi<0>(g, ms_hint, s) : g.fmt == 2 ? pick_epi<2>(g, ms_hint, s) : pick_epi<1>(g, ms_hint, s);
 }
 
 // ---------------------------------------------------------------------------
@@ -683,7 +682,7 @@ __global__ __launch_bounds__(256) void k_down_combine(const float *__restrict__ 
       for (int jj = 0; jj < NJ; ++jj) {
         const int64_t eb = (int64_t)eraw[q] * H;
         wq[n][q][jj] = *reinterpret_cast<const uint4 *>(w2 + (eb + rc) * rowbytes + cc[jj] * 16);
-        sc[n][q][jj] = block_scale<FMT>(w2s, (eb + rc) * sc_per_row + (FMT == 0 ? (cc[jj] >> 1) : cc[jj]));
+        sc[n][q][jj] = block_scale<FMT>(w2s, (eb + rc) * sc_per_row + (Fmt<FMT>::kBlock == 64 ? (cc[jj] >> 1) : cc[jj]));
       }
   }
   __builtin_amdgcn_sched_barrier(0);  // every load is in flight before any wait
@@ -790,6 +789,8 @@ hipError_t launch_gemv_down_combine(int fmt, const float *h, const int32_t *slot
   if (!down_combine_supported(I, k)) return hipErrorInvalidValue;
   if (fmt == 0)
     down_combine_shape<0>(h, slot_pos, topk_ids, topk_w, T, k, w2, w2_scale, b2, H, I, out, s);
+  else if (fmt == 2)
+    down_combine_shape<2>(h, slot_pos, topk_ids, topk_w, T, k, w2, w2_scale, b2, H, I, out, s);
   else
     down_combine_shape<1>(h, slot_pos, topk_ids, topk_w, T, k, w2, w2_scale, b2, H, I, out, s);
   return hipGetLastError();

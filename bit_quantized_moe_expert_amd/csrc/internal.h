@@ -34,6 +34,7 @@ hipError_t launch_quantize(int fmt, const float *w, int64_t rows, int64_t K, uin
                            void *scale, hipStream_t s);
 hipError_t launch_dequantize(int fmt, const uint8_t *packed, const void *scale, int64_t rows,
                              int64_t K, float *out, hipStream_t s);
+hipError_t launch_absmax_bf16(const float *a, int64_t n, uint16_t *out, int32_t *inexact, hipStream_t s);
 
 // Router logits. With split_ws (>= router_split_bytes(E, H) bytes, 256-byte
 // aligned) and T >= kMfmaLogitsT, H % 32 == 0: the matrix-core kernel.

@@ -59,7 +59,7 @@ __device__ inline void build_mfma_table(uint4 *tab) {
     const uint32_t b = (uint32_t)f >> 4;   // 16 words of two replicas per entry
     const float2 pv = pair_gather<FMT>(cb, b);
     uint2 v;
-    if (FMT == 0) {
+    if (Fmt<FMT>::kNF4) {
       const uint32_t he = f32_to_bf16_rne(pv.x), ho = f32_to_bf16_rne(pv.y);
       const uint32_t le = f32_to_bf16_rne(pv.x - bf16_to_f32(he));
       const uint32_t lo = f32_to_bf16_rne(pv.y - bf16_to_f32(ho));
@@ -179,14 +179,11 @@ __global__ __launch_bounds__(512) void k_mfma(GemmArgs p, int ntn, int per) {
     bok = nvalid && kk < K;
     const int64_t kc = kk < K ? kk : 0;
     bq = *reinterpret_cast<const uint4 *>(Be + nrow_c * rowbytes + kc / 2);
-    const int64_t sidx = FMT == 0 ? (k0 < K ? k0 / 64 : 0) : kc / 32;
-    if (FMT == 0)
-      braw = reinterpret_cast<const uint32_t *>(p.B_scale)[sc_base + nrow_c * sc_per_row + sidx];
-    else
-      braw = reinterpret_cast<const uint8_t *>(p.B_scale)[sc_base + nrow_c * sc_per_row + sidx];
+    const int64_t sidx = Fmt<FMT>::kNF4 ? (k0 < K ? k0 / 64 : 0) : kc / 32;
+    braw = Fmt<FMT>::raw(p.B_scale, sc_base + nrow_c * sc_per_row + sidx);
   };
   auto scale_of = [&](uint32_t raw, bool ok) -> float {
-    const float v = FMT == 0 ? __uint_as_float(raw) : e8m0_to_f32(raw);
+    const float v = Fmt<FMT>::value(raw);
     return ok ? v : 0.0f;
   };
 
@@ -241,7 +238,7 @@ __global__ __launch_bounds__(512) void k_mfma(GemmArgs p, int ntn, int per) {
         const uint2 *tu = t[s & 1];
         const bf16x8_t *ahs = ah[s & (NA - 1)];
         const bf16x8_t *als = al[s & (NA - 1)];
-        if (FMT == 0) {
+        if (Fmt<FMT>::kNF4) {
           const bf16x8_t bh = as_bf16x8(tu[0].x, tu[1].x, tu[2].x, tu[3].x);
           const bf16x8_t bl = as_bf16x8(tu[0].y, tu[1].y, tu[2].y, tu[3].y);
           // passes over the four independent accumulators, so consecutive
@@ -278,7 +275,7 @@ __global__ __launch_bounds__(512) void k_mfma(GemmArgs p, int ntn, int per) {
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (FMT == 0) {  // NF4: the block's absmax scales its partial product
+    if (Fmt<FMT>::kNF4) {  // NF4: the block's absmax scales its partial product
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
@@ -403,7 +400,7 @@ static hipError_t mfma_pick(const GemmArgs &g, hipStream_t s) {
 
 hipError_t launch_mfma_grouped(const GemmArgs &g, hipStream_t s) {
   if (g.max_tiles <= 0) return hipSuccess;
-  return g.fmt == 0 ? mfma_pick<0>(g, s) : mfma_pick<1>(g, s);
+  return g.fmt == 0 ? mfma_pick<0>(g, s) : g.fmt == 2 ? mfma_pick<2>(g, s) : mfma_pick<1>(g, s);
 }
 
 }  // namespace nf4moe

@@ -16,15 +16,21 @@
 
 namespace nf4moe {
 
-// One wave per 64-element NF4 block, one lane per element.
+// One wave per 64-element NF4 block, one lane per element. BF16ABS: the
+// absmax is stored as bf16, rounded up to the nearest bf16 value when it is
+// not one (exact, and the same codes as the fp32 form, for bf16-source
+// weights, whose block maximum is itself a bf16 value), and the codes are
+// chosen against that stored value.
+template <bool BF16ABS>
 __global__ __launch_bounds__(256) void k_quant_nf4(const float *__restrict__ w, int64_t nblocks,
                                                    uint8_t *__restrict__ packed,
-                                                   float *__restrict__ absmax) {
+                                                   void *__restrict__ absmax) {
   const int64_t blk = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (blk >= nblocks) return;  // the whole wave leaves together
   const int lane = threadIdx.x & 63;
   const float v = w[blk * 64 + lane];
-  const float a = wave_max(fabsf(v));
+  float a = wave_max(fabsf(v));
+  if (BF16ABS) a = __uint_as_float(bf16_round_up_bits(__float_as_uint(a)) << 16);
   uint32_t code = 7;
   if (a != 0.0f) {
     const double wd = (double)v, ad = (double)a;
@@ -37,7 +43,23 @@ __global__ __launch_bounds__(256) void k_quant_nf4(const float *__restrict__ w, 
   }
   const uint32_t odd = __shfl_xor(code, 1, kWave);
   if ((lane & 1) == 0) packed[blk * 32 + (lane >> 1)] = (uint8_t)((code << 4) | odd);
-  if (lane == 0) absmax[blk] = a;
+  if (lane == 0) {
+    if (BF16ABS)
+      reinterpret_cast<uint16_t *>(absmax)[blk] = (uint16_t)(__float_as_uint(a) >> 16);
+    else
+      reinterpret_cast<float *>(absmax)[blk] = a;
+  }
+}
+
+// fp32 absmax -> bf16 (rounded up when not exact); counts the inexact ones.
+__global__ __launch_bounds__(256) void k_absmax_bf16(const float *__restrict__ a, int64_t n,
+                                                     uint16_t *__restrict__ out, int32_t *__restrict__ inexact) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const bool live = i < n;
+  const uint32_t b = live ? __float_as_uint(a[i]) : 0u;
+  if (live) out[i] = (uint16_t)bf16_round_up_bits(b);
+  const uint64_t bad = __ballot(live && (b & 0xffffu) != 0u);
+  if ((threadIdx.x & 63) == 0 && bad) atomicAdd(inexact, (int32_t)__popcll(bad));
 }
 
 // One half-wave per 32-element MXFP4 block.
@@ -74,9 +96,9 @@ __global__ __launch_bounds__(256) void k_dequant(const uint8_t *__restrict__ pac
   if (i >= nbytes) return;
   const uint32_t b = packed[i];
   const int64_t k = 2 * i;                       // flat element index of the even element
-  if (FMT == 0) {
-    const float a = reinterpret_cast<const float *>(scale)[k / 64];
-    out[i] = make_float2(even_value<0>(b) * a, odd_value<0>(b) * a);
+  if (Fmt<FMT>::kNF4) {
+    const float a = Fmt<FMT>::value(Fmt<FMT>::raw(scale, k / 64));
+    out[i] = make_float2(even_value<FMT>(b) * a, odd_value<FMT>(b) * a);
   } else {
     const uint32_t e = reinterpret_cast<const uint8_t *>(scale)[k / 32];
     if (e == 255u) {
@@ -99,8 +121,12 @@ hipError_t launch_quantize(int fmt, const float *w, int64_t rows, int64_t K, uin
     const int64_t m = (n - e0) < kPiece ? (n - e0) : kPiece;
     if (fmt == 0) {
       const int64_t nb = m / 64;
-      hipLaunchKernelGGL(k_quant_nf4, dim3((unsigned)((nb + 3) / 4)), dim3(256), 0, s, w + e0, nb,
-                         packed + e0 / 2, (float *)scale + e0 / 64);
+      hipLaunchKernelGGL(k_quant_nf4<false>, dim3((unsigned)((nb + 3) / 4)), dim3(256), 0, s, w + e0, nb,
+                         packed + e0 / 2, (void *)((float *)scale + e0 / 64));
+    } else if (fmt == 2) {
+      const int64_t nb = m / 64;
+      hipLaunchKernelGGL(k_quant_nf4<true>, dim3((unsigned)((nb + 3) / 4)), dim3(256), 0, s, w + e0, nb,
+                         packed + e0 / 2, (void *)((uint16_t *)scale + e0 / 64));
     } else {
       const int64_t nb = m / 32;
       hipLaunchKernelGGL(k_quant_mxfp4, dim3((unsigned)((nb + 7) / 8)), dim3(256), 0, s, w + e0,
@@ -121,10 +147,23 @@ hipError_t launch_dequantize(int fmt, const uint8_t *packed, const void *scale, 
       hipLaunchKernelGGL(k_dequant<0>, grid, dim3(256), 0, s, packed + e0 / 2,
                          (const void *)((const float *)scale + e0 / 64), nbytes,
                          (float2 *)(out + e0));
+    else if (fmt == 2)
+      hipLaunchKernelGGL(k_dequant<2>, grid, dim3(256), 0, s, packed + e0 / 2,
+                         (const void *)((const uint16_t *)scale + e0 / 64), nbytes,
+                         (float2 *)(out + e0));
     else
       hipLaunchKernelGGL(k_dequant<1>, grid, dim3(256), 0, s, packed + e0 / 2,
                          (const void *)((const uint8_t *)scale + e0 / 32), nbytes,
                          (float2 *)(out + e0));
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_absmax_bf16(const float *a, int64_t n, uint16_t *out, int32_t *inexact, hipStream_t s) {
+  for (int64_t i0 = 0; i0 < n; i0 += kPiece) {
+    const int64_t m = (n - i0) < kPiece ? (n - i0) : kPiece;
+    hipLaunchKernelGGL(k_absmax_bf16, dim3((unsigned)((m + 255) / 256)), dim3(256), 0, s, a + i0, m, out + i0,
+                       inexact);
   }
   return hipGetLastError();
 }

@@ -55,7 +55,17 @@ typedef enum {
   NF4MOE_ERR_HIP = 4          /* a HIP runtime call failed (launch, device query) */
 } nf4moe_status_t;
 
-typedef enum { NF4MOE_FMT_NF4_B64 = 0, NF4MOE_FMT_MXFP4_B32 = 1 } nf4moe_format_t;
+/* Weight formats. NF4_B64_BF16ABS is NF4_B64 with each block's absmax stored
+ * as bf16 (2 bytes instead of 4, 5.6 % fewer bytes per weight row): the
+ * experts4bit-qlora page's bf16 absmax, lossless for bf16-source weights
+ * because a block maximum of bf16 values is a bf16 value ("The one ordering
+ * trap" paragraph before it: --absmax-dtype bf16). Codes, nibble order and the
+ * decode c[code] * absmax (one fp32 product) are those of NF4_B64. */
+typedef enum {
+  NF4MOE_FMT_NF4_B64 = 0,
+  NF4MOE_FMT_MXFP4_B32 = 1,
+  NF4MOE_FMT_NF4_B64_BF16ABS = 2
+} nf4moe_format_t;
 typedef enum { NF4MOE_DT_F32 = 0, NF4MOE_DT_BF16 = 1 } nf4moe_dtype_t;
 
 /* Which grouped-GEMM kernel family runs. AUTO picks from the routed row count
@@ -113,6 +123,10 @@ typedef struct {
  * MXFP4 (same section, block 2; OCP MX v1.0): X = floor(log2 amax) - 2 clamped
  *   to [-127, 127], e8m0 = X + 127; code = nearest e2m1 of w / 2^X, ties to the
  *   even code, saturating at 6; code bit 3 = the input's sign bit.
+ * NF4_B64_BF16ABS: the NF4 rule with the block absmax rounded up to the nearest
+ *   bf16 value before the codes are chosen (no change when it is one, as for
+ *   bf16-source weights: then codes and decoded values equal NF4_B64's); scales
+ *   uint16 bf16 bits [rows, K/64].
  * Errors: INVALID_ARG for null pointers, rows < 0, K not a multiple of the block,
  * packed not 4-byte aligned. rows == 0 is a no-op. Non-finite inputs give
  * unspecified codes.
@@ -126,6 +140,17 @@ nf4moe_status_t nf4moe_quantize(nf4moe_format_t fmt, const float *w, int64_t row
  * per-element decode is identical). Errors as for nf4moe_quantize. */
 nf4moe_status_t nf4moe_dequantize(nf4moe_format_t fmt, const uint8_t *packed, const void *scale,
                                   int64_t rows, int64_t K, float *w_out, void *stream);
+
+/* nf4moe_absmax_to_bf16 -- the bf16 absmax cast of an existing NF4_B64 scale
+ * array (experts4bit-qlora page, the --absmax-dtype bf16 paragraph: the cast is
+ * taken only where it is exact and is refused otherwise). absmax fp32 [n] ->
+ * out uint16 bf16 bits [n], each rounded up to the nearest bf16 value when it
+ * is not one; *n_inexact (device int32, zeroed by the caller) receives the
+ * number of such entries: a caller refuses the cast unless it reads 0, and the
+ * codes stay valid only then. Asynchronous on `stream`. Errors: INVALID_ARG for
+ * n < 0, NULL or misaligned pointers; n == 0 is a no-op. */
+nf4moe_status_t nf4moe_absmax_to_bf16(const float *absmax, int64_t n, uint16_t *out, int32_t *n_inexact,
+                                      void *stream);
 
 /* nf4moe_router_workspace_bytes -- workspace that lets nf4moe_router_logits use
  * the matrix cores (3 * E * H * 2 bytes: router_w split exactly into three bf16

@@ -28,6 +28,10 @@ Readings of points the pages leave open (each listed in the design doc):
     parity unpinned against real checkpoints (none here).
   * NF4 quantize: exact nearest code, ties to the lower code; an all-zero
     block stores absmax 0 and code 7 (the 0.0 entry).
+  * NF4 with bf16 absmax (the experts4bit-qlora page's --absmax-dtype bf16,
+    lossless for bf16-source weights): the block absmax is rounded up to the
+    nearest bf16 value (unchanged when it is one) and the codes are chosen
+    against that value; the decode widens it back to fp32.
   * MXFP4 quantize: OCP MX v1.0 rule, shared exponent
     X = floor(log2(amax)) - 2 clamped to [-127, 127], e2m1 nearest with ties
     to the even code, saturating at 6; the code's sign bit is the input's
@@ -53,7 +57,7 @@ import numpy as np
 from scipy.special import ndtri
 
 __all__ = [
-    "FMT_NF4", "FMT_MXFP4", "NF4_BLOCK", "MXFP4_BLOCK",
+    "FMT_NF4", "FMT_MXFP4", "FMT_NF4_BF16ABS", "NF4_BLOCK", "MXFP4_BLOCK", "bf16_round_up",
     "nf4_codebook", "e2m1_values",
     "nf4_quantize", "nf4_dequantize", "mxfp4_quantize", "mxfp4_dequantize",
     "quantize", "dequantize", "block_size",
@@ -64,6 +68,7 @@ __all__ = [
 
 FMT_NF4 = 0
 FMT_MXFP4 = 1
+FMT_NF4_BF16ABS = 2      # NF4 with the block absmax stored as bf16
 GLU_SWIGLU = 0
 GLU_CLAMPED = 1
 NF4_BLOCK = 64
@@ -106,14 +111,26 @@ def e2m1_values() -> np.ndarray:
 
 
 def block_size(fmt: int) -> int:
-    return NF4_BLOCK if fmt == FMT_NF4 else MXFP4_BLOCK
+    return MXFP4_BLOCK if fmt == FMT_MXFP4 else NF4_BLOCK
 
 
 # --------------------------------------------------------------------------
 # NF4 quantize / dequantize
 # --------------------------------------------------------------------------
-def nf4_quantize(w: np.ndarray):
-    """fp32 [N, K] -> (packed uint8 [N, K/2], absmax float32 [N, K/64]).
+def bf16_round_up(a) -> np.ndarray:
+    """The smallest bfloat16 value >= each non-negative finite value of a, as
+    fp64 (a itself when it is one): with a = m * 2^e, m in [0.5, 1), bf16 keeps
+    8 significant bits, so the grid step is 2^(e - 8)."""
+    a = np.asarray(a, dtype=np.float64)
+    _, e = np.frexp(a)
+    step = np.ldexp(1.0, e - 8)
+    return np.where(a > 0, np.ceil(a / step) * step, a)
+
+
+def nf4_quantize(w: np.ndarray, absmax_bf16: bool = False):
+    """fp32 [N, K] -> (packed uint8 [N, K/2], absmax float32 [N, K/64]), or with
+    absmax_bf16 the absmax as bf16 bits (uint16), rounded up to a bf16 value
+    before the codes are chosen.
 
     grouped-nf4-gemm PKG-INFO, "Try it on CPU right now", block 1, and the
     page "How do I run a grouped GEMM ...", section "Supported scope": per row,
@@ -132,6 +149,8 @@ def nf4_quantize(w: np.ndarray):
     for r0 in range(0, N, step):
         blocks = w[r0:r0 + step].reshape(-1, K // NF4_BLOCK, NF4_BLOCK).astype(np.float64)
         a = np.abs(blocks).max(axis=2)                        # exact (a max)
+        if absmax_bf16:
+            a = bf16_round_up(a)
         # Nearest code to w among c_i * absmax. c_i * absmax is exact in fp64
         # (24-bit by 24-bit significands), and so is each distance near a tie;
         # argmin returns the first (lower) code on an exact tie.
@@ -141,6 +160,10 @@ def nf4_quantize(w: np.ndarray):
         codes[r0:r0 + step] = c.reshape(-1, K)
         absmax[r0:r0 + step] = a
     packed = ((codes[:, 0::2] << 4) | codes[:, 1::2]).astype(np.uint8)
+    if absmax_bf16:
+        bits = absmax.astype(np.float32).view(np.uint32)
+        assert not np.any(bits & 0xFFFF), "absmax is not a bf16 value"
+        return packed, (bits >> 16).astype(np.uint16)
     return packed, absmax.astype(np.float32)
 
 
@@ -223,12 +246,17 @@ def mxfp4_dequantize(packed: np.ndarray, scales: np.ndarray, N: int, K: int) -> 
 
 
 def quantize(fmt: int, w: np.ndarray):
-    return nf4_quantize(w) if fmt == FMT_NF4 else mxfp4_quantize(w)
+    if fmt == FMT_MXFP4:
+        return mxfp4_quantize(w)
+    return nf4_quantize(w, absmax_bf16=(fmt == FMT_NF4_BF16ABS))
 
 
 def dequantize(fmt: int, packed, scale, N: int, K: int) -> np.ndarray:
     if fmt == FMT_NF4:
         return nf4_dequantize(packed, scale, N, K)
+    if fmt == FMT_NF4_BF16ABS:   # widen the bf16 absmax to fp32, then the NF4 decode
+        bits = np.asarray(scale, dtype=np.uint16).astype(np.uint32) << 16
+        return nf4_dequantize(packed, bits.view(np.float32), N, K)
     return mxfp4_dequantize(packed, scale, N, K)
 
 

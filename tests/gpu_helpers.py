@@ -68,11 +68,13 @@ class _Proj:
         return self.st._get(int(e))[self.i]
 
 
-def build_layers(wl: S.Workload, layer=0, device="cuda", on_device_rng=False, path=0, gptoss=None):
+def build_layers(wl: S.Workload, layer=0, device="cuda", on_device_rng=False, path=0, gptoss=None,
+                 bf16_source=False):
     """Returns (device MoELayer, oracle layer dict, fp32 sources).
 
     gptoss: None, or dict(alpha, limit, interleaved) for the gpt-oss expert form
-    (clamped GLU, per-expert biases; interleaved gate / up rows)."""
+    (clamped GLU, per-expert biases; interleaved gate / up rows). bf16_source:
+    round the weights to bf16 values first (a bf16 checkpoint)."""
     import torch
     import bit_quantized_moe_expert_amd as M
     W_r, b_r = S.make_router(wl, layer)
@@ -85,6 +87,16 @@ def build_layers(wl: S.Workload, layer=0, device="cuda", on_device_rng=False, pa
         w2 = S.make_stack(wl, layer, "w2")
         w13_d = torch.from_numpy(w13).to(device)
         w2_d = torch.from_numpy(w2).to(device)
+    if bf16_source:
+        if on_device_rng:
+            w13 = w13.to(torch.bfloat16).to(torch.float32)
+            w2 = w2.to(torch.bfloat16).to(torch.float32)
+            w13_d, w2_d = w13, w2
+        else:
+            w13 = O.bf16_bits_to_f64(S.f32_to_bf16_bits(w13)).astype(np.float32)
+            w2 = O.bf16_bits_to_f64(S.f32_to_bf16_bits(w2)).astype(np.float32)
+            w13_d = torch.from_numpy(w13).to(device)
+            w2_d = torch.from_numpy(w2).to(device)
     extra, o_extra = {}, {}
     if gptoss is not None:
         b13, b2 = S.make_biases(wl, layer)

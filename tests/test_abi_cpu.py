@@ -59,10 +59,15 @@ def test_quantize_validation():
     assert q(1, FAKE, 4, 48, FAKE, FAKE, STREAM) == INVALID           # K not multiple of 32
     assert q(0, FAKE, -1, 64, FAKE, FAKE, STREAM) == INVALID
     assert q(0, None, 4, 64, FAKE, FAKE, STREAM) == INVALID
-    assert q(2, FAKE, 4, 64, FAKE, FAKE, STREAM) == INVALID
+    assert q(3, FAKE, 4, 64, FAKE, FAKE, STREAM) == INVALID           # unknown format
     assert q(0, FAKE + 1, 4, 64, FAKE, FAKE, STREAM) == INVALID       # misaligned
     assert q(0, FAKE, 0, 64, FAKE, FAKE, STREAM) == OK                # empty: no-op
     assert L.nf4moe_dequantize(0, FAKE, FAKE, 2, 100, FAKE, STREAM) == INVALID
+    assert L.nf4moe_dequantize(2, FAKE, FAKE + 1, 2, 64, FAKE, STREAM) == INVALID   # bf16 absmax misaligned
+    cast = L.nf4moe_absmax_to_bf16
+    assert cast(FAKE, -1, FAKE, FAKE, STREAM) == INVALID
+    assert cast(None, 4, FAKE, FAKE, STREAM) == INVALID
+    assert cast(FAKE, 0, FAKE, FAKE, STREAM) == OK                    # empty: no-op
 
 
 def test_router_and_route_validation():

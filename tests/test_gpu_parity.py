@@ -31,7 +31,7 @@ def _planted_weights(fmt, rows, K, seed):
     w[1, :blk] = -0.0                                        # negative zeros
     w[1, blk:2 * blk] = np.float32(1e-30) * rng.standard_normal(blk).astype(np.float32)  # tiny
     w[2, :blk] = rng.standard_normal(blk).astype(np.float32) * np.float32(1e30)          # huge
-    if fmt == O.FMT_NF4:
+    if fmt != O.FMT_MXFP4:
         c = O.nf4_codebook()
         w[3, 0] = 1.0
         for i in range(15):                                  # exact midpoints where representable
@@ -48,7 +48,8 @@ def _planted_weights(fmt, rows, K, seed):
 
 @pytest.mark.parametrize("fmt,rows,K", [(O.FMT_NF4, 8, 256), (O.FMT_NF4, 37, 2048),
                                         (O.FMT_NF4, 5, 2944), (O.FMT_MXFP4, 8, 256),
-                                        (O.FMT_MXFP4, 37, 2048), (O.FMT_MXFP4, 5, 2880)])
+                                        (O.FMT_MXFP4, 37, 2048), (O.FMT_MXFP4, 5, 2880),
+                                        (O.FMT_NF4_BF16ABS, 8, 256), (O.FMT_NF4_BF16ABS, 37, 2048)])
 def test_quantize_dequantize_bitexact(fmt, rows, K):
     w = _planted_weights(fmt, rows, K, seed=rows * 7 + K)
     pk_o, sc_o = O.quantize(fmt, w)
@@ -59,6 +60,20 @@ def test_quantize_dequantize_bitexact(fmt, rows, K):
     deq = M.dequantize(pk, sc, K, fmt).cpu().numpy()
     ref = O.dequantize(fmt, pk_o, sc_o, rows, K)
     assert np.array_equal(deq.view(np.uint32), ref.view(np.uint32)), "decoded values differ"
+
+
+def test_absmax_to_bf16_cast():
+    """The bf16 absmax cast: exact (and counted 0) on bf16 values, rounded up and
+    counted otherwise."""
+    rng = np.random.default_rng(63)
+    a = np.abs(rng.standard_normal(10_000) * 0.05).astype(np.float32)
+    exact = (a.view(np.uint32) & np.uint32(0xFFFF0000)).view(np.float32)
+    bits, bad = M.absmax_to_bf16(torch.from_numpy(exact).to(DEV))
+    assert bad == 0 and np.array_equal(bits.cpu().numpy().view(np.uint16), (exact.view(np.uint32) >> 16).astype(np.uint16))
+    bits, bad = M.absmax_to_bf16(torch.from_numpy(a).to(DEV))
+    assert bad == int(np.count_nonzero(a.view(np.uint32) & 0xFFFF))
+    up = O.bf16_round_up(a).astype(np.float32).view(np.uint32) >> 16
+    assert np.array_equal(bits.cpu().numpy().view(np.uint16), up.astype(np.uint16))
 
 
 def test_quantize_large_stack_bitexact_sample():
@@ -151,7 +166,7 @@ def test_grouped_gemm_page_example(fmt, path, dtype):
     check_bound(got, ref, "page example")
 
 
-@pytest.mark.parametrize("fmt,N,K", [(O.FMT_NF4, 200, 320), (O.FMT_MXFP4, 136, 288),
+@pytest.mark.parametrize("fmt,N,K", [(O.FMT_NF4, 200, 320), (O.FMT_MXFP4, 136, 288), (O.FMT_NF4_BF16ABS, 136, 320),
                                      (O.FMT_NF4, 384, 1024), (O.FMT_MXFP4, 2880, 2880)])
 @pytest.mark.parametrize("path", [M.PATH_SMALL_M, M.PATH_MFMA])
 def test_grouped_gemm_ragged(fmt, N, K, path):
@@ -185,6 +200,7 @@ def _dgrad_case(fmt, N, K, E, sizes, experts, out_dtype, seed):
     (O.FMT_MXFP4, 320, 288, [5, 0, 129, 7]),             # MXFP4, K % 128 != 0
     (O.FMT_NF4, 2048, 1024, [257, 3, 0, 64]),            # OLMoE-shaped gate_up dgrad
     (O.FMT_MXFP4, 2880, 2880, [40, 131]),                # gpt-oss-shaped
+    (O.FMT_NF4_BF16ABS, 192, 320, [1, 130, 0, 169, 2]),  # bf16 absmax
 ])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_grouped_dgrad(fmt, N, K, sizes, dtype):
@@ -250,6 +266,30 @@ GPTOSS_SMALL = [
 def test_forward_gptoss_form(case, T, path):
     wl, opts = case
     _forward_case(wl, T, path, gptoss=opts)
+
+
+# NF4 with bf16 absmax: parity with the oracle on fp32-source weights (absmax
+# rounded up), and bit-identical outputs to the fp32-absmax layer on bf16-source
+# weights, where the two forms hold the same codes and absmax values.
+@pytest.mark.parametrize("T", [1, 2, 5, 333])
+@pytest.mark.parametrize("path", [M.PATH_AUTO, M.PATH_SMALL_M, M.PATH_MFMA])
+def test_forward_bf16_absmax(T, path):
+    _forward_case(S.custom(E=16, top_k=4, H=512, I=256, fmt=O.FMT_NF4_BF16ABS, wid=61), T, path)
+
+
+@pytest.mark.parametrize("T", [1, 5, 333])
+@pytest.mark.parametrize("path", [M.PATH_SMALL_M, M.PATH_MFMA])
+def test_forward_bf16_absmax_bitwise_equals_fp32_absmax(T, path):
+    wl0 = S.custom(E=16, top_k=4, H=512, I=256, fmt=O.FMT_NF4, wid=62)
+    wl2 = S.custom(E=16, top_k=4, H=512, I=256, fmt=O.FMT_NF4_BF16ABS, wid=62)
+    l0, _, _ = build_layers(wl0, 0, DEV, path=path, bf16_source=True)
+    l2, _, _ = build_layers(wl2, 0, DEV, path=path, bf16_source=True)
+    assert l2.w13_scale.dtype == torch.int16 and l0.w13_scale.dtype == torch.float32
+    assert torch.equal(l0.w13, l2.w13) and torch.equal(l0.w2, l2.w2)
+    x = bits_to_torch_bf16(S.make_x(wl0, T))
+    a, b = M.moe_forward(l0, x), M.moe_forward(l2, x)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
 def test_forward_rejects_bad_glu():

@@ -523,3 +523,61 @@ def test_gptoss_zero_weights_leave_the_biases():
     for j in range(2):
         ref += w[:, j:j + 1] * b2[ids[:, j]]
     assert np.allclose(out, ref, rtol=1e-15, atol=0)
+
+
+# ----------------------------------------------------------------------------
+# NF4 with bf16 absmax (experts4bit-qlora page, the --absmax-dtype bf16 paragraph:
+# 5.6 % off every row, lossless for bf16-source weights).
+def _bf16_source(rng, shape):
+    w = (rng.standard_normal(shape) * 0.02).astype(np.float32)
+    return (w.view(np.uint32) & np.uint32(0xFFFF0000)).view(np.float32)   # bf16 values
+
+
+def test_bf16_round_up_grid():
+    """bf16_round_up: a bf16 value, >= a, and the next bf16 value below it is < a."""
+    rng = np.random.default_rng(60)
+    a = np.abs(rng.standard_normal(2000) * 10.0 ** rng.integers(-8, 8, 2000)).astype(np.float32)
+    r = O.bf16_round_up(a)
+    bits = r.astype(np.float32).view(np.uint32)
+    assert np.all(bits & 0xFFFF == 0) and np.all(r >= a)
+    below = ((bits >> 16) - 1).astype(np.uint32) << 16
+    assert np.all(below.view(np.float32).astype(np.float64) < a)
+    exact = (a.view(np.uint32) & np.uint32(0xFFFF0000)).view(np.float32)
+    assert np.array_equal(O.bf16_round_up(exact), exact.astype(np.float64))   # a bf16 value stays
+
+
+def test_bf16_absmax_is_lossless_for_bf16_source():
+    """For bf16-source weights the bf16-absmax form has the fp32 form's codes,
+    its absmax bit for bit, and the same decoded weights."""
+    rng = np.random.default_rng(61)
+    w = _bf16_source(rng, (24, 512))
+    p0, s0 = O.nf4_quantize(w)
+    p2, s2 = O.quantize(O.FMT_NF4_BF16ABS, w)
+    assert np.array_equal(p0, p2)
+    assert s2.dtype == np.uint16 and np.array_equal(s2.astype(np.uint32) << 16, s0.view(np.uint32))
+    assert np.array_equal(O.dequantize(O.FMT_NF4_BF16ABS, p2, s2, 24, 512), O.nf4_dequantize(p0, s0, 24, 512))
+
+
+def test_bf16_absmax_rounds_up_for_fp32_source():
+    """fp32-source weights: the stored absmax is the bf16 round-up of max|w|, no
+    weight leaves the codebook's range, and the NF4 error bound holds for it."""
+    rng = np.random.default_rng(62)
+    w = (rng.standard_normal((16, 256)) * 0.02).astype(np.float32)
+    p2, s2 = O.quantize(O.FMT_NF4_BF16ABS, w)
+    a = np.abs(w.reshape(16, 4, 64).astype(np.float64)).max(axis=2)
+    a2 = (s2.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    assert np.array_equal(a2, O.bf16_round_up(a))
+    deq = O.dequantize(O.FMT_NF4_BF16ABS, p2, s2, 16, 256).astype(np.float64).reshape(16, 4, 64)
+    gap = np.max(np.diff(O.nf4_codebook().astype(np.float64))) / 2
+    err = np.abs(deq - w.reshape(16, 4, 64).astype(np.float64))
+    assert np.all(err <= gap * a2[..., None] * (1 + 1e-6))
+
+
+def test_bf16_absmax_share_printed():
+    """The page: fp32 absmax is 294,912 of 2,654,208 B of a Qwen3-30B expert row
+    set, and bf16 absmax takes 5.6 % off."""
+    H, I = 2048, 768
+    codes = 3 * H * I // 2
+    fp32_abs, bf16_abs = 3 * H * I // 64 * 4, 3 * H * I // 64 * 2
+    assert fp32_abs == 294_912 and codes + fp32_abs == 2_654_208
+    assert round(100 * (fp32_abs - bf16_abs) / (codes + fp32_abs), 1) == 5.6
