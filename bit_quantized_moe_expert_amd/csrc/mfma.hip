@@ -74,7 +74,9 @@ __device__ inline void build_mfma_table(uint4 *tab) {
 // AM: activation operand mode. 0: bf16 A; 2: an fp32 A given as 32-bit
 // (hi, lo) bf16 pairs, its truncated bf16 hi and the RNE bf16 of the rest
 // (the SwiGLU epilogue writes h so), each weight product taking three MFMAs.
-template <int FMT, int EPI, int AM>
+// XF: the extended gate_up / down epilogue (clamped GLU, interleaved gate and
+// up rows, per-expert biases); XF = 0 instantiates the plain kernel.
+template <int FMT, int EPI, int AM, int XF>
 __global__ __launch_bounds__(512) void k_mfma(GemmArgs p, int ntn, int per) {
   static_assert(AM == 0 || AM == 2, "operand mode");
   constexpr bool AF32 = AM != 0;                      // a lo part exists
@@ -112,7 +114,7 @@ __global__ __launch_bounds__(512) void k_mfma(GemmArgs p, int ntn, int per) {
   int64_t col, nrow;
   if (EPI == EPI_SWIGLU) {
     col = (int64_t)nt * 128 + 32 * (wave & 3) + l32;
-    nrow = p.glu_inter ? 2 * col + (wave >> 2) : col + (wave >> 2) * ncol;
+    nrow = (XF && p.glu_inter) ? 2 * col + (wave >> 2) : col + (wave >> 2) * ncol;
   } else {
     col = (int64_t)nt * 256 + 32 * wave + l32;
     nrow = col;
@@ -320,7 +322,7 @@ __global__ __launch_bounds__(512) void k_mfma(GemmArgs p, int ntn, int per) {
     lds_barrier();
     if (wave >= 4) return;
     float bg = 0.0f, bu = 0.0f;  // this column's gate and up biases
-    if (p.bias && nvalid) {
+    if (XF && p.bias && nvalid) {
       const float *bb = p.bias + (int64_t)e * N;
       bg = bb[nrow];
       bu = bb[p.glu_inter ? nrow + 1 : nrow + ncol];
@@ -332,12 +334,13 @@ __global__ __launch_bounds__(512) void k_mfma(GemmArgs p, int ntn, int per) {
         const int m = mb * 32 + 8 * (v >> 2) + 4 * g + (v & 3);
         const float up = xch[((w4 * 4 + mb) * 16 + v) * 64 + lane];
         if (m >= trows || !nvalid) continue;
-        float gt = C[mb][v], ut = up;
-        if (p.bias) {
-          gt += bg;
-          ut += bu;
+        float h;
+        if constexpr (XF) {
+          h = glu_value(p.glu, p.glu_alpha, p.glu_limit, C[mb][v] + bg, up + bu);
+        } else {
+          const float gt = C[mb][v];
+          h = gt / (1.0f + expf(-gt)) * up;
         }
-        const float h = glu_value(p.glu, p.glu_alpha, p.glu_limit, gt, ut);
         const int64_t o = (int64_t)(trow0 + m) * ncol + col;
         if (p.c_split) {  // (truncated bf16 hi, RNE bf16 of the rest) in one word
           const uint32_t hi = __float_as_uint(h) & 0xffff0000u;
@@ -350,7 +353,7 @@ __global__ __launch_bounds__(512) void k_mfma(GemmArgs p, int ntn, int per) {
     return;
   }
   if (!nvalid) return;
-  const float yb = (EPI == EPI_SLOT && p.bias) ? p.bias[(int64_t)e * N + col] : 0.0f;
+  const float yb = (XF && EPI == EPI_SLOT && p.bias) ? p.bias[(int64_t)e * N + col] : 0.0f;
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb) {
 #pragma unroll
@@ -365,20 +368,20 @@ __global__ __launch_bounds__(512) void k_mfma(GemmArgs p, int ntn, int per) {
         reinterpret_cast<uint16_t *>(p.c)[r * N + col] = (uint16_t)f32_to_bf16_rne(y);
       } else {
         const int64_t slot = p.slot_of[r];
-        reinterpret_cast<float *>(p.c)[slot * N + col] = p.slot_w[slot] * (p.bias ? y + yb : y);
+        reinterpret_cast<float *>(p.c)[slot * N + col] = p.slot_w[slot] * (XF ? y + yb : y);
       }
     }
   }
 }
 
-template <int FMT, int EPI, int AM>
+template <int FMT, int EPI, int AM, int XF = 0>
 static hipError_t launch_mfma_t(const GemmArgs &g, hipStream_t s) {
   const int64_t ncol = (EPI == EPI_SWIGLU) ? g.N / 2 : g.N;
   const int ntn = (int)((EPI == EPI_SWIGLU) ? cdiv(ncol, 128) : cdiv(ncol, 256));
   const int64_t total = (int64_t)g.max_tiles * ntn;
   const int64_t padded = cdiv(total, 8) * 8;
   const int per = (int)(padded / 8);
-  NF4MOE_LAUNCH(g, (k_mfma<FMT, EPI, AM>), dim3((unsigned)padded), dim3(512), s, g, ntn, per);
+  NF4MOE_LAUNCH(g, (k_mfma<FMT, EPI, AM, XF>), dim3((unsigned)padded), dim3(512), s, g, ntn, per);
   return hipGetLastError();
 }
 
@@ -386,15 +389,19 @@ static hipError_t launch_mfma_t(const GemmArgs &g, hipStream_t s) {
 // output (down projection) the pre-split planes.
 template <int FMT>
 static hipError_t mfma_pick(const GemmArgs &g, hipStream_t s) {
+  const bool xf = g.glu != 0 || g.glu_inter != 0 || g.bias != nullptr;
+  if (xf && g.epi != EPI_SWIGLU && g.epi != EPI_SLOT) return hipErrorInvalidValue;
   switch (g.epi) {
     case EPI_SWIGLU:
-      return g.a_is_f32 == 0 ? launch_mfma_t<FMT, EPI_SWIGLU, 0>(g, s) : hipErrorInvalidValue;
+      if (g.a_is_f32 != 0) return hipErrorInvalidValue;
+      return xf ? launch_mfma_t<FMT, EPI_SWIGLU, 0, 1>(g, s) : launch_mfma_t<FMT, EPI_SWIGLU, 0>(g, s);
     case EPI_PLAIN_F32:
       return g.a_is_f32 == 0 ? launch_mfma_t<FMT, EPI_PLAIN_F32, 0>(g, s) : hipErrorInvalidValue;
     case EPI_PLAIN_BF16:
       return g.a_is_f32 == 0 ? launch_mfma_t<FMT, EPI_PLAIN_BF16, 0>(g, s) : hipErrorInvalidValue;
     default:
-      return g.a_is_f32 == 2 ? launch_mfma_t<FMT, EPI_SLOT, 2>(g, s) : hipErrorInvalidValue;
+      if (g.a_is_f32 != 2) return hipErrorInvalidValue;
+      return xf ? launch_mfma_t<FMT, EPI_SLOT, 2, 1>(g, s) : launch_mfma_t<FMT, EPI_SLOT, 2>(g, s);
   }
 }
 
