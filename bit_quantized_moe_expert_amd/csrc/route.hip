@@ -38,20 +38,29 @@ __global__ __launch_bounds__(256) void k_logits_rows(const uint16_t *__restrict_
   for (int h = threadIdx.x * 8; h < H; h += 256 * 8) {
     const float4 w0 = *reinterpret_cast<const float4 *>(w + h);
     const float4 w1 = *reinterpret_cast<const float4 *>(w + h + 4);
+    // Tokens in batches of 8: the batch's loads (clamped to a valid row, no
+    // branch) are all issued before the first is used.
 #pragma unroll
-    for (int t = 0; t < TMAX; ++t) {
-      if (t < T) {
-        const uint4 xv = *reinterpret_cast<const uint4 *>(x + (int64_t)t * H + h);
-        float a = acc[t];
-        a = fmaf(bf16lo_to_f32(xv.x), w0.x, a);
-        a = fmaf(bf16hi_to_f32(xv.x), w0.y, a);
-        a = fmaf(bf16lo_to_f32(xv.y), w0.z, a);
-        a = fmaf(bf16hi_to_f32(xv.y), w0.w, a);
-        a = fmaf(bf16lo_to_f32(xv.z), w1.x, a);
-        a = fmaf(bf16hi_to_f32(xv.z), w1.y, a);
-        a = fmaf(bf16lo_to_f32(xv.w), w1.z, a);
-        a = fmaf(bf16hi_to_f32(xv.w), w1.w, a);
-        acc[t] = a;
+    for (int t0 = 0; t0 < TMAX; t0 += 8) {
+      if (t0 >= T) break;  // uniform
+      uint4 xv[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int t = t0 + i < T ? t0 + i : 0;
+        xv[i] = *reinterpret_cast<const uint4 *>(x + (int64_t)t * H + h);
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        float a = acc[t0 + i];
+        a = fmaf(bf16lo_to_f32(xv[i].x), w0.x, a);
+        a = fmaf(bf16hi_to_f32(xv[i].x), w0.y, a);
+        a = fmaf(bf16lo_to_f32(xv[i].y), w0.z, a);
+        a = fmaf(bf16hi_to_f32(xv[i].y), w0.w, a);
+        a = fmaf(bf16lo_to_f32(xv[i].z), w1.x, a);
+        a = fmaf(bf16hi_to_f32(xv[i].z), w1.y, a);
+        a = fmaf(bf16lo_to_f32(xv[i].w), w1.z, a);
+        a = fmaf(bf16hi_to_f32(xv[i].w), w1.w, a);
+        acc[t0 + i] = a;   // rows past T are computed from row 0 and never stored
       }
     }
   }
@@ -257,22 +266,18 @@ hipError_t launch_router_logits(const uint16_t *x, int T, int H, const float *W,
 // descending, id ascending); lane j keeps the j-th pick.
 // ---------------------------------------------------------------------------
 template <int EPL>
-__global__ __launch_bounds__(256) void k_topk(const float *__restrict__ L, int T, int E, int k,
-                                              int renorm, int32_t *__restrict__ ids,
-                                              float *__restrict__ wts) {
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;
+__device__ inline void wave_topk(const float *Lrow, int E, int k, int renorm, int &my_id, float &wgt) {
   const int lane = threadIdx.x & 63;
   constexpr int kNone = INT_MAX;
   float v[EPL];
 #pragma unroll
   for (int j = 0; j < EPL; ++j) {
     const int e = lane + 64 * j;
-    v[j] = e < E ? L[(int64_t)t * E + e] : -__builtin_inff();
+    v[j] = e < E ? Lrow[e] : -__builtin_inff();
   }
   uint32_t taken = 0;
-  int my_id = 0;
   float my_v = 0.0f;
+  my_id = 0;
   for (int i = 0; i < k; ++i) {
     float bv = -__builtin_inff();
     int bid = kNone;
@@ -315,7 +320,19 @@ __global__ __launch_bounds__(256) void k_topk(const float *__restrict__ L, int T
       for (int l = 0; l < 64 && 64 * j + l < E; ++l) den += __shfl(ex, l, kWave);
     }
   }
-  const float wgt = expf(my_v - v0) / den;
+  wgt = expf(my_v - v0) / den;
+}
+
+template <int EPL>
+__global__ __launch_bounds__(256) void k_topk(const float *__restrict__ L, int T, int E, int k,
+                                              int renorm, int32_t *__restrict__ ids,
+                                              float *__restrict__ wts) {
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const int lane = threadIdx.x & 63;
+  int my_id;
+  float wgt;
+  wave_topk<EPL>(L + (int64_t)t * E, E, k, renorm, my_id, wgt);
   if (lane < k) {
     ids[(int64_t)t * k + lane] = my_id;
     wts[(int64_t)t * k + lane] = wgt;
@@ -479,18 +496,22 @@ __global__ __launch_bounds__(256) void k_group_scatter(const int32_t *__restrict
 }
 
 // ---------------------------------------------------------------------------
-// Decode-sized routing tail (T <= kSmallT tokens, E <= kSmallE experts) in one
-// workgroup of 1024 threads: top-k by rank (each (token, expert) counts the
-// experts ordered before it, in parallel), softmax, counting sort with exact
-// stable ranks, the non-empty expert list and the MFMA tiles.
+// Small-batch routing tail (T <= kSmallT tokens, E <= kSmallE experts,
+// T * E <= kSmallTE, T * k <= 1024) in one workgroup of 1024 threads: top-k by
+// rank (each (token, expert) counts the experts ordered before it, reading the
+// token's logits from LDS), softmax in the routing kernels' order, counting
+// sort with exact stable ranks, the non-empty expert list and the MFMA tiles.
+// (A wave-per-token argmax, as in k_topk, measured slower here: its k rounds
+// of dependent cross-lane shuffles outlast the parallel rank count.)
 // ---------------------------------------------------------------------------
-constexpr int kSmallT = 8;
+constexpr int kSmallT = 32;
 constexpr int kSmallE = 256;
+constexpr int kSmallTE = 4096;  // bounds the O(T * E * E) rank count of one workgroup
 
 __global__ __launch_bounds__(1024) void k_route_tail_small(const float *__restrict__ L, int T, int E,
                                                            int k, int renorm, int bm, int max_tiles,
                                                            RouteBufs o) {
-  __shared__ float Ls[kSmallT * kSmallE];
+  __shared__ __attribute__((aligned(16))) float Ls[kSmallTE];
   __shared__ int sel_id[kSmallT * kMaxTopK];
   __shared__ float sel_v[kSmallT * kMaxTopK];
   __shared__ int cnt[kSmallE];
@@ -498,17 +519,24 @@ __global__ __launch_bounds__(1024) void k_route_tail_small(const float *__restri
   __shared__ int s_total;
   const int tid = threadIdx.x;
   const int TE = T * E, R = T * k;
-  for (int i = tid; i < TE; i += 1024) Ls[i] = L[i];
+  const int Ep = (E + 3) & ~3;  // LDS row stride: 16-byte rows, padded with -inf
+  for (int i = tid; i < T * Ep; i += 1024) {
+    const int t = i / Ep, f = i - t * Ep;
+    Ls[i] = f < E ? L[(int64_t)t * E + f] : -__builtin_inff();
+  }
   for (int e = tid; e < E; e += 1024) cnt[e] = 0;
   __syncthreads();
   for (int i = tid; i < TE; i += 1024) {
     const int t = i / E, e = i - t * E;
-    const float v = Ls[i];
-    const float *row = Ls + t * E;
+    const float *row = Ls + t * Ep;
+    const float v = row[e];
     int rank = 0;
-    for (int f = 0; f < E; ++f) {
-      const float u = row[f];
-      rank += (u > v || (u == v && f < e)) ? 1 : 0;
+    for (int f = 0; f < Ep; f += 4) {  // the lanes of a wave share the row: broadcast reads
+      const float4 u = *reinterpret_cast<const float4 *>(row + f);
+      rank += (u.x > v || (u.x == v && f < e)) ? 1 : 0;
+      rank += (u.y > v || (u.y == v && f + 1 < e)) ? 1 : 0;
+      rank += (u.z > v || (u.z == v && f + 2 < e)) ? 1 : 0;
+      rank += (u.w > v || (u.w == v && f + 3 < e)) ? 1 : 0;
     }
     if (rank < k) {
       sel_id[t * k + rank] = e;
@@ -517,20 +545,18 @@ __global__ __launch_bounds__(1024) void k_route_tail_small(const float *__restri
   }
   __syncthreads();
   if (tid < R) {
-    const int t = tid / k, j = tid - t * k;
+    // the denominator in the routing kernels' order: selected experts by rank,
+    // or every expert by id
+    const int t = tid / k;
     const float v0 = sel_v[t * k];
-    float w;
+    float sum = 0.0f;
     if (renorm) {
-      float sum = 0.0f;
       for (int q = 0; q < k; ++q) sum += expf(sel_v[t * k + q] - v0);
-      w = expf(sel_v[tid] - v0) / sum;
     } else {
-      float sum = 0.0f;
-      for (int f = 0; f < E; ++f) sum += expf(Ls[t * E + f] - v0);
-      w = expf(sel_v[tid] - v0) / sum;
+      for (int f = 0; f < E; ++f) sum += expf(Ls[t * Ep + f] - v0);
     }
     o.topk_ids[tid] = sel_id[tid];
-    o.topk_w[tid] = w;
+    o.topk_w[tid] = expf(sel_v[tid] - v0) / sum;
     atomicAdd(&cnt[sel_id[tid]], 1);
   }
   __syncthreads();
@@ -564,7 +590,7 @@ __global__ __launch_bounds__(1024) void k_route_tail_small(const float *__restri
 hipError_t launch_route(const float *logits, int T, int E, int k, int renorm, const RouteBufs &rb,
                         int bm, hipStream_t s) {
   const int R = T * k;
-  if (T <= kSmallT && E <= kSmallE) {
+  if (T <= kSmallT && E <= kSmallE && T * ((E + 3) & ~3) <= kSmallTE && R <= 1024) {
     const int max_tiles = (int)cdiv(R, bm) + (R < E ? R : E);
     hipLaunchKernelGGL(k_route_tail_small, dim3(1), dim3(1024), 0, s, logits, T, E, k, renorm, bm,
                        max_tiles, rb);

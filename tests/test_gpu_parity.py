@@ -119,7 +119,8 @@ def _route_case(T, E, k, renorm, ties, seed):
     assert np.max(np.abs(got["topk_w"].cpu().numpy() - w_o)) <= 1e-6
 
 
-@pytest.mark.parametrize("T,E,k", [(1, 64, 8), (16, 8, 2), (300, 128, 8), (4097, 64, 8),
+@pytest.mark.parametrize("T,E,k", [(1, 64, 8), (16, 8, 2), (32, 128, 8), (20, 200, 4), (33, 64, 8),
+                                   (300, 128, 8), (4097, 64, 8),
                                    (50, 1000, 32), (7, 8, 8), (64, 4, 1), (600, 1024, 4)])
 @pytest.mark.parametrize("renorm", [1, 0])
 def test_route_permute_bitexact(T, E, k, renorm):
