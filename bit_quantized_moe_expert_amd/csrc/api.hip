@@ -55,7 +55,7 @@ struct Carve {
 };
 
 struct RoutePlan {
-  int R, nchunks, max_grp, max_tiles;
+  int R, nchunks, max_grp, max_tiles, tile_rows;
 };
 
 RoutePlan route_plan(int T, int E, int k) {
@@ -63,7 +63,8 @@ RoutePlan route_plan(int T, int E, int k) {
   rp.R = T * k;
   rp.nchunks = (int)cdiv(rp.R, kChunk);
   rp.max_grp = rp.R < E ? rp.R : E;
-  rp.max_tiles = (int)cdiv(rp.R, kMfmaBM) + rp.max_grp;
+  rp.tile_rows = mfma_tile_rows(rp.R, E);
+  rp.max_tiles = (int)cdiv(rp.R, rp.tile_rows) + rp.max_grp;
   return rp;
 }
 
@@ -75,7 +76,8 @@ void carve_route_scratch(Carve &cv, const RoutePlan &rp, int E, RouteBufs &rb) {
   rb.grp_row0 = cv.take<int32_t>(E);
   rb.grp_rows = cv.take<int32_t>(E);
   rb.counters = cv.take<int32_t>(16);
-  rb.tiles = cv.take<int4>(rp.max_tiles > 0 ? rp.max_tiles : 1);
+  // room for 64-row tiles whatever the plan, so the size only grows with R
+  rb.tiles = cv.take<int4>((size_t)cdiv(rp.R, 64) + rp.max_grp + 1);
 }
 
 struct ForwardCarve {
@@ -285,7 +287,7 @@ size_t nf4moe_gemm_workspace_bytes(int32_t G, int32_t R) {
   cv.take<int32_t>(G);
   cv.take<int32_t>(G);
   cv.take<int32_t>(16);
-  cv.take<int4>((size_t)cdiv(R, kMfmaBM) + G);
+  cv.take<int4>((size_t)cdiv(R, 64) + G);  // room for 64-row tiles
   return align_up(cv.off);
 }
 
@@ -329,8 +331,9 @@ nf4moe_status_t nf4moe_grouped_gemm(nf4moe_format_t fmt, const uint16_t *a, cons
   rb.grp_row0 = cv.take<int32_t>(G);
   rb.grp_rows = cv.take<int32_t>(G);
   rb.counters = cv.take<int32_t>(16);
-  rb.tiles = cv.take<int4>((size_t)cdiv(R, kMfmaBM) + G);
-  hipError_t e = launch_groups_from_offsets(group_offsets, group_experts, G, R, E, rb, kMfmaBM, s);
+  rb.tiles = cv.take<int4>((size_t)cdiv(R, 64) + G);
+  const int bm = mfma_tile_rows(R, G);
+  hipError_t e = launch_groups_from_offsets(group_offsets, group_experts, G, R, E, rb, bm, s);
   if (e != hipSuccess) return hip_status(e, "group table launch");
   GemmArgs g = base_args(fmt);
   g.a = a;
@@ -348,7 +351,8 @@ nf4moe_status_t nf4moe_grouped_gemm(nf4moe_format_t fmt, const uint16_t *a, cons
   g.max_grp = G;
   g.tiles = rb.tiles;
   g.n_tiles = rb.counters + 1;
-  g.max_tiles = (int)(cdiv(R, kMfmaBM) + G);
+  g.max_tiles = (int)(cdiv(R, bm) + G);
+  g.tile_rows = bm;
   g.epi = c_dtype == NF4MOE_DT_F32 ? EPI_PLAIN_F32 : EPI_PLAIN_BF16;
   g.c = c;
   if (use == NF4MOE_PATH_SMALL_M)
@@ -451,7 +455,7 @@ static nf4moe_status_t forward_impl(const nf4moe_layer_t *layer, const uint16_t 
   // gate_up kernel; otherwise they are their own launches.
   const bool fused_route = use == NF4MOE_PATH_SMALL_M && T == 1 && L.E <= 128;
   if (!fused_route) {
-    e = launch_route(fc.logits, T, L.E, L.top_k, L.renormalize, fc.rb, kMfmaBM, s);
+    e = launch_route(fc.logits, T, L.E, L.top_k, L.renormalize, fc.rb, rp.tile_rows, s);
     if (e != hipSuccess) return hip_status(e, "route launch");
   }
   if ((e = mark(1)) != hipSuccess) return hip_status(e, "event record");
@@ -476,6 +480,7 @@ static nf4moe_status_t forward_impl(const nf4moe_layer_t *layer, const uint16_t 
   g.tiles = fc.rb.tiles;
   g.n_tiles = fc.rb.counters + 1;
   g.max_tiles = rp.max_tiles;
+  g.tile_rows = rp.tile_rows;
   g.epi = EPI_SWIGLU;
   g.glu = L.glu;
   g.glu_alpha = L.glu_alpha;

@@ -94,7 +94,20 @@ struct GemmArgs {
   // Per-expert bias [E, N] added to the product (by weight row) before the
   // epilogue: SwiGLU before the activation, slot before the routing weight.
   const float *bias;
+  // MFMA path: rows per tile of the tile table (128, or 64 for routed batches
+  // with few rows per expert); 0 means 128.
+  int tile_rows;
 };
+
+// Rows per MFMA tile for R routed rows over at most G groups: 64-row tiles
+// when the groups average at most 48 rows, else 128. (Measured: 64-row tiles
+// take 14-29 % off Qwen3-shaped T = 128 / 512 and OLMoE-shaped T = 64 layers;
+// at 64 rows per group, gpt-oss-shaped T = 2048, they cost 8 %: half the
+// MFMAs per decoded weight.)
+inline int mfma_tile_rows(int64_t R, int64_t G) {
+  const int64_t groups = R < G ? R : G;
+  return (groups > 0 && R <= 48 * groups) ? 64 : 128;
+}
 
 // Launch through hipExtLaunchKernelGGL when the arguments carry events.
 #define NF4MOE_LAUNCH(G, KERNEL, GRID, BLOCK, STREAM, ...)                                          \

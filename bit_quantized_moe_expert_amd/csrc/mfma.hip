@@ -34,7 +34,6 @@ namespace nf4moe {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
-constexpr int kBM = kMfmaBM;  // 128
 constexpr int kBK = 64;
 constexpr int kApad = 72;     // bf16 per LDS row of A (64 + 8 padding)
 
@@ -76,10 +75,14 @@ __device__ inline void build_mfma_table(uint4 *tab) {
 // (the SwiGLU epilogue writes h so), each weight product taking three MFMAs.
 // XF: the extended gate_up / down epilogue (clamped GLU, interleaved gate and
 // up rows, per-expert biases); XF = 0 instantiates the plain kernel.
-template <int FMT, int EPI, int AM, int XF>
+// MB: 32-row blocks per tile (4: 128-row tiles; 2: 64-row tiles, for routed
+// batches with few rows per expert, where 128-row tiles would be mostly empty).
+template <int FMT, int EPI, int AM, int XF, int MB>
 __global__ __launch_bounds__(512) void k_mfma(GemmArgs p, int ntn, int per) {
   static_assert(AM == 0 || AM == 2, "operand mode");
+  static_assert(MB == 4 || MB == 2, "row blocks");
   constexpr bool AF32 = AM != 0;                      // a lo part exists
+  constexpr int kBM = 32 * MB;                        // rows per tile
   constexpr int ABUF = kBM * kApad * 2;               // bytes per A buffer
   constexpr int NBUF = AF32 ? 4 : 2;                  // hi[2] (+ lo[2])
   __shared__ __attribute__((aligned(16))) uint8_t smem[kTabBytes + NBUF * ABUF];
@@ -127,35 +130,37 @@ __global__ __launch_bounds__(512) void k_mfma(GemmArgs p, int ntn, int per) {
   const int64_t sc_per_row = K / Fmt<FMT>::kBlock;
   const int64_t sc_base = (int64_t)e * N * sc_per_row;
 
-  // A-tile slice owned by this thread for the LDS fill: row am, 16 elements
-  // starting at k0 + 16 * aq. Rows past the tile read a valid row (the tile's
+  // A-tile slice owned by this thread for the LDS fill: row am, EPT elements
+  // starting at k0 + EPT * aq. Rows past the tile read a valid row (the tile's
   // first) and are zeroed when stored.
-  const int am = tid >> 2, aq = tid & 3;
+  constexpr int TPR = 512 / kBM;                      // fill threads per row
+  constexpr int EPT = 64 / TPR;                       // elements per thread: 16 or 8
+  const int am = tid / TPR, aq = tid % TPR;
   const bool arow_ok = am < trows;
   int64_t arow;
   {
     const int r = trow0 + (arow_ok ? am : 0);
     arow = p.a_row_of ? (int64_t)(p.a_row_of[r] / p.a_div) : (int64_t)r;
   }
-  constexpr int AW = AF32 ? 4 : 2;                    // 16-byte words per thread
+  constexpr int AW = EPT * (AF32 ? 4 : 2) / 16;       // 16-byte words per thread
   uint4 areg[AW];
   bool a_ok = false;
   auto load_a = [&](int64_t k0) {
-    const int64_t kk = k0 + 16 * aq;
+    const int64_t kk = k0 + EPT * aq;
     a_ok = arow_ok && kk < K;
     const int64_t kc = kk < K ? kk : 0;
-    // AM 0: 16 bf16; AM 2: 16 (hi, lo) bf16 pairs, 4 bytes each
+    // AM 0: EPT bf16; AM 2: EPT (hi, lo) bf16 pairs, 4 bytes each
     const uint4 *src = reinterpret_cast<const uint4 *>(reinterpret_cast<const uint8_t *>(p.a) +
                                                        (arow * K + kc) * (AM == 2 ? 4 : 2));
 #pragma unroll
     for (int i = 0; i < AW; ++i) areg[i] = src[i];
   };
   auto store_a = [&](int buf) {
-    uint16_t *dh = abuf(0, buf) + am * kApad + 16 * aq;
+    uint16_t *dh = abuf(0, buf) + am * kApad + EPT * aq;
     if (AM == 2) {  // de-interleave the pairs into the hi and lo tiles
-      uint16_t *dl = abuf(1, buf) + am * kApad + 16 * aq;
+      uint16_t *dl = abuf(1, buf) + am * kApad + EPT * aq;
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
+      for (int i = 0; i < EPT / 8; ++i) {
         const uint4 u = areg[2 * i], v = areg[2 * i + 1];
         const uint32_t w[8] = {u.x, u.y, u.z, u.w, v.x, v.y, v.z, v.w};
         uint32_t h4[4], l4[4];
@@ -169,7 +174,7 @@ __global__ __launch_bounds__(512) void k_mfma(GemmArgs p, int ntn, int per) {
       }
     } else {
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < AW; ++i)
         *reinterpret_cast<uint4 *>(dh + 8 * i) = a_ok ? areg[i] : make_uint4(0, 0, 0, 0);
     }
   };
@@ -190,9 +195,9 @@ __global__ __launch_bounds__(512) void k_mfma(GemmArgs p, int ntn, int per) {
   };
 
   const f32x16_t zero16 = {};
-  f32x16_t C[4], P[4];
+  f32x16_t C[MB], P[MB];
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb) C[mb] = zero16;
+  for (int mb = 0; mb < MB; ++mb) C[mb] = zero16;
 
   // One K-step on LDS buffer `cur` with codes bq and scale bs, prefetching
   // the next step into (bqn, brn, bokn) and the other LDS buffer.
@@ -213,10 +218,10 @@ __global__ __launch_bounds__(512) void k_mfma(GemmArgs p, int ntn, int per) {
     // s's MFMAs (fp32 A: only the lookups; its fragments would not fit).
     constexpr int NA = AF32 ? 1 : 2;
     uint2 t[2][4];
-    bf16x8_t ah[NA][4], al[NA][4];
+    bf16x8_t ah[NA][MB], al[NA][MB];
     auto read_a = [&](int sa, bf16x8_t *dh, bf16x8_t *dl) {
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb) {
+      for (int mb = 0; mb < MB; ++mb) {
         const int row = mb * 32 + l32;
         const int colk = 32 * g + 8 * sa;
         dh[mb] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4 *>(Ah + row * kApad + colk));
@@ -246,14 +251,14 @@ __global__ __launch_bounds__(512) void k_mfma(GemmArgs p, int ntn, int per) {
           // passes over the four independent accumulators, so consecutive
           // MFMAs never depend on each other
 #pragma unroll
-          for (int mb = 0; mb < 4; ++mb)
+          for (int mb = 0; mb < MB; ++mb)
             P[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahs[mb], bh, s == 0 ? zero16 : P[mb], 0, 0, 0);
 #pragma unroll
-          for (int mb = 0; mb < 4; ++mb)
+          for (int mb = 0; mb < MB; ++mb)
             P[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahs[mb], bl, P[mb], 0, 0, 0);
           if (AF32) {
 #pragma unroll
-            for (int mb = 0; mb < 4; ++mb)
+            for (int mb = 0; mb < MB; ++mb)
               P[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(als[mb], bh, P[mb], 0, 0, 0);
           }
         } else {
@@ -266,11 +271,11 @@ __global__ __launch_bounds__(512) void k_mfma(GemmArgs p, int ntn, int per) {
           }
           const bf16x8_t bv = as_bf16x8(d[0], d[1], d[2], d[3]);
 #pragma unroll
-          for (int mb = 0; mb < 4; ++mb)
+          for (int mb = 0; mb < MB; ++mb)
             C[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahs[mb], bv, C[mb], 0, 0, 0);
           if (AF32) {
 #pragma unroll
-            for (int mb = 0; mb < 4; ++mb)
+            for (int mb = 0; mb < MB; ++mb)
               C[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(als[mb], bv, C[mb], 0, 0, 0);
           }
         }
@@ -279,7 +284,7 @@ __global__ __launch_bounds__(512) void k_mfma(GemmArgs p, int ntn, int per) {
     }
     if (Fmt<FMT>::kNF4) {  // NF4: the block's absmax scales its partial product
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
+      for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int v = 0; v < 16; ++v) C[mb][v] = fmaf(bs, P[mb][v], C[mb][v]);
     }
@@ -315,9 +320,9 @@ __global__ __launch_bounds__(512) void k_mfma(GemmArgs p, int ntn, int per) {
     const int w4 = wave & 3;
     if (wave >= 4) {
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
+      for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) xch[((w4 * 4 + mb) * 16 + v) * 64 + lane] = C[mb][v];
+        for (int v = 0; v < 16; ++v) xch[((w4 * MB + mb) * 16 + v) * 64 + lane] = C[mb][v];
     }
     lds_barrier();
     if (wave >= 4) return;
@@ -328,11 +333,11 @@ __global__ __launch_bounds__(512) void k_mfma(GemmArgs p, int ntn, int per) {
       bu = bb[p.glu_inter ? nrow + 1 : nrow + ncol];
     }
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
+    for (int mb = 0; mb < MB; ++mb) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int m = mb * 32 + 8 * (v >> 2) + 4 * g + (v & 3);
-        const float up = xch[((w4 * 4 + mb) * 16 + v) * 64 + lane];
+        const float up = xch[((w4 * MB + mb) * 16 + v) * 64 + lane];
         if (m >= trows || !nvalid) continue;
         float h;
         if constexpr (XF) {
@@ -355,7 +360,7 @@ __global__ __launch_bounds__(512) void k_mfma(GemmArgs p, int ntn, int per) {
   if (!nvalid) return;
   const float yb = (XF && EPI == EPI_SLOT && p.bias) ? p.bias[(int64_t)e * N + col] : 0.0f;
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb) {
+  for (int mb = 0; mb < MB; ++mb) {
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const int m = mb * 32 + 8 * (v >> 2) + 4 * g + (v & 3);
@@ -374,15 +379,23 @@ __global__ __launch_bounds__(512) void k_mfma(GemmArgs p, int ntn, int per) {
   }
 }
 
-template <int FMT, int EPI, int AM, int XF = 0>
-static hipError_t launch_mfma_t(const GemmArgs &g, hipStream_t s) {
+template <int FMT, int EPI, int AM, int XF, int MB>
+static hipError_t launch_mfma_mb(const GemmArgs &g, hipStream_t s) {
   const int64_t ncol = (EPI == EPI_SWIGLU) ? g.N / 2 : g.N;
   const int ntn = (int)((EPI == EPI_SWIGLU) ? cdiv(ncol, 128) : cdiv(ncol, 256));
   const int64_t total = (int64_t)g.max_tiles * ntn;
   const int64_t padded = cdiv(total, 8) * 8;
   const int per = (int)(padded / 8);
-  NF4MOE_LAUNCH(g, (k_mfma<FMT, EPI, AM, XF>), dim3((unsigned)padded), dim3(512), s, g, ntn, per);
+  NF4MOE_LAUNCH(g, (k_mfma<FMT, EPI, AM, XF, MB>), dim3((unsigned)padded), dim3(512), s, g, ntn, per);
   return hipGetLastError();
+}
+
+// The tile table's row count (GemmArgs::tile_rows, 128 unless set) picks MB.
+template <int FMT, int EPI, int AM, int XF = 0>
+static hipError_t launch_mfma_t(const GemmArgs &g, hipStream_t s) {
+  if (g.tile_rows == 64) return launch_mfma_mb<FMT, EPI, AM, XF, 2>(g, s);
+  if (g.tile_rows == 0 || g.tile_rows == 128) return launch_mfma_mb<FMT, EPI, AM, XF, 4>(g, s);
+  return hipErrorInvalidValue;
 }
 
 // Instantiated operand modes: SwiGLU (gate_up) and plain outputs bf16 A; slot

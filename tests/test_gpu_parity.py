@@ -305,6 +305,16 @@ def test_forward_rejects_bad_glu():
         M.moe_forward(dev_layer, x)
 
 
+@pytest.mark.parametrize("fmt", [O.FMT_NF4, O.FMT_MXFP4])
+@pytest.mark.parametrize("T", [800, 1000])
+def test_forward_mfma_tile_heights(fmt, T):
+    """Both MFMA tile heights: ~200 and ~250 rows per expert take 128-row tiles,
+    the same shapes with 16x the experts take 64-row tiles."""
+    for E in (4, 64):
+        wl = S.custom(E=E, top_k=1, H=256, I=128, fmt=fmt, wid=70 + E)
+        _forward_case(wl, T, M.PATH_MFMA, sample=[0, T // 2, T - 1])
+
+
 def test_forward_deterministic():
     wl = S.custom(E=16, top_k=4, H=512, I=256, wid=25)
     for T, path in ((1, 0), (300, 2), (40, 1)):
