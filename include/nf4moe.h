@@ -36,6 +36,8 @@
  *  MXFP4_B32 codes uint8 [.., N, K/2], LOW nibble = even k, OCP e2m1 values;
  *            scales uint8 e8m0 [.., N, K/32]; value = e2m1(code) * 2^(e8m0-127),
  *            e8m0 = 255 is NaN. K % 32 == 0.
+ *  NF4_B64_BF16ABS  as NF4_B64 with the absmax stored as bf16 bits, uint16
+ *            [.., N, K/64]; the decode widens it to fp32 first.
  */
 #ifndef NF4MOE_H
 #define NF4MOE_H
@@ -69,8 +71,9 @@ typedef enum {
 typedef enum { NF4MOE_DT_F32 = 0, NF4MOE_DT_BF16 = 1 } nf4moe_dtype_t;
 
 /* Which grouped-GEMM kernel family runs. AUTO picks from the routed row count
- * known on the host (R = T * top_k): small R runs the bandwidth-bound decode
- * kernels, large R the MFMA kernels. The other values force one family (for
+ * known on the host (R = T * top_k): R <= 128 (with H, I <= 4096) runs the
+ * bandwidth-bound decode kernels, larger R the MFMA kernels (with 64-row tiles
+ * when the groups average at most 48 rows, else 128). The other values force one family (for
  * A/B measurement and tests); the result must satisfy the same tolerance. */
 typedef enum { NF4MOE_PATH_AUTO = 0, NF4MOE_PATH_SMALL_M = 1, NF4MOE_PATH_MFMA = 2 } nf4moe_path_t;
 
@@ -251,9 +254,15 @@ size_t nf4moe_workspace_bytes(const nf4moe_layer_t *layer, int32_t T_max);
  *   out bf16 [T, H] (device)
  *   topk_ids_out [T, k] int32 / topk_w_out [T, k] fp32: optional copies of the
  *   routing decision (device, may be NULL).
- * Intermediates (h, partial products) stay fp32; no bf16 expert weight is
- * written anywhere. Errors: INVALID_ARG (layer fields, sizes, pointers),
- * WORKSPACE (ws_bytes < nf4moe_workspace_bytes(layer, T)). T == 0 is a no-op. */
+ * The gate_up epilogue is SwiGLU, or with layer->glu the clamped GLU with the
+ * layer's biases (see nf4moe_glu_t). Intermediates (h, partial products) stay
+ * fp32; no bf16 expert weight is written anywhere.
+ * Row-count invariance (the pages' STATUS page, kernel section): on the small-M
+ * path (AUTO picks it for T * top_k <= 128) a token's outputs and routing carry
+ * the same bits whatever the other tokens of the call; on the MFMA path, among
+ * calls of 33 tokens or more; across the two they differ in summation order.
+ * Errors: INVALID_ARG (layer fields, sizes, pointers), WORKSPACE (ws_bytes <
+ * nf4moe_workspace_bytes(layer, T)). T == 0 is a no-op. */
 nf4moe_status_t nf4moe_moe_forward(const nf4moe_layer_t *layer, const uint16_t *x, int32_t T,
                                    uint16_t *out, int32_t *topk_ids_out, float *topk_w_out,
                                    void *ws, size_t ws_bytes, void *stream);
