@@ -264,60 +264,85 @@ hipError_t launch_router_logits(const uint16_t *x, int T, int H, const float *W,
 // top-k + softmax: one wave per token. Lane l holds the logits of experts
 // l, l + 64, ...; k rounds of a wave-wide argmax under the order (logit
 // descending, id ascending); lane j keeps the j-th pick.
+//
+// The argmax runs on order-preserving 32-bit keys of the logits: the wave
+// maximum of the keys comes from DPP row shifts and row broadcasts (no LDS
+// round trips), and the lowest expert id holding it from one ballot per
+// logit slot, so ties go to the lower id as the compare order requires.
 // ---------------------------------------------------------------------------
+// Larger float -> larger key; -0 is folded onto +0 first, so floats that
+// compare equal get equal keys.
+__device__ inline uint32_t float_order_key(float v) {
+  const uint32_t b = __float_as_uint(v + 0.0f);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+// Maximum of v over the 64 lanes: within each row of 16 lanes by right
+// shifts (1, 2, 3, then 4 and 8 on the upper banks), then across rows by the
+// row-15 and row-31 broadcasts; lane 63 ends with the maximum.
+__device__ inline uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x111, 0xf, 0xf, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x112, 0xf, 0xf, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x113, 0xf, 0xf, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x114, 0xf, 0xe, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x118, 0xf, 0xc, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x142, 0xa, 0xf, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x143, 0xc, 0xf, false));
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+__device__ inline float lane_value(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+
 template <int EPL>
 __device__ inline void wave_topk(const float *Lrow, int E, int k, int renorm, int &my_id, float &wgt) {
   const int lane = threadIdx.x & 63;
-  constexpr int kNone = INT_MAX;
   float v[EPL];
+  uint32_t key[EPL];  // 0: no expert, or already picked (below every logit's key)
 #pragma unroll
   for (int j = 0; j < EPL; ++j) {
     const int e = lane + 64 * j;
     v[j] = e < E ? Lrow[e] : -__builtin_inff();
+    key[j] = e < E ? float_order_key(v[j]) : 0u;
   }
-  uint32_t taken = 0;
   float my_v = 0.0f;
   my_id = 0;
   for (int i = 0; i < k; ++i) {
-    float bv = -__builtin_inff();
-    int bid = kNone;
+    uint32_t lm = key[0];
+#pragma unroll
+    for (int j = 1; j < EPL; ++j) lm = max(lm, key[j]);
+    const uint32_t wm = wave_max_u32(lm);
+    int win = -1;  // lowest id holding the maximum (uniform)
 #pragma unroll
     for (int j = 0; j < EPL; ++j) {
-      const int e = lane + 64 * j;
-      if (e < E && !((taken >> j) & 1u)) {
-        if (bid == kNone || v[j] > bv || (v[j] == bv && e < bid)) {
-          bv = v[j];
-          bid = e;
-        }
-      }
+      const uint64_t m = __ballot(key[j] == wm);
+      if (win < 0 && m != 0) win = 64 * j + (int)__builtin_ctzll(m);
     }
 #pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) {
-      const float ov = __shfl_xor(bv, m, kWave);
-      const int oid = __shfl_xor(bid, m, kWave);
-      if (oid != kNone && (bid == kNone || ov > bv || (ov == bv && oid < bid))) {
-        bv = ov;
-        bid = oid;
-      }
-    }
-    if ((bid & 63) == lane) taken |= 1u << (bid >> 6);
+    for (int j = 0; j < EPL; ++j)
+      if (win == lane + 64 * j) key[j] = 0u;
+    float wv = 0.0f;  // the pick's logit, read from its lane
+#pragma unroll
+    for (int j = 0; j < EPL; ++j)
+      if ((win >> 6) == j) wv = lane_value(v[j], win & 63);
     if (lane == i) {
-      my_id = bid;
-      my_v = bv;
+      my_id = win;
+      my_v = wv;
     }
   }
-  const float v0 = __shfl(my_v, 0, kWave);  // the largest logit
+  const float v0 = lane_value(my_v, 0);  // the largest logit
   // Denominator summed in one fixed order (selected experts by rank, or all
   // experts by id), the order every routing kernel here uses.
   float den = 0.0f;
   if (renorm) {
     const float ex = lane < k ? expf(my_v - v0) : 0.0f;
-    for (int q = 0; q < k; ++q) den += __shfl(ex, q, kWave);
+    for (int q = 0; q < k; ++q) den += lane_value(ex, q);
   } else {
 #pragma unroll
     for (int j = 0; j < EPL; ++j) {
       const float ex = lane + 64 * j < E ? expf(v[j] - v0) : 0.0f;
-      for (int l = 0; l < 64 && 64 * j + l < E; ++l) den += __shfl(ex, l, kWave);
+      for (int l = 0; l < 64 && 64 * j + l < E; ++l) den += lane_value(ex, l);
     }
   }
   wgt = expf(my_v - v0) / den;
@@ -497,28 +522,27 @@ __global__ __launch_bounds__(256) void k_group_scatter(const int32_t *__restrict
 
 // ---------------------------------------------------------------------------
 // Small-batch routing tail (T <= kSmallT tokens, E <= kSmallE experts,
-// T * E <= kSmallTE, T * k <= 1024) in one workgroup of 1024 threads: top-k by
-// rank (each (token, expert) counts the experts ordered before it, reading the
-// token's logits from LDS), softmax in the routing kernels' order, counting
-// sort with exact stable ranks, the non-empty expert list and the MFMA tiles.
-// (A wave-per-token argmax, as in k_topk, measured slower here: its k rounds
-// of dependent cross-lane shuffles outlast the parallel rank count.)
+// T * E <= kSmallTE, T * k <= 1024) in one workgroup of 1024 threads: the
+// token's logits copied to LDS, top-k + softmax by wave_topk (one wave per
+// token, as k_topk), then one block scan for the expert offsets, the
+// non-empty expert list and the MFMA tiles, and stable ranks by ballots.
 // ---------------------------------------------------------------------------
 constexpr int kSmallT = 32;
 constexpr int kSmallE = 256;
-constexpr int kSmallTE = 4096;  // bounds the O(T * E * E) rank count of one workgroup
+constexpr int kSmallTE = 4096;  // bounds the LDS copy of the logits
 
 __global__ __launch_bounds__(1024) void k_route_tail_small(const float *__restrict__ L, int T, int E,
                                                            int k, int renorm, int bm, int max_tiles,
                                                            RouteBufs o) {
   __shared__ __attribute__((aligned(16))) float Ls[kSmallTE];
   __shared__ int sel_id[kSmallT * kMaxTopK];
-  __shared__ float sel_v[kSmallT * kMaxTopK];
+  __shared__ float sel_w[kSmallT * kMaxTopK];
   __shared__ int cnt[kSmallE];
   __shared__ int offs[kSmallE];
+  __shared__ int wcnt[16][kSmallE];  // per wave: slots routed to each expert
   __shared__ int s_total;
   const int tid = threadIdx.x;
-  const int TE = T * E, R = T * k;
+  const int R = T * k;
   const int Ep = (E + 3) & ~3;  // LDS row stride: 16-byte rows, padded with -inf
   for (int i = tid; i < T * Ep; i += 1024) {
     const int t = i / Ep, f = i - t * Ep;
@@ -526,65 +550,77 @@ __global__ __launch_bounds__(1024) void k_route_tail_small(const float *__restri
   }
   for (int e = tid; e < E; e += 1024) cnt[e] = 0;
   __syncthreads();
-  for (int i = tid; i < TE; i += 1024) {
-    const int t = i / E, e = i - t * E;
-    const float *row = Ls + t * Ep;
-    const float v = row[e];
-    int rank = 0;
-    for (int f = 0; f < Ep; f += 4) {  // the lanes of a wave share the row: broadcast reads
-      const float4 u = *reinterpret_cast<const float4 *>(row + f);
-      rank += (u.x > v || (u.x == v && f < e)) ? 1 : 0;
-      rank += (u.y > v || (u.y == v && f + 1 < e)) ? 1 : 0;
-      rank += (u.z > v || (u.z == v && f + 2 < e)) ? 1 : 0;
-      rank += (u.w > v || (u.w == v && f + 3 < e)) ? 1 : 0;
-    }
-    if (rank < k) {
-      sel_id[t * k + rank] = e;
-      sel_v[t * k + rank] = v;
+  // top k of each token: one wave per token (wave_topk), weights included
+  {
+    const int wave = tid >> 6, lane = tid & 63;
+    for (int t = wave; t < T; t += 16) {
+      int my_id;
+      float wgt;
+      if (E <= 64)
+        wave_topk<1>(Ls + t * Ep, E, k, renorm, my_id, wgt);
+      else if (E <= 128)
+        wave_topk<2>(Ls + t * Ep, E, k, renorm, my_id, wgt);
+      else
+        wave_topk<4>(Ls + t * Ep, E, k, renorm, my_id, wgt);
+      if (lane < k) {
+        sel_id[t * k + lane] = my_id;
+        sel_w[t * k + lane] = wgt;
+      }
     }
   }
   __syncthreads();
   if (tid < R) {
-    // the denominator in the routing kernels' order: selected experts by rank,
-    // or every expert by id
-    const int t = tid / k;
-    const float v0 = sel_v[t * k];
-    float sum = 0.0f;
-    if (renorm) {
-      for (int q = 0; q < k; ++q) sum += expf(sel_v[t * k + q] - v0);
-    } else {
-      for (int f = 0; f < E; ++f) sum += expf(Ls[t * Ep + f] - v0);
-    }
     o.topk_ids[tid] = sel_id[tid];
-    o.topk_w[tid] = expf(sel_v[tid] - v0) / sum;
+    o.topk_w[tid] = sel_w[tid];
     atomicAdd(&cnt[sel_id[tid]], 1);
   }
+  // zero the per-wave expert counts of the stable ranking below
+  for (int i = tid; i < 16 * E; i += 1024) wcnt[i / E][i % E] = 0;
   __syncthreads();
+  // One scan gives each expert its first sorted row (11 bits: R <= 1024), its
+  // slot in the non-empty expert list (9 bits: E <= 256) and its first tile
+  // (11 bits: at most R + E tiles).
   const int c = tid < E ? cnt[tid] : 0;
-  const int ex = block_scan_1024(c, &s_total);
+  const int nt = (c + bm - 1) / bm;
+  const int ex = block_scan_1024(c | ((c > 0 ? 1 : 0) << 11) | (nt << 20), &s_total);
+  const int off = ex & 0x7ff, slot = (ex >> 11) & 0x1ff, tile0 = ex >> 20;
   if (tid < E) {
-    offs[tid] = ex;
-    o.expert_offsets[tid] = ex;
+    offs[tid] = off;
+    o.expert_offsets[tid] = off;
   }
-  if (tid == 0) o.expert_offsets[E] = R;
-  const int slot = block_scan_1024(c > 0 ? 1 : 0, &s_total);
+  if (tid == 0) {
+    o.expert_offsets[E] = R;
+    o.counters[0] = (s_total >> 11) & 0x1ff;
+    o.counters[1] = min(s_total >> 20, max_tiles);
+  }
   if (c > 0) {
     o.grp_expert[slot] = tid;
-    o.grp_row0[slot] = ex;
+    o.grp_row0[slot] = off;
     o.grp_rows[slot] = c;
+    for (int i = 0; i < nt && tile0 + i < max_tiles; ++i)
+      o.tiles[tile0 + i] = make_int4(tid, off + i * bm, min(bm, c - i * bm), c);
   }
-  if (tid == 0) o.counters[0] = s_total;
-  if (tid < R) {  // stable position: earlier slots routed to the same expert
-    const int e = sel_id[tid];
-    int rank = 0;
-    for (int q = 0; q < tid; ++q) rank += sel_id[q] == e ? 1 : 0;
-    const int pos = offs[e] + rank;
+  // Stable position of slot s among the slots routed to its expert: its rank
+  // among equal ids in its wave (one ballot per id bit) plus the counts of
+  // the earlier waves.
+  const int wave = tid >> 6;
+  const bool valid = tid < R;
+  const int e = valid ? sel_id[tid] : E;  // E: sentinel shared by the idle lanes
+  uint64_t m = ~0ull;
+  for (int bit = 0; bit < 9; ++bit) {
+    const int on = (e >> bit) & 1;
+    const uint64_t bal = __ballot(on);
+    m &= on ? bal : ~bal;
+  }
+  const int rank = __popcll(m & lanemask_lt());
+  if (valid && rank == 0) wcnt[wave][e] = __popcll(m);
+  __syncthreads();
+  if (valid) {
+    int pos = offs[e] + rank;
+    for (int w = 0; w < wave; ++w) pos += wcnt[w][e];
     o.sorted_slots[pos] = tid;
     o.slot_pos[tid] = pos;
   }
-  const int ngrp = s_total;
-  __syncthreads();
-  build_tiles(o.grp_expert, o.grp_row0, o.grp_rows, ngrp, bm, max_tiles, o.tiles, o.counters + 1);
 }
 
 hipError_t launch_route(const float *logits, int T, int E, int k, int renorm, const RouteBufs &rb,
