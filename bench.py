@@ -268,7 +268,7 @@ def main():
     flops = 6.0 * R * wl.H * wl.I
     ms = graph_ms if graph_ms is not None else eager_ms
     value = T / (ms * 1e-3)
-    small = (path == M.PATH_SMALL_M) or (path == M.PATH_AUTO and R <= 128 and max(wl.H, wl.I) <= 4096)
+    small = (path == M.PATH_SMALL_M) or (path == M.PATH_AUTO and R <= 64 and max(wl.H, wl.I) <= 4096)
     if small:
         gate_bytes = active * g_b
         roof = {"bound": "hbm", "achieved": gate_bytes / (gate_mean_ms * 1e-3) / 1e9,

@@ -36,7 +36,7 @@ int fmt_block(nf4moe_format_t f) { return fmt_nf4(f) ? 64 : 32; }
 bool fmt_ok(nf4moe_format_t f) { return fmt_nf4(f) || f == NF4MOE_FMT_MXFP4_B32; }
 int scale_align(nf4moe_format_t f) { return f == NF4MOE_FMT_NF4_B64 ? 4 : f == NF4MOE_FMT_NF4_B64_BF16ABS ? 2 : 1; }
 
-constexpr int kSmallR = 128;       // routed rows up to which AUTO picks the small-M kernels
+constexpr int kSmallR = 64;        // routed rows up to which AUTO picks the small-M kernels
 constexpr int kTokenCentricT = 2;  // tokens up to which the down projection is token-centric
 constexpr int64_t kSmallMaxK = 4096;
 

@@ -71,7 +71,7 @@ typedef enum {
 typedef enum { NF4MOE_DT_F32 = 0, NF4MOE_DT_BF16 = 1 } nf4moe_dtype_t;
 
 /* Which grouped-GEMM kernel family runs. AUTO picks from the routed row count
- * known on the host (R = T * top_k): R <= 128 (with H, I <= 4096) runs the
+ * known on the host (R = T * top_k): R <= 64 (with H, I <= 4096) runs the
  * bandwidth-bound decode kernels, larger R the MFMA kernels (with 64-row tiles
  * when the groups average at most 48 rows, else 128). The other values force one family (for
  * A/B measurement and tests); the result must satisfy the same tolerance. */
@@ -258,7 +258,7 @@ size_t nf4moe_workspace_bytes(const nf4moe_layer_t *layer, int32_t T_max);
  * layer's biases (see nf4moe_glu_t). Intermediates (h, partial products) stay
  * fp32; no bf16 expert weight is written anywhere.
  * Row-count invariance (the pages' STATUS page, kernel section): on the small-M
- * path (AUTO picks it for T * top_k <= 128) a token's outputs and routing carry
+ * path (AUTO picks it for T * top_k <= 64) a token's outputs and routing carry
  * the same bits whatever the other tokens of the call; on the MFMA path, among
  * calls of 33 tokens or more; across the two they differ in summation order.
  * Errors: INVALID_ARG (layer fields, sizes, pointers), WORKSPACE (ws_bytes <

@@ -81,8 +81,8 @@ def test_small_m_row_count_invariance(wl):
 
 @pytest.mark.parametrize("wl", CASES, ids=lambda w: w.name)
 def test_auto_decode_sizes_row_count_invariance(wl):
-    """AUTO picks the small-M path while T * top_k <= 128: every such T agrees."""
-    tmax = 128 // wl.top_k
+    """AUTO picks the small-M path while T * top_k <= 64: every such T agrees."""
+    tmax = 64 // wl.top_k
     _check_invariance(wl, M.PATH_AUTO, list(range(1, tmax)), [1, tmax - 1], tmax)
 
 
