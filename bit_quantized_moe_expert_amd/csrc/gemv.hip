@@ -722,12 +722,11 @@ __global__ __launch_bounds__(256) void k_down_combine(const float *__restrict__ 
   }
 }
 
-template <int FMT, int LPR, int NJ, int NP>
-static void launch_down_combine_t(const float *h, const int32_t *slot_pos, const int32_t *topk_ids,
-                                  const float *topk_w, int T, int k, const uint8_t *w2,
-                                  const void *w2_scale, const float *b2, int H, int I, uint16_t *out,
-                                  hipStream_t s) {
-  constexpr int RB = 8;
+template <int FMT, int LPR, int NJ, int NP, int RB>
+static void launch_down_combine_rb(const float *h, const int32_t *slot_pos, const int32_t *topk_ids,
+                                   const float *topk_w, int T, int k, const uint8_t *w2,
+                                   const void *w2_scale, const float *b2, int H, int I, uint16_t *out,
+                                   hipStream_t s) {
   const dim3 grid((unsigned)cdiv(H, RB), (unsigned)T);
   if (b2)
     hipLaunchKernelGGL((k_down_combine<FMT, LPR, NJ, NP, RB, 1>), grid, dim3(256), 0, s, h, slot_pos, topk_ids,
@@ -735,6 +734,25 @@ static void launch_down_combine_t(const float *h, const int32_t *slot_pos, const
   else
     hipLaunchKernelGGL((k_down_combine<FMT, LPR, NJ, NP, RB, 0>), grid, dim3(256), 0, s, h, slot_pos, topk_ids,
                        topk_w, T, k, w2, w2_scale, H, I, out, b2);
+}
+
+// Output rows per workgroup: the smallest of 4, 8, 12 that keeps the grid
+// within two workgroups per CU (T * H / RB <= 512): a one-token OLMoE- or
+// Qwen3-shaped layer (H = 2048) runs 512 workgroups of 4 rows, a gpt-oss-shaped
+// one (H = 2880) 360 of 8, two tokens 512 of 8 or 480 of 12. A row's arithmetic
+// does not depend on how many rows share its workgroup.
+template <int FMT, int LPR, int NJ, int NP>
+static void launch_down_combine_t(const float *h, const int32_t *slot_pos, const int32_t *topk_ids,
+                                  const float *topk_w, int T, int k, const uint8_t *w2,
+                                  const void *w2_scale, const float *b2, int H, int I, uint16_t *out,
+                                  hipStream_t s) {
+  constexpr int64_t kMaxWG = 512;
+  if ((int64_t)T * cdiv(H, 4) <= kMaxWG)
+    launch_down_combine_rb<FMT, LPR, NJ, NP, 4>(h, slot_pos, topk_ids, topk_w, T, k, w2, w2_scale, b2, H, I, out, s);
+  else if ((int64_t)T * cdiv(H, 8) <= kMaxWG)
+    launch_down_combine_rb<FMT, LPR, NJ, NP, 8>(h, slot_pos, topk_ids, topk_w, T, k, w2, w2_scale, b2, H, I, out, s);
+  else
+    launch_down_combine_rb<FMT, LPR, NJ, NP, 12>(h, slot_pos, topk_ids, topk_w, T, k, w2, w2_scale, b2, H, I, out, s);
 }
 
 // Lane-segment shape of the grouped GEMV for K = I (pick_shape's rule): LPR

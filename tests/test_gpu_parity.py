@@ -128,6 +128,26 @@ def test_route_permute_bitexact(T, E, k, renorm):
     _route_case(T, E, k, renorm, ties=True, seed=T * 3 + E)
 
 
+@pytest.mark.parametrize("T,E,k", [(5, 64, 8), (40, 128, 6), (3, 200, 4)])
+def test_route_permute_signed_zero_and_masked_experts(T, E, k):
+    """Logits equal as floats but not as bits (+0 / -0) tie and go to the lower
+    id; experts masked with -inf are picked last (lower id first among them)."""
+    rng = np.random.default_rng(T + E)
+    L = np.where(rng.random((T, E)) < 0.5, np.float32(0.0), np.float32(-0.0)).astype(np.float32)
+    L[:, 1::7] = np.float32(0.5)
+    L[:, 3::5] = -np.inf
+    L[0, :] = -np.inf
+    L[0, E - 1] = np.float32(-0.0)
+    got = M.route_permute(torch.from_numpy(L).to(DEV), k, 1)
+    torch.cuda.synchronize()
+    ids_o, w_o = O.topk_route(L.astype(np.float64), k, 1)
+    off_o, slots_o = O.permute(ids_o, E)
+    assert np.array_equal(got["topk_ids"].cpu().numpy(), ids_o)
+    assert np.array_equal(got["expert_offsets"].cpu().numpy(), off_o)
+    assert np.array_equal(got["sorted_slots"].cpu().numpy(), slots_o)
+    assert np.max(np.abs(got["topk_w"].cpu().numpy() - w_o)) <= 1e-6
+
+
 def test_route_permute_empty():
     got = M.route_permute(torch.zeros(0, 16, dtype=torch.float32, device=DEV), 2)
     assert np.array_equal(got["expert_offsets"].cpu().numpy(), np.zeros(17, np.int32))
