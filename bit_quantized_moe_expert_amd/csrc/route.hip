@@ -38,19 +38,20 @@ __global__ __launch_bounds__(256) void k_logits_rows(const uint16_t *__restrict_
   for (int h = threadIdx.x * 8; h < H; h += 256 * 8) {
     const float4 w0 = *reinterpret_cast<const float4 *>(w + h);
     const float4 w1 = *reinterpret_cast<const float4 *>(w + h + 4);
-    // Tokens in batches of 8: the batch's loads (clamped to a valid row, no
-    // branch) are all issued before the first is used.
+    // Tokens in batches of up to 8: the batch's loads (clamped to a valid row,
+    // no branch) are all issued before the first is used.
+    constexpr int BT = TMAX < 8 ? TMAX : 8;
 #pragma unroll
-    for (int t0 = 0; t0 < TMAX; t0 += 8) {
+    for (int t0 = 0; t0 < TMAX; t0 += BT) {
       if (t0 >= T) break;  // uniform
-      uint4 xv[8];
+      uint4 xv[BT];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
+      for (int i = 0; i < BT; ++i) {
         const int t = t0 + i < T ? t0 + i : 0;
         xv[i] = *reinterpret_cast<const uint4 *>(x + (int64_t)t * H + h);
       }
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
+      for (int i = 0; i < BT; ++i) {
         float a = acc[t0 + i];
         a = fmaf(bf16lo_to_f32(xv[i].x), w0.x, a);
         a = fmaf(bf16hi_to_f32(xv[i].x), w0.y, a);
@@ -237,7 +238,9 @@ __global__ __launch_bounds__(256) void k_logits_tiled(const uint16_t *__restrict
 hipError_t launch_router_logits(const uint16_t *x, int T, int H, const float *W, const float *b,
                                 int E, float *logits, void *split_ws, hipStream_t s, bool rows_only) {
   if (T <= 0) return hipSuccess;
-  if (rows_only) {  // the per-token order of k_logits_rows for every T
+  if (T == 1) {  // one token: no idle token slots (the same per-token order)
+    hipLaunchKernelGGL(k_logits_rows<1>, dim3(E), dim3(256), 0, s, x, T, H, W, b, E, logits);
+  } else if (rows_only) {  // the per-token order of k_logits_rows for every T
     if (T <= 8)
       hipLaunchKernelGGL(k_logits_rows<8>, dim3(E), dim3(256), 0, s, x, T, H, W, b, E, logits);
     else
