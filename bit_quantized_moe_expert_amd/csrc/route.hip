@@ -241,7 +241,11 @@ hipError_t launch_router_logits(const uint16_t *x, int T, int H, const float *W,
   if (T == 1) {  // one token: no idle token slots (the same per-token order)
     hipLaunchKernelGGL(k_logits_rows<1>, dim3(E), dim3(256), 0, s, x, T, H, W, b, E, logits);
   } else if (rows_only) {  // the per-token order of k_logits_rows for every T
-    if (T <= 8)
+    if (T <= 2)
+      hipLaunchKernelGGL(k_logits_rows<2>, dim3(E), dim3(256), 0, s, x, T, H, W, b, E, logits);
+    else if (T <= 4)
+      hipLaunchKernelGGL(k_logits_rows<4>, dim3(E), dim3(256), 0, s, x, T, H, W, b, E, logits);
+    else if (T <= 8)
       hipLaunchKernelGGL(k_logits_rows<8>, dim3(E), dim3(256), 0, s, x, T, H, W, b, E, logits);
     else
       hipLaunchKernelGGL(k_logits_rows<32>, dim3(E, (unsigned)cdiv(T, 32)), dim3(256), 0, s, x, T, H, W,
