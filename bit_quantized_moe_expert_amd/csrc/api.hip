@@ -37,7 +37,12 @@ bool fmt_ok(nf4moe_format_t f) { return fmt_nf4(f) || f == NF4MOE_FMT_MXFP4_B32;
 int scale_align(nf4moe_format_t f) { return f == NF4MOE_FMT_NF4_B64 ? 4 : f == NF4MOE_FMT_NF4_B64_BF16ABS ? 2 : 1; }
 
 constexpr int kSmallR = 64;        // routed rows up to which AUTO picks the small-M kernels
-constexpr int kTokenCentricT = 2;  // tokens up to which the down projection is token-centric
+// Tokens up to which the small-M path's down projection is token-centric (fused
+// with the combine: no slot buffer, no combine launch). Each token re-reads the
+// weights of its experts, which pays at these sizes: same box, against the
+// grouped GEMV + combine, OLMoE-shaped T = 4 / 8 48.5 / 70.6 -> 44.9 / 67.1 us,
+// Qwen3-shaped T = 8 64.0 -> 58.2 us, gpt-oss-shaped T = 16 423.6 -> 419.2 us.
+constexpr int kTokenCentricT = 32;
 
 // Activation rows the grouped GEMV applies per weight pass, from the average
 // rows per group: 1 up to 2 (the usual decode batch: one or two rows per

@@ -747,7 +747,7 @@ static void launch_down_combine_rb(const float *h, const int32_t *slot_pos, cons
 // Output rows per workgroup: the smallest of 4, 8, 12 that keeps the grid
 // within two workgroups per CU (T * H / RB <= 512): a one-token OLMoE- or
 // Qwen3-shaped layer (H = 2048) runs 512 workgroups of 4 rows, a gpt-oss-shaped
-// one (H = 2880) 360 of 8, two tokens 512 of 8 or 480 of 12. A row's arithmetic
+// one (H = 2880) 360 of 8, two tokens 512 of 8 or 480 of 12, more tokens 12. A row's arithmetic
 // does not depend on how many rows share its workgroup.
 template <int FMT, int LPR, int NJ, int NP>
 static void launch_down_combine_t(const float *h, const int32_t *slot_pos, const int32_t *topk_ids,
