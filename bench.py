@@ -94,6 +94,25 @@ def measured_traffic(workload, kind):
     return float(rec["hbm_bytes_per_launch"])
 
 
+def spin_cycles_for(seconds, stream):
+    """Cycles of torch.cuda._sleep's spin kernel that last about `seconds` on
+    this GPU: the counter's rate from two spins of different lengths (their
+    difference cancels the launch overhead), after one call that loads the
+    kernel."""
+    import torch
+    torch.cuda._sleep(1 << 10)
+    lens, secs = (1 << 20, 1 << 23), []
+    for c in lens:
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        torch.cuda._sleep(c)
+        b.record(stream)
+        torch.cuda.synchronize()
+        secs.append(a.elapsed_time(b) * 1e-3)
+    rate = (lens[1] - lens[0]) / max(secs[1] - secs[0], 1e-6)  # cycles per second
+    return int(min(max(seconds, 0.001), 1.0) * rate)
+
+
 def workload(args):
     import moe_synth as S
     wl = S.WORKLOADS[args.workload]
@@ -242,10 +261,25 @@ def main():
         for ev in row:
             ev.record(stream)
     torch.cuda.synchronize()
+    # The host records the events and launches of a profiled step in about
+    # 0.1 ms (0.3 ms allowed below); shorter steps are queued behind a spin kernel, so that the stream
+    # runs them back to back, as in the timed loops, instead of each starting on
+    # an idle GPU.
+    step_ms = graph_ms if graph_ms is not None else eager_ms
+    spin_ev = None
+    if step_ms < 0.2:
+        spin = spin_cycles_for(0.0003 * prof_steps + 0.02, stream)
+        spin_ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+        spin_ev[0].record(stream)
+        torch.cuda._sleep(spin)
+        spin_ev[1].record(stream)
+    t_enq = time.perf_counter()
     for i in range(prof_steps):
         fwd.set_layer(layers[i % nlayers])
         fwd.profiled(xs[i % nlayers], out, [ev.cuda_event for ev in evs[i]])
+    enqueue_ms = (time.perf_counter() - t_enq) * 1e3
     torch.cuda.synchronize()
+    spin_ms = spin_ev[0].elapsed_time(spin_ev[1]) if spin_ev is not None else None
     stage = np.array([[r[0].elapsed_time(r[1]), r[1].elapsed_time(r[2]), r[2].elapsed_time(r[3])]
                       for r in evs])
     route_ms, gate_ms, down_ms = (float(v) for v in np.median(stage, axis=0))
@@ -282,6 +316,8 @@ def main():
     roof["traffic"] = measured_traffic(wl.name if T == wl.tokens[0] else f"{wl.name}_T{T}", kind)
     roof["kernel"] = "k_gemv<SwiGLU> (gate_up)" if small else "k_mfma<SwiGLU> (gate_up)"
     roof["kernel_ms_mean"] = gate_mean_ms
+    roof["kernel_timing"] = {"launches": prof_steps, "queued_behind_spin_ms": spin_ms,
+                             "host_enqueue_ms": enqueue_ms}
     roof["kernel_source_hash"] = kernel_source_hash(kind)
 
     # ---- CPU baseline: the fp64 oracle on a bounded sample of the same workload
