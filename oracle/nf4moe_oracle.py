@@ -17,7 +17,7 @@ Every floating-point step here is fp64 unless a step's definition fixes fp32:
 the stored absmax (fp32), the decoded weight (one fp32 product) and the e8m0
 scale (a power of two).
 
-Readings of points the pages leave open (each listed in the design doc):
+Readings of points the pages leave open:
   * NF4 codebook values: the pages name the bitsandbytes 16-entry NormalFloat
     codebook but never print it. We build it with the published QLoRA
     construction (normal quantiles with offset 0.9677083, 8 positive, 7
