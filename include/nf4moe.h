@@ -52,7 +52,7 @@ extern "C" {
 typedef enum {
   NF4MOE_OK = 0,
   NF4MOE_ERR_INVALID_ARG = 1, /* bad size, null or misaligned pointer, bad enum */
-  NF4MOE_ERR_UNSUPPORTED = 2, /* valid request outside what this build supports */
+  NF4MOE_ERR_UNSUPPORTED = 2, /* valid request outside what this library supports */
   NF4MOE_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required     */
   NF4MOE_ERR_HIP = 4          /* a HIP runtime call failed (launch, device query) */
 } nf4moe_status_t;

@@ -274,7 +274,7 @@ def router_logits(x_bits: np.ndarray, router_w: np.ndarray, router_b=None) -> np
 
     The router stays outside the kernel on the pages (page "How do I run a
     grouped GEMM ...", section "Why it happens": sorting tokens by expert and
-    scattering back are outside the kernel); this build moves it in. Config
+    scattering back are outside the kernel); this library moves it in. Config
     text: softmax, then top-k, renormalised.
     """
     x = bf16_bits_to_f64(x_bits)

@@ -423,7 +423,7 @@ def test_gate_up_halves_matter():
 
 # ----------------------------------------------------------------------------
 # The gpt-oss expert form (experts4bit-qlora page, "Scope": per-expert biases and
-# a clamped-GLU epilogue; the formula is this build's reading, a parameterised
+# a clamped-GLU epilogue; the formula is this library's reading, a parameterised
 # clamp of the gate and up values around a GLU with sigmoid(alpha * g)).
 def test_clamped_glu_special_values():
     a, lim = 1.702, 7.0
