@@ -61,7 +61,7 @@ __all__ = [
     "nf4_codebook", "e2m1_values",
     "nf4_quantize", "nf4_dequantize", "mxfp4_quantize", "mxfp4_dequantize",
     "quantize", "dequantize", "block_size",
-    "bf16_bits_to_f64", "router_logits", "topk_route", "topk_gap", "permute",
+    "bf16_bits_to_f64", "router_logits", "topk_route", "permute",
     "grouped_gemm", "grouped_dgrad", "swiglu", "clamped_glu", "GLU_SWIGLU", "GLU_CLAMPED",
     "moe_forward", "rel_err",
 ]
@@ -310,14 +310,6 @@ def topk_route(logits: np.ndarray, top_k: int, renormalize: bool = True):
             full = np.exp(L[t] - m)
             w[t] = full[order] / full.sum()
     return ids, w
-
-
-def topk_gap(logits: np.ndarray, top_k: int) -> np.ndarray:
-    """Per token: (k-th largest logit) - ((k+1)-th largest), +inf when k == E."""
-    L = np.sort(np.asarray(logits, dtype=np.float64), axis=1)[:, ::-1]
-    if top_k >= L.shape[1]:
-        return np.full(L.shape[0], np.inf)
-    return L[:, top_k - 1] - L[:, top_k]
 
 
 def permute(topk_ids: np.ndarray, E: int):

@@ -350,18 +350,29 @@ def test_swiglu_closed_forms():
     assert abs(h[3] - 60.0) < 1e-9
 
 
-def _forward_py(layer, xb):
-    """Pure-Python forward on tiny shapes: loops, math.exp, no numpy algebra."""
+def _forward_py(layer, xb, forced=None):
+    """Pure-Python forward on tiny shapes: loops, math.exp, no numpy algebra.
+    forced: optional [T, k] expert ids used in place of the top-k selection;
+    the routing weights are then the softmax over those ids' logits
+    (renormalize = 1) or the full softmax at those ids (renormalize = 0)."""
     fmt, E, H, I, k = layer["fmt"], layer["E"], layer["H"], layer["I"], layer["top_k"]
+    renorm = bool(layer.get("renormalize", 1))
     W13 = [_deq_py(fmt, layer["w13"][e], layer["w13_scale"][e], 2 * I, H) for e in range(E)]
     W2 = [_deq_py(fmt, layer["w2"][e], layer["w2_scale"][e], H, I) for e in range(E)]
     out = []
     for t in range(xb.shape[0]):
         x = [float(np.array([int(v) << 16], np.uint32).view(np.float32)[0]) for v in xb[t]]
         L = [math.fsum(x[h] * float(layer["router_w"][e, h]) for h in range(H)) for e in range(E)]
-        order = sorted(range(E), key=lambda e: (-L[e], e))[:k]
-        ex = [math.exp(L[e] - L[order[0]]) for e in order]
-        ws = [v / math.fsum(ex) for v in ex]
+        if forced is None:
+            order = sorted(range(E), key=lambda e: (-L[e], e))[:k]
+        else:
+            order = [int(e) for e in forced[t]]
+        if renorm:
+            ex = [math.exp(L[e]) for e in order]
+            ws = [v / math.fsum(ex) for v in ex]
+        else:
+            den = math.fsum(math.exp(L[e]) for e in range(E))
+            ws = [math.exp(L[e]) / den for e in order]
         o = [0.0] * H
         for wj, e in zip(ws, order):
             gu = [math.fsum(x[h] * W13[e][n][h] for h in range(H)) for n in range(2 * I)]
@@ -386,6 +397,73 @@ def test_moe_forward_bruteforce(fmt):
     out = O.moe_forward(layer, xb)
     ref = _forward_py(layer, xb)
     assert np.allclose(out, ref, rtol=1e-10, atol=1e-14)
+
+
+def _tiny_layer(fmt, E, k, renorm, wid):
+    wl = S.custom(E=E, top_k=k, H=64, I=64, fmt=fmt, wid=wid, renormalize=renorm)
+    W_r, _ = S.make_router(wl)
+    w13 = S.make_stack(wl, 0, "w13"); w2 = S.make_stack(wl, 0, "w2")
+    q13 = [O.quantize(fmt, w13[e]) for e in range(E)]
+    q2 = [O.quantize(fmt, w2[e]) for e in range(E)]
+    layer = dict(fmt=fmt, E=E, H=64, I=64, top_k=k, renormalize=renorm, router_w=W_r, router_b=None,
+                 w13=np.stack([q[0] for q in q13]), w13_scale=np.stack([q[1] for q in q13]),
+                 w2=np.stack([q[0] for q in q2]), w2_scale=np.stack([q[1] for q in q2]))
+    return wl, layer
+
+
+# The forward with given expert ids (topk_ids_override) is how every GPU parity
+# test and the smoke check call the oracle: the GPU's fp32 selection is handed
+# in, and the oracle recomputes the routing weights from its own fp64 logits.
+@pytest.mark.parametrize("renorm", [1, 0])
+def test_override_with_own_selection_is_the_default_path(renorm):
+    """Handing the oracle its own top-k ids reproduces the default forward bit
+    for bit (catches an override branch whose weights use another formula or
+    normaliser than the default selection's, e.g. a renormalised softmax when
+    renormalize = 0)."""
+    wl, layer = _tiny_layer(O.FMT_NF4, 6, 3, renorm, wid=81)
+    xb = S.make_x(wl, 5)
+    out, inner = O.moe_forward(layer, xb, return_all=True)
+    out2, inner2 = O.moe_forward(layer, xb, topk_ids_override=inner["topk_ids"], return_all=True)
+    assert np.array_equal(out, out2)
+    assert np.array_equal(inner["topk_w"], inner2["topk_w"])
+
+
+@pytest.mark.parametrize("renorm", [1, 0])
+def test_override_order_within_a_token_does_not_matter(renorm):
+    """The layer output is a weighted sum over the selected set: listing the
+    same ids in another order gives the same output (catches weights that stay
+    attached to a slot position instead of to their expert, e.g. a weight
+    vector not permuted with the ids)."""
+    wl, layer = _tiny_layer(O.FMT_MXFP4, 6, 3, renorm, wid=82)
+    xb = S.make_x(wl, 4)
+    _, inner = O.moe_forward(layer, xb, return_all=True)
+    ids = inner["topk_ids"]
+    rev = np.ascontiguousarray(ids[:, ::-1])
+    rot = np.ascontiguousarray(np.roll(ids, 1, axis=1))
+    a = O.moe_forward(layer, xb, topk_ids_override=ids)
+    for other in (rev, rot):
+        b = O.moe_forward(layer, xb, topk_ids_override=other)
+        assert np.allclose(a, b, rtol=1e-13, atol=1e-15 * np.abs(a).max())
+
+
+@pytest.mark.parametrize("fmt,renorm", [(O.FMT_NF4, 1), (O.FMT_MXFP4, 0)])
+def test_override_forced_selection_matches_bruteforce(fmt, renorm):
+    """A forced selection that is not the top-k (the lowest logits, and a
+    mixed one, in non-descending order) against the pure-Python forward given
+    the same ids (catches a wrong weight order, a wrong softmax base or sum, or
+    weights taken from the wrong experts)."""
+    E, k = 5, 2
+    wl, layer = _tiny_layer(fmt, E, k, renorm, wid=83)
+    xb = S.make_x(wl, 3)
+    L = O.router_logits(xb, layer["router_w"])
+    forced = np.empty((3, k), np.int32)
+    for t in range(3):
+        asc = sorted(range(E), key=lambda e: (L[t, e], e))
+        forced[t] = [asc[0], asc[2]] if t != 1 else [asc[3], asc[0]]
+    out = O.moe_forward(layer, xb, topk_ids_override=forced)
+    ref = _forward_py(layer, xb, forced=forced)
+    assert np.allclose(out, ref, rtol=1e-10, atol=1e-14)
+    assert not np.allclose(out, O.moe_forward(layer, xb))        # the forcing took effect
 
 
 def test_moe_forward_single_expert_k1_closed_form():
