@@ -136,6 +136,21 @@ def _dev(t, name, dtype=None):
     return t
 
 
+def _shape(t, name, shape):
+    """Refuse a tensor whose shape is not `shape` (None entries match any size).
+    The C ABI sees raw pointers only, so every size it is told must match the
+    buffer; this runs before the device check."""
+    torch = _torch()
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    got = tuple(t.shape)
+    if len(got) != len(shape) or any(w is not None and g != w for g, w in zip(got, shape)):
+        want = "(" + ", ".join("*" if w is None else str(w) for w in shape) + ")"
+        raise ValueError(f"{name} has shape {got}, expected {want}")
+
+
 def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
@@ -171,6 +186,11 @@ def quantize(w, fmt: int = FMT_NF4):
 def dequantize(packed, scale, K: int, fmt: int = FMT_NF4):
     """(packed [..., K/2], scale) -> fp32 [..., K] (device)."""
     torch = _torch()
+    if K <= 0 or K % BLOCK[fmt]:
+        raise ValueError(f"K={K} must be a positive multiple of {BLOCK[fmt]}")
+    lead = tuple(packed.shape[:-1])
+    _shape(packed, "packed", lead + (K // 2,))
+    _shape(scale, "scale", lead + (K // BLOCK[fmt],))
     _dev(packed, "packed", torch.uint8)
     _dev(scale, "scale", _scale_dtype(fmt))
     rows = packed.numel() // (K // 2)
@@ -196,12 +216,15 @@ def router_logits(x, router_w, router_b=None, matrix_cores: bool = True):
     matrix_cores: hand the library the workspace that enables its MFMA kernel
     (used for T > 32, H % 32 == 0); False keeps the vector-ALU kernels."""
     torch = _torch()
+    _shape(x, "x", (None, None))
+    T, H = x.shape
+    _shape(router_w, "router_w", (None, H))
+    E = router_w.shape[0]
+    _shape(router_b, "router_b", (E,))
     _dev(x, "x", torch.bfloat16)
     _dev(router_w, "router_w", torch.float32)
     if router_b is not None:
         _dev(router_b, "router_b", torch.float32)
-    T, H = x.shape
-    E = router_w.shape[0]
     out = torch.empty(T, E, dtype=torch.float32, device=x.device)
     ws, nb = None, 0
     if matrix_cores:
@@ -215,6 +238,7 @@ def router_logits(x, router_w, router_b=None, matrix_cores: bool = True):
 def route_permute(logits, top_k: int, renormalize: bool = True):
     """logits fp32 [T, E] -> dict(topk_ids, topk_w, expert_offsets, sorted_slots)."""
     torch = _torch()
+    _shape(logits, "logits", (None, None))
     _dev(logits, "logits", torch.float32)
     T, E = logits.shape
     dev = logits.device
@@ -237,6 +261,18 @@ def grouped_gemm(a, B, B_scale, group_offsets, K: int, R: int, group_experts=Non
     Returns c [R, N] (fp32 or bf16)."""
     torch = _torch()
     out_dtype = out_dtype or torch.float32
+    if K <= 0 or K % BLOCK[fmt]:
+        raise ValueError(f"K={K} must be a positive multiple of {BLOCK[fmt]}")
+    _shape(B, "B", (None, None, K // 2))
+    E, N = B.shape[0], B.shape[1]
+    _shape(B_scale, "B_scale", (E, N, K // BLOCK[fmt]))
+    _shape(a, "a", (None, K))
+    _shape(group_offsets, "group_offsets", (None,))
+    G = group_offsets.numel() - 1
+    _shape(group_experts, "group_experts", (G,))
+    _shape(a_row_of, "a_row_of", (R,))
+    if a_row_of is None and a.shape[0] < R:
+        raise ValueError(f"a has {a.shape[0]} rows, fewer than R={R} (and no a_row_of gather)")
     _dev(a, "a", torch.bfloat16)
     _dev(B, "B", torch.uint8)
     _dev(B_scale, "B_scale", _scale_dtype(fmt))
@@ -245,8 +281,6 @@ def grouped_gemm(a, B, B_scale, group_offsets, K: int, R: int, group_experts=Non
         _dev(group_experts, "group_experts", torch.int32)
     if a_row_of is not None:
         _dev(a_row_of, "a_row_of", torch.int32)
-    E, N = B.shape[0], B.shape[1]
-    G = group_offsets.numel() - 1
     c = torch.empty(R, N, dtype=out_dtype, device=a.device)
     need = lib().nf4moe_gemm_workspace_bytes(G, R)
     ws, wsp, nb = _workspace(need, a.device)
@@ -264,15 +298,22 @@ def grouped_dgrad(dc, B, B_scale, group_offsets, K: int, group_experts=None, fmt
     order; B [E, N, K/2] u8; group_offsets int32 [G+1] (device). Returns da [R, K]."""
     torch = _torch()
     out_dtype = out_dtype or torch.float32
+    if K <= 0 or K % BLOCK[fmt]:
+        raise ValueError(f"K={K} must be a positive multiple of {BLOCK[fmt]}")
+    _shape(B, "B", (None, None, K // 2))
+    E, N = B.shape[0], B.shape[1]
+    _shape(B_scale, "B_scale", (E, N, K // BLOCK[fmt]))
+    _shape(dc, "dc", (None, N))
+    R = dc.shape[0]
+    _shape(group_offsets, "group_offsets", (None,))
+    G = group_offsets.numel() - 1
+    _shape(group_experts, "group_experts", (G,))
     _dev(dc, "dc", torch.bfloat16)
     _dev(B, "B", torch.uint8)
     _dev(B_scale, "B_scale", _scale_dtype(fmt))
     _dev(group_offsets, "group_offsets", torch.int32)
     if group_experts is not None:
         _dev(group_experts, "group_experts", torch.int32)
-    R, N = dc.shape
-    E = B.shape[0]
-    G = group_offsets.numel() - 1
     da = torch.empty(R, K, dtype=out_dtype, device=dc.device)
     need = lib().nf4moe_gemm_workspace_bytes(G, R)
     ws, wsp, nb = _workspace(need, dc.device)
@@ -311,8 +352,26 @@ class MoELayer:
     b13: object = None
     b2: object = None
 
+    def check_shapes(self):
+        """Refuse tensors whose shapes do not match (E, H, I) and the format."""
+        if self.fmt not in BLOCK:
+            raise ValueError(f"unknown format {self.fmt}")
+        blk = BLOCK[self.fmt]
+        E, H, I = self.E, self.H, self.I
+        if E < 1 or H <= 0 or I <= 0 or H % 64 or I % blk:
+            raise ValueError(f"E={E}, H={H}, I={I}: need E >= 1, H % 64 == 0, I % {blk} == 0")
+        _shape(self.w13, "w13", (E, 2 * I, H // 2))
+        _shape(self.w13_scale, "w13_scale", (E, 2 * I, H // blk))
+        _shape(self.w2, "w2", (E, H, I // 2))
+        _shape(self.w2_scale, "w2_scale", (E, H, I // blk))
+        _shape(self.router_w, "router_w", (E, H))
+        _shape(self.router_b, "router_b", (E,))
+        _shape(self.b13, "b13", (E, 2 * I))
+        _shape(self.b2, "b2", (E, H))
+
     def struct(self) -> Layer:
         torch = _torch()
+        self.check_shapes()
         sd = _scale_dtype(self.fmt)
         _dev(self.w13, "w13", torch.uint8)
         _dev(self.w2, "w2", torch.uint8)
@@ -353,12 +412,18 @@ class Forward:
 
     def __call__(self, x, out=None, topk_ids=None, topk_w=None):
         torch = _torch()
+        check_forward_args(self.layer, x, out, topk_ids, topk_w)
         _dev(x, "x", torch.bfloat16)
         T = x.shape[0]
         if T > self.T_max:
             raise ValueError(f"T={T} > T_max={self.T_max}")
         if out is None:
             out = torch.empty(T, self.layer.H, dtype=torch.bfloat16, device=x.device)
+        _dev(out, "out", torch.bfloat16)
+        if topk_ids is not None:
+            _dev(topk_ids, "topk_ids", torch.int32)
+        if topk_w is not None:
+            _dev(topk_w, "topk_w", torch.float32)
         _check(lib().nf4moe_moe_forward(ctypes.byref(self.st), _ptr(x), T, _ptr(out), _ptr(topk_ids),
                                         _ptr(topk_w), self.wsp, self.nb, _stream()))
         return out
@@ -367,12 +432,27 @@ class Forward:
     def profiled(self, x, out, events):
         """Same computation with 6 caller HIP event handles: [0..3] recorded between
         stages, [4], [5] the gate_up kernel's own start and end."""
+        torch = _torch()
         if len(events) != 6:
             raise ValueError("profiled() takes 6 events")
+        check_forward_args(self.layer, x, out, None, None)
+        _dev(x, "x", torch.bfloat16)
+        _dev(out, "out", torch.bfloat16)
+        if x.shape[0] > self.T_max:
+            raise ValueError(f"T={x.shape[0]} > T_max={self.T_max}")
         arr = (ctypes.c_void_p * 6)(*events)
         _check(lib().nf4moe_moe_forward_profiled(ctypes.byref(self.st), _ptr(x), x.shape[0], _ptr(out),
                                                  self.wsp, self.nb, _stream(), arr))
         return out
+
+
+def check_forward_args(layer: MoELayer, x, out=None, topk_ids=None, topk_w=None):
+    """Shapes of a forward call: x [T, H]; out [T, H]; topk_ids / topk_w [T, top_k]."""
+    _shape(x, "x", (None, layer.H))
+    T = x.shape[0]
+    _shape(out, "out", (T, layer.H))
+    _shape(topk_ids, "topk_ids", (T, layer.top_k))
+    _shape(topk_w, "topk_w", (T, layer.top_k))
 
 
 def moe_forward(layer: MoELayer, x, return_routing: bool = False):

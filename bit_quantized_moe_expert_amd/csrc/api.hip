@@ -319,8 +319,9 @@ nf4moe_status_t nf4moe_grouped_gemm(nf4moe_format_t fmt, const uint16_t *a, cons
   if (E < 1) return fail(NF4MOE_ERR_INVALID_ARG, "E=%d must be positive", E);
   if (G < 1 || G > 65536) return fail(NF4MOE_ERR_INVALID_ARG, "G=%d outside 1..65536", G);
   if (R < 0) return fail(NF4MOE_ERR_INVALID_ARG, "R=%d < 0", R);
-  if (a_rows < 0 || (!a_row_of && a_rows < R))
-    return fail(NF4MOE_ERR_INVALID_ARG, "a_rows=%d too small for R=%d without a gather", a_rows, R);
+  if (a_rows < 0 || (!a_row_of && a_rows < R) || (R > 0 && a_rows < 1))
+    return fail(NF4MOE_ERR_INVALID_ARG, "a_rows=%d too small for R=%d%s", a_rows, R,
+                a_row_of ? "" : " without a gather");
   if (c_dtype != NF4MOE_DT_F32 && c_dtype != NF4MOE_DT_BF16)
     return fail(NF4MOE_ERR_INVALID_ARG, "unknown output dtype %d", (int)c_dtype);
   if (path < NF4MOE_PATH_AUTO || path > NF4MOE_PATH_MFMA)
@@ -354,6 +355,7 @@ nf4moe_status_t nf4moe_grouped_gemm(nf4moe_format_t fmt, const uint16_t *a, cons
   g.a = a;
   g.a_is_f32 = 0;
   g.a_row_of = a_row_of;
+  g.a_rows = a_rows;
   g.B = B;
   g.B_scale = B_scale;
   g.N = N;
@@ -482,6 +484,7 @@ static nf4moe_status_t forward_impl(const nf4moe_layer_t *layer, const uint16_t 
   g.a_is_f32 = 0;
   g.a_row_of = fc.rb.sorted_slots;
   g.a_div = L.top_k;
+  g.a_rows = T;
   g.B = L.w13;
   g.B_scale = L.w13_scale;
   g.N = 2 * (int64_t)L.I;
@@ -534,6 +537,7 @@ static nf4moe_status_t forward_impl(const nf4moe_layer_t *layer, const uint16_t 
     d.c_split = 0;
     d.a_row_of = nullptr;
     d.a_div = 1;
+    d.a_rows = rp.R;
     d.B = L.w2;
     d.B_scale = L.w2_scale;
     d.N = L.H;

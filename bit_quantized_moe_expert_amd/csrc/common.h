@@ -95,6 +95,17 @@ __device__ inline uint32_t f32_to_bf16_rne(float f) {
   return u >> 16;
 }
 
+// Order-preserving 32-bit key of a float for the routing order (logit
+// descending, expert id ascending): larger float -> larger key; -0 is folded
+// onto +0 first, so floats that compare equal get equal keys. Every float has
+// a key, NaN included (a positive NaN above +inf, a negative one below -inf),
+// so ranking on (key, id) is a total order and always selects exactly k
+// experts, whatever the logits hold.
+__device__ inline uint32_t float_order_key(float v) {
+  const uint32_t b = __float_as_uint(v + 0.0f);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
 // Codebook value of a 4-bit code computed with a select tree on literals, so a
 // table build touches no memory.
 __device__ inline float nf4_value_sel(uint32_t c) {

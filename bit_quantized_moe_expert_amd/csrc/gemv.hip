@@ -110,7 +110,9 @@ constexpr int gemv_wave_loads() {
 
 // Routing of a single token inside the gate_up kernel, spread over the
 // kGemvWaves waves of a workgroup. Rank of expert e under (logit descending,
-// id ascending) = number of experts f ordered before it; wave w counts the f in
+// id ascending), compared on float_order_key so that the order is total for
+// any logits (NaN included) and the ranks of the E experts are a permutation
+// of 0..E-1 = number of experts f ordered before it; wave w counts the f in
 // its slice of E / kGemvWaves ids (route_partial), the partial counts meet in
 // LDS across the workgroup barrier, and route_finish sums them, selects the k
 // experts, and returns the expert of group `gi` (the gi-th selected id in
@@ -143,6 +145,7 @@ __device__ inline void route_partial(const GemmArgs &p, const RouteToken<EPL> &r
   const int lane = threadIdx.x & 63;
   const int E = p.route_E;
   int cnt[EPL];
+  uint32_t kv[EPL];
 #pragma unroll
   for (int j = 0; j < EPL; ++j) cnt[j] = 0;
   float uu[S];
@@ -152,13 +155,16 @@ __device__ inline void route_partial(const GemmArgs &p, const RouteToken<EPL> &r
     uu[i] = p.route_logits[f < E ? f : E - 1];
   }
 #pragma unroll
+  for (int j = 0; j < EPL; ++j) kv[j] = max(float_order_key(r.v[j]), 1u);  // as wave_topk
+#pragma unroll
   for (int i = 0; i < S; ++i) {
     const int f = wave * S + i;
-    const float u = f < E ? uu[i] : -__builtin_inff();
+    if (f >= E) continue;                           // wave-uniform: ids past E count for no one
+    const uint32_t ku = max(float_order_key(uu[i]), 1u);
 #pragma unroll
     for (int j = 0; j < EPL; ++j) {
       const int e = lane + 64 * j;
-      cnt[j] += (u > r.v[j] || (u == r.v[j] && f < e)) ? 1 : 0;
+      cnt[j] += (ku > kv[j] || (ku == kv[j] && f < e)) ? 1 : 0;
     }
   }
 #pragma unroll
@@ -319,7 +325,10 @@ __global__ __launch_bounds__(gemv_waves<ROUTE>() * 64) void k_gemv(GemmArgs p) {
       const bool live = (m0 + m) < rows;
       const int r = row0 + (live ? m0 + m : 0);
       int64_t arow = ROUTE > 0 ? 0 : r;
-      if (ROUTE == 0 && p.a_row_of) arow = p.a_row_of[r] / p.a_div;
+      if (ROUTE == 0 && p.a_row_of) {                // a bad index cannot read past a
+        arow = p.a_row_of[r] / p.a_div;
+        arow = arow < 0 ? 0 : (arow < p.a_rows ? arow : p.a_rows - 1);
+      }
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
         const int64_t c = li + (int64_t)LPR * j;

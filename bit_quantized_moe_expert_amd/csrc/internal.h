@@ -62,6 +62,7 @@ struct GemmArgs {
   int a_is_f32;             //   (bf16 hi, bf16 lo) pairs [*, K] (2: MFMA path only)
   const int32_t *a_row_of;  // row r reads a[a_row_of[r]] or, with a_div > 1, a[a_row_of[r] / a_div]
   int a_div;
+  int a_rows;               // rows of a: a gathered row index is clamped into [0, a_rows)
   const uint8_t *B;         // [E, N, K/2]
   const void *B_scale;
   int64_t N, K;             // N = weight rows (2I for SwiGLU), K

@@ -141,6 +141,7 @@ __global__ __launch_bounds__(512) void k_mfma(GemmArgs p, int ntn, int per) {
   {
     const int r = trow0 + (arow_ok ? am : 0);
     arow = p.a_row_of ? (int64_t)(p.a_row_of[r] / p.a_div) : (int64_t)r;
+    arow = arow < 0 ? 0 : (arow < p.a_rows ? arow : p.a_rows - 1);  // a bad index cannot read past a
   }
   constexpr int AW = EPT * (AF32 ? 4 : 2) / 16;       // 16-byte words per thread
   uint4 areg[AW];

@@ -277,12 +277,7 @@ hipError_t launch_router_logits(const uint16_t *x, int T, int H, const float *W,
 // round trips), and the lowest expert id holding it from one ballot per
 // logit slot, so ties go to the lower id as the compare order requires.
 // ---------------------------------------------------------------------------
-// Larger float -> larger key; -0 is folded onto +0 first, so floats that
-// compare equal get equal keys.
-__device__ inline uint32_t float_order_key(float v) {
-  const uint32_t b = __float_as_uint(v + 0.0f);
-  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
-}
+// float_order_key (common.h) gives the keys.
 
 // Maximum of v over the 64 lanes: within each row of 16 lanes by right
 // shifts (1, 2, 3, then 4 and 8 on the upper banks), then across rows by the
@@ -311,7 +306,9 @@ __device__ inline void wave_topk(const float *Lrow, int E, int k, int renorm, in
   for (int j = 0; j < EPL; ++j) {
     const int e = lane + 64 * j;
     v[j] = e < E ? Lrow[e] : -__builtin_inff();
-    key[j] = e < E ? float_order_key(v[j]) : 0u;
+    // key 0 belongs to one NaN bit pattern only; it ties with key 1 (another
+    // NaN) instead, so that 0 stays the marker
+    key[j] = e < E ? max(float_order_key(v[j]), 1u) : 0u;
   }
   float my_v = 0.0f;
   my_id = 0;

@@ -189,8 +189,13 @@ size_t nf4moe_route_workspace_bytes(int32_t T, int32_t E, int32_t top_k);
  * This is the pages' "a_cat sorted by expert, sizes + expert_ids" grouping
  * ("Why it happens" dataflow), done on the device with no host sync.
  * ids, offsets and slots are exact integers (bit-identical to a stable sort of
- * the same fp32 logits). Errors: INVALID_ARG (T < 0, E outside 1..1024, top_k
- * outside 1..min(E, 32), null pointers), WORKSPACE (ws_bytes too small). */
+ * the same fp32 logits). Non-finite logits: the order compares IEEE total-order
+ * keys with -0 taken as +0 (+inf and -inf in place, a positive NaN above +inf,
+ * a negative NaN below -inf; ties still go to the lower id), so every token
+ * always gets k distinct experts and every index stays in range; the weights
+ * of a token with a NaN or infinite logit are unspecified (NaN in practice).
+ * Errors: INVALID_ARG (T < 0, E outside 1..1024, top_k outside 1..min(E, 32),
+ * null pointers), WORKSPACE (ws_bytes too small). */
 nf4moe_status_t nf4moe_route_permute(const float *logits, int32_t T, int32_t E, int32_t top_k,
                                      int32_t renormalize, int32_t *topk_ids, float *topk_w,
                                      int32_t *expert_offsets, int32_t *sorted_slots,
@@ -204,7 +209,9 @@ size_t nf4moe_gemm_workspace_bytes(int32_t G, int32_t R);
  * W decoded from 4-bit codes in registers, fp32 accumulation.
  *   a        bf16 [a_rows, K] (device, 16-byte aligned rows: K % 8 == 0)
  *   a_row_of int32 [R] (device) or NULL: row r reads a[a_row_of[r]] (gather),
- *            NULL means a[r] (then a_rows >= R)
+ *            NULL means a[r] (then a_rows >= R). Indices outside [0, a_rows)
+ *            are a caller error; the kernels clamp them into that range, so
+ *            such a row's output is unspecified but no read leaves a
  *   B, B_scale  expert stack [E, N, K/2] + scales in `fmt` (device)
  *   G, group_offsets int32 [G+1] (device): group g = rows [off[g], off[g+1]),
  *            off[0] = 0, non-decreasing, off[G] = R (the caller guarantees this;
@@ -257,6 +264,10 @@ size_t nf4moe_workspace_bytes(const nf4moe_layer_t *layer, int32_t T_max);
  * The gate_up epilogue is SwiGLU, or with layer->glu the clamped GLU with the
  * layer's biases (see nf4moe_glu_t). Intermediates (h, partial products) stay
  * fp32; no bf16 expert weight is written anywhere.
+ * Non-finite input (NaN or inf in x, the weights or the router): routing keeps
+ * the order of nf4moe_route_permute (k distinct in-range experts per token,
+ * whichever kernel routes), so no index leaves its buffer; the outputs of the
+ * affected tokens are then unspecified.
  * Row-count invariance (the pages' STATUS page, kernel section): on the small-M
  * path (AUTO picks it for T * top_k <= 64) a token's outputs and routing carry
  * the same bits whatever the other tokens of the call; on the MFMA path, among

@@ -107,6 +107,7 @@ def test_grouped_gemm_validation():
     assert call(G=0) == INVALID
     assert call(R=-1) == INVALID
     assert call(a_rows=4) == INVALID          # no gather and too few rows
+    assert call(row_of=FAKE, a_rows=0) == INVALID   # a gather from an empty a
     assert call(dt=5) == INVALID
     assert call(path=9) == INVALID
     assert call(goff=None) == INVALID
@@ -165,3 +166,66 @@ def test_cpu_tensors_are_refused():
     torch = pytest.importorskip("torch")
     with pytest.raises(ValueError, match="GPU only"):
         pkg.quantize(torch.zeros(4, 64))
+
+
+def test_binding_refuses_mismatched_shapes():
+    """The binding checks every tensor's shape against E, H, I, K, T before it
+    passes raw pointers on (the C ABI cannot see buffer sizes); these checks run
+    before the device check, so CPU tensors reach them here."""
+    torch = pytest.importorskip("torch")
+    f32, u8 = torch.float32, torch.uint8
+    E, H, I, k = 4, 128, 64, 2
+
+    def layer(**kw):
+        d = dict(fmt=pkg.FMT_NF4, E=E, H=H, I=I, top_k=k,
+                 w13=torch.zeros(E, 2 * I, H // 2, dtype=u8), w13_scale=torch.zeros(E, 2 * I, H // 64),
+                 w2=torch.zeros(E, H, I // 2, dtype=u8), w2_scale=torch.zeros(E, H, I // 64),
+                 router_w=torch.zeros(E, H))
+        d.update(kw)
+        return pkg.MoELayer(**d)
+
+    layer().check_shapes()                                   # consistent shapes pass
+    bad = [dict(w13=torch.zeros(E, 2 * I, H, dtype=u8)),     # unpacked width
+           dict(w13_scale=torch.zeros(E, I, H // 64)),
+           dict(w2=torch.zeros(E, I, H // 2, dtype=u8)),     # transposed down stack
+           dict(w2_scale=torch.zeros(E, H, I // 32)),        # MXFP4-sized scales for NF4
+           dict(router_w=torch.zeros(E + 1, H)),
+           dict(router_b=torch.zeros(E - 1)),
+           dict(b13=torch.zeros(E, I)), dict(b2=torch.zeros(E, I))]
+    for kw in bad:
+        with pytest.raises(ValueError, match="shape"):
+            layer(**kw).struct()
+    with pytest.raises(ValueError, match="GPU only"):        # right shapes, wrong device
+        layer().struct()
+    lay = layer()
+    x = torch.zeros(3, H, dtype=torch.bfloat16)
+    pkg.check_forward_args(lay, x, torch.zeros(3, H, dtype=torch.bfloat16),
+                           torch.zeros(3, k, dtype=torch.int32), torch.zeros(3, k))
+    for args in ((torch.zeros(3, H + 64, dtype=torch.bfloat16),),
+                 (x, torch.zeros(2, H, dtype=torch.bfloat16)),
+                 (x, None, torch.zeros(3, k + 1, dtype=torch.int32)),
+                 (x, None, None, torch.zeros(k, 3))):
+        with pytest.raises(ValueError, match="shape"):
+            pkg.check_forward_args(lay, *args)
+    B = torch.zeros(E, 256, 256, dtype=u8)
+    Bs = torch.zeros(E, 256, 8)
+    off = torch.zeros(3, dtype=torch.int32)
+    a = torch.zeros(8, 512, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="shape"):
+        pkg.grouped_gemm(torch.zeros(8, 256, dtype=torch.bfloat16), B, Bs, off, 512, 8)   # a's K
+    with pytest.raises(ValueError, match="shape"):
+        pkg.grouped_gemm(a, B, Bs, off, 1024, 8)                                           # B's K
+    with pytest.raises(ValueError, match="shape"):
+        pkg.grouped_gemm(a, B, Bs, off, 512, 8, group_experts=torch.zeros(3, dtype=torch.int32))
+    with pytest.raises(ValueError, match="shape"):
+        pkg.grouped_gemm(a, B, Bs, off, 512, 8, a_row_of=torch.zeros(7, dtype=torch.int32))
+    with pytest.raises(ValueError, match="fewer than R"):
+        pkg.grouped_gemm(a, B, Bs, off, 512, 9)
+    with pytest.raises(ValueError, match="GPU only"):
+        pkg.grouped_gemm(a, B, Bs, off, 512, 8)
+    with pytest.raises(ValueError, match="shape"):
+        pkg.grouped_dgrad(torch.zeros(8, 128, dtype=torch.bfloat16), B, Bs, off, 512)     # dc's N
+    with pytest.raises(ValueError, match="shape"):
+        pkg.dequantize(B, torch.zeros(E, 256, 4), 512)
+    with pytest.raises(ValueError, match="shape"):
+        pkg.router_logits(x, torch.zeros(E, H + 64))

@@ -138,3 +138,48 @@ def test_small_m_grouped_gemm_rows_independent():
     pair = run([1, 2], [1, 2], [30, 16, 0])
     assert np.array_equal(pair[0], big[30]) and np.array_equal(pair[1], big[16])
     assert np.array_equal(pair[2], big[0])
+
+
+@pytest.mark.parametrize("E,k", [(64, 8), (100, 6)])
+def test_one_token_routing_ties_signed_zeros_and_nan(E, k):
+    """The one-token routing folded into the gate_up kernel ranks on the same
+    total order as the routing kernels (logit descending, id ascending on
+    order keys): exact ties from duplicated router rows, +0 / -0 logits from
+    zero rows, and a token whose activations hold a NaN. Each token alone (the
+    fused routing) must pick the ids and weights the separate routing kernels
+    pick for it inside a two-token call, and, for finite logits, the oracle's
+    selection rule on the GPU's own fp32 logits."""
+    wl = S.custom(E=E, top_k=k, H=256, I=128, wid=37 + E)
+    layer, _, _ = build_layers(wl, 0, DEV, path=M.PATH_AUTO)
+    W = layer.router_w.clone()
+    zero = [1, 4, 9, 17, 33, 40, 41, 50, E - 1]          # 9 zero rows: a tie across the k-th place
+    dup = [10, 11, 12, 20]                                # identical rows: exact ties
+    W[zero] = 0.0
+    W[dup[:-1]] = W[dup[-1]]
+    b = np.full(E, -4.0, np.float32)
+    b[zero] = np.where(np.arange(len(zero)) % 2 == 0, np.float32(0.0), np.float32(-0.0))
+    b[dup] = 0.0
+    layer.router_w = W.contiguous()
+    layer.router_b = torch.from_numpy(b).to(DEV)
+    X = S.make_x(wl, 7)
+    X[6, 5] = 0x7FC0                                      # a NaN activation
+    Wn, bn = layer.router_w.cpu().numpy(), b
+    ties_seen = 0
+    for t in range(7):
+        one = _run(layer, X[t:t + 1])
+        two = _run(layer, np.ascontiguousarray(X[[t, (t + 1) % 6]]))
+        assert np.array_equal(one[1][0], two[1][0]), f"token {t}: ids {one[1][0]} vs {two[1][0]}"
+        assert len(set(one[1][0].tolist())) == k and np.all((one[1][0] >= 0) & (one[1][0] < E))
+        if t == 6:
+            assert np.all(np.isnan(one[2][0].view(np.float32))) and np.all(np.isnan(two[2][0].view(np.float32)))
+            continue
+        assert np.array_equal(one[2][0], two[2][0]), f"token {t}: weights differ"
+        assert np.array_equal(one[0][0], two[0][0]), f"token {t}: outputs differ"
+        L32 = M.router_logits(bits_to_torch_bf16(X[t:t + 1]), layer.router_w, layer.router_b,
+                              matrix_cores=False).cpu().numpy().astype(np.float64)
+        ids_o, w_o = O.topk_route(L32, k, True)
+        assert np.array_equal(one[1][0], ids_o[0])
+        assert np.max(np.abs(one[2][0].view(np.float32) - w_o[0])) <= 1e-6
+        srt = np.sort(L32[0])[::-1]
+        ties_seen += int(srt[k - 1] == srt[k])
+    assert ties_seen > 0, "no token had a tie across the k-th place"
