@@ -81,6 +81,8 @@ def lib() -> ctypes.CDLL:
         "nf4moe_moe_forward_profiled": [ctypes.POINTER(Layer), vp, i32, vp, vp, sz, vp,
                                         ctypes.POINTER(ctypes.c_void_p)],
         "nf4moe_codebook": [ctypes.c_int, ctypes.POINTER(ctypes.c_float)],
+        "nf4moe_stream_read_sink_words": [i64],
+        "nf4moe_stream_read": [vp, i64, vp, vp],
         "nf4moe_status_string": [ctypes.c_int],
         "nf4moe_last_error": [],
         "nf4moe_version": [],
@@ -92,6 +94,7 @@ def lib() -> ctypes.CDLL:
     for name in ("nf4moe_route_workspace_bytes", "nf4moe_gemm_workspace_bytes", "nf4moe_workspace_bytes",
                  "nf4moe_router_workspace_bytes"):
         getattr(L, name).restype = ctypes.c_size_t
+    L.nf4moe_stream_read_sink_words.restype = ctypes.c_int64
     for name in ("nf4moe_status_string", "nf4moe_last_error", "nf4moe_version"):
         getattr(L, name).restype = ctypes.c_char_p
     _lib = L
@@ -169,6 +172,23 @@ def _workspace(nbytes: int, device):
 def _scale_dtype(fmt):
     torch = _torch()
     return {FMT_NF4: torch.float32, FMT_MXFP4: torch.uint8, FMT_NF4_BF16ABS: torch.int16}[fmt]
+
+
+def stream_read(buf, nbytes: int, sink):
+    """Measurement aid: one launch reading the first nbytes of buf (device) once
+    with 16-byte loads; sink is a device int32 tensor of at least
+    stream_read_sink_words(nbytes) elements."""
+    _dev(buf, "buf")
+    _dev(sink, "sink")
+    if nbytes > buf.numel() * buf.element_size():
+        raise ValueError(f"nbytes={nbytes} exceeds the buffer")
+    if sink.numel() * sink.element_size() < 4 * stream_read_sink_words(nbytes):
+        raise ValueError("sink too small")
+    _check(lib().nf4moe_stream_read(_ptr(buf), nbytes, _ptr(sink), _stream()))
+
+
+def stream_read_sink_words(nbytes: int) -> int:
+    return int(lib().nf4moe_stream_read_sink_words(nbytes))
 
 
 def quantize(w, fmt: int = FMT_NF4):

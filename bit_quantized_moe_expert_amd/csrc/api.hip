@@ -578,4 +578,16 @@ nf4moe_status_t nf4moe_moe_forward_profiled(const nf4moe_layer_t *layer, const u
   return forward_impl(layer, x, T, out, nullptr, nullptr, ws, ws_bytes, stream, events);
 }
 
+int64_t nf4moe_stream_read_sink_words(int64_t bytes) {
+  return bytes > 0 && bytes % 16 == 0 ? stream_read_grid(bytes) : 0;
+}
+
+nf4moe_status_t nf4moe_stream_read(const void *buf, int64_t bytes, uint32_t *sink, void *stream) {
+  if (bytes <= 0 || bytes % 16) return fail(NF4MOE_ERR_INVALID_ARG, "bytes=%lld must be a positive multiple of 16", (long long)bytes);
+  if (stream_read_grid(bytes) > 0x7fffffff) return fail(NF4MOE_ERR_UNSUPPORTED, "bytes=%lld too large", (long long)bytes);
+  if (!buf || !sink) return fail(NF4MOE_ERR_INVALID_ARG, "NULL pointer");
+  if (!aligned(buf, 16) || !aligned(sink, 4)) return fail(NF4MOE_ERR_INVALID_ARG, "misaligned pointer");
+  return hip_status(launch_stream_read(buf, bytes, sink, (hipStream_t)stream), "stream read launch");
+}
+
 }  // extern "C"

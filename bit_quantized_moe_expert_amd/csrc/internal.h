@@ -133,4 +133,9 @@ hipError_t launch_gemv_down_combine(int fmt, const float *h, const int32_t *slot
 // out[t] = bf16(sum_j slotbuf[t*k + j]) in j order.
 hipError_t launch_combine(const float *slotbuf, int T, int k, int H, uint16_t *out, hipStream_t s);
 
+// Plain streaming read of `bytes` (a multiple of 16) with one XOR word per
+// workgroup written to sink[stream_read_grid(bytes)]: a measurement aid.
+int64_t stream_read_grid(int64_t bytes);
+hipError_t launch_stream_read(const void *src, int64_t bytes, uint32_t *sink, hipStream_t s);
+
 }  // namespace nf4moe

@@ -290,6 +290,16 @@ nf4moe_status_t nf4moe_moe_forward_profiled(const nf4moe_layer_t *layer, const u
                                             int32_t T, uint16_t *out, void *ws, size_t ws_bytes,
                                             void *stream, void *const *events);
 
+/* nf4moe_stream_read -- a measurement aid, not part of the layer: one launch
+ * that reads `bytes` bytes of `buf` (device, 16-byte aligned, bytes a positive
+ * multiple of 16) once with 16-byte loads and writes one 32-bit XOR per
+ * workgroup to sink (device, nf4moe_stream_read_sink_words(bytes) words). Its
+ * duration gives the plain HBM read rate of a single launch of that size, the
+ * measured ceiling the decode kernels are set beside. Errors: INVALID_ARG for
+ * a bad size, NULL or misaligned pointers; UNSUPPORTED past 2^31 workgroups. */
+int64_t nf4moe_stream_read_sink_words(int64_t bytes);
+nf4moe_status_t nf4moe_stream_read(const void *buf, int64_t bytes, uint32_t *sink, void *stream);
+
 /* nf4moe_codebook -- host copy of the 16 fp32 decode values the kernels use for
  * `fmt` (index = 4-bit code). No device access. Returns INVALID_ARG for a bad fmt
  * or NULL out. */

@@ -238,11 +238,12 @@ def mxfp4_dequantize(packed: np.ndarray, scales: np.ndarray, N: int, K: int) -> 
     codes = np.empty((N, K), dtype=np.uint8)
     codes[:, 0::2] = packed & 0xF
     codes[:, 1::2] = packed >> 4
-    vals = e2m1_values()[codes].astype(np.float64)
-    ex = np.repeat(scales.astype(np.int64), MXFP4_BLOCK, axis=1)
-    out = np.ldexp(vals, ex - 127)
-    out[ex == 255] = np.nan
-    return out.astype(np.float32)
+    vals = e2m1_values()[codes].astype(np.float64).reshape(N, K // MXFP4_BLOCK, MXFP4_BLOCK)
+    ex = scales.astype(np.int64)
+    mult = np.ldexp(1.0, ex - 127)                 # the block's power of two, exact in fp64
+    mult[ex == 255] = np.nan
+    out = vals * mult[..., None]                   # exact: a 2-bit significand times 2^X
+    return out.reshape(N, K).astype(np.float32)
 
 
 def quantize(fmt: int, w: np.ndarray):

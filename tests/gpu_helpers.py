@@ -53,6 +53,24 @@ class LazyStack:
             self.cache[e] = O.quantize(self.fmt, np.ascontiguousarray(w, np.float32))
         return self.cache[e]
 
+    def prefetch(self, experts, workers=16):
+        """Quantize the listed experts ahead of use on a thread pool (numpy's
+        array operations release the GIL, so the oracle's per-expert
+        quantization runs in parallel); the values are those _get computes."""
+        from concurrent.futures import ThreadPoolExecutor
+        todo = sorted(set(int(e) for e in experts) - set(self.cache))
+        if not todo:
+            return
+        with ThreadPoolExecutor(max(1, min(workers, len(todo)))) as ex:
+            for e, q in zip(todo, ex.map(self._quantize_one, todo)):
+                self.cache[e] = q
+
+    def _quantize_one(self, e):
+        w = self.src[e]
+        if not isinstance(w, np.ndarray):
+            w = w.detach().cpu().numpy()
+        return O.quantize(self.fmt, np.ascontiguousarray(w, np.float32))
+
     def packed(self):
         return _Proj(self, 0)
 
@@ -63,6 +81,9 @@ class LazyStack:
 class _Proj:
     def __init__(self, st, i):
         self.st, self.i = st, i
+
+    def stack(self):
+        return self.st
 
     def __getitem__(self, e):
         return self.st._get(int(e))[self.i]
@@ -149,3 +170,45 @@ def check_routing_near_ties(gpu_ids, L64, k, renorm=True):
                 assert abs(L64[t, a] - L64[t, b]) <= tau[t], (
                     f"token {t} slot {j}: gpu {a} ({L64[t, a]}) vs oracle {b} ({L64[t, b]})")
     return n
+
+
+def prefetch_experts(o_layer, experts, workers=16):
+    """Quantize (oracle side) the experts a sample will touch, in parallel."""
+    for key in ("w13", "w2"):
+        st = o_layer[key]
+        if isinstance(st, _Proj):
+            st.stack().prefetch(experts, workers)
+
+
+def coverage_tokens(gids, E, tile_rows, n, seed, allowed=None):
+    """Tokens to compare at full size, chosen from the GPU's routing so that
+    every expert group's first row, last row and the first row of its last
+    (partial) tile, and the rows on each side of its first tile boundary, are
+    among the compared rows (a group's rows are its slots t*k + j in ascending
+    order); then seeded random tokens up to n. allowed: optional boolean mask
+    of tokens that may be chosen (e.g. those whose experts the oracle has)."""
+    T, k = gids.shape
+    flat = gids.reshape(-1).astype(np.int64)
+    order = np.argsort(flat, kind="stable")
+    counts = np.bincount(flat, minlength=E)
+    off = np.concatenate([[0], np.cumsum(counts)])
+    ok = np.ones(T, bool) if allowed is None else np.asarray(allowed, bool)
+    chosen = []
+    for e in range(E):
+        c = int(counts[e])
+        if c == 0:
+            continue
+        pos = [0, c - 1, (c - 1) // tile_rows * tile_rows]
+        if c > tile_rows:
+            pos += [tile_rows - 1, tile_rows]
+        for p in pos:
+            t = int(order[off[e] + p]) // k
+            if ok[t]:
+                chosen.append(t)
+    chosen = list(dict.fromkeys(chosen))
+    rest = np.setdiff1d(np.flatnonzero(ok), chosen)
+    extra = max(0, n - len(chosen))
+    if extra and rest.size:
+        rng = np.random.default_rng(seed)
+        chosen += rng.choice(rest, min(extra, rest.size), replace=False).tolist()
+    return np.array(sorted(chosen), dtype=np.int64)

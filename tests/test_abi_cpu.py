@@ -229,3 +229,12 @@ def test_binding_refuses_mismatched_shapes():
         pkg.dequantize(B, torch.zeros(E, 256, 4), 512)
     with pytest.raises(ValueError, match="shape"):
         pkg.router_logits(x, torch.zeros(E, H + 64))
+
+
+def test_stream_read_validation():
+    assert L.nf4moe_stream_read_sink_words(16 * 1024) == 1
+    assert L.nf4moe_stream_read_sink_words(18) == 0
+    assert L.nf4moe_stream_read(FAKE, 0, FAKE, STREAM) == INVALID
+    assert L.nf4moe_stream_read(FAKE, 24, FAKE, STREAM) == INVALID
+    assert L.nf4moe_stream_read(FAKE + 8, 32, FAKE, STREAM) == INVALID
+    assert L.nf4moe_stream_read(None, 32, FAKE, STREAM) == INVALID

@@ -155,7 +155,7 @@ def test_one_token_routing_ties_signed_zeros_and_nan(E, k):
     zero = [1, 4, 9, 17, 33, 40, 41, 50, E - 1]          # 9 zero rows: a tie across the k-th place
     dup = [10, 11, 12, 20]                                # identical rows: exact ties
     W[zero] = 0.0
-    W[dup[:-1]] = W[dup[-1]]
+    W[dup[:-1]] = W[dup[-1]].clone()
     b = np.full(E, -4.0, np.float32)
     b[zero] = np.where(np.arange(len(zero)) % 2 == 0, np.float32(0.0), np.float32(-0.0))
     b[dup] = 0.0

@@ -4,13 +4,16 @@ Bit-exact: NF4 / MXFP4 codes and scales, every decoded weight, top-k ids,
 expert offsets and the sorted slot permutation. Toleranced (the output
 contract): |gpu - oracle| <= 1e-2 |oracle| + 1e-3 rms(oracle) elementwise.
 """
+import json
+import os
+
 import numpy as np
 import pytest
 
 import moe_synth as S
 import oracle as O
 from gpu_helpers import (bf16_to_np, bits_to_torch_bf16, build_layers, check_bound,
-                         check_routing_near_ties)
+                         check_routing_near_ties, coverage_tokens, prefetch_experts)
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -21,6 +24,7 @@ if not torch.cuda.is_available():
 import bit_quantized_moe_expert_amd as M  # noqa: E402
 
 DEV = "cuda"
+GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "printed_examples.json")))
 
 
 def _planted_weights(fmt, rows, K, seed):
@@ -178,12 +182,16 @@ def _grouped_case(fmt, N, K, E, sizes, experts, path, out_dtype, gather, seed):
 @pytest.mark.parametrize("path", [M.PATH_SMALL_M, M.PATH_MFMA])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_grouped_gemm_page_example(fmt, path, dtype):
-    """E, N, K = 8, 256, 512; sizes [3, 1, 4]; expert_ids [5, 0, 2]; relative
-    Frobenius error <= 1e-2 (the page's own check), plus the elementwise bound."""
+    """The page's own example (tests/golden/printed_examples.json,
+    "grouped_example": E, N, K = 8, 256, 512; sizes [3, 1, 4]; expert_ids
+    [5, 0, 2]) and its check, relative Frobenius error <= 1e-2, plus the
+    elementwise bound."""
+    g = GOLD["grouped_example"]
     od = torch.float32 if dtype == "f32" else torch.bfloat16
-    got, ref = _grouped_case(fmt, 256, 512, 8, [3, 1, 4], [5, 0, 2], path, od, False, seed=11)
+    got, ref = _grouped_case(fmt, g["N"], g["K"], g["E"], g["sizes"], g["expert_ids"], path, od, False,
+                             seed=11)
     fro = np.linalg.norm(got - ref) / np.linalg.norm(ref)
-    assert fro <= 1e-2
+    assert fro <= g["rel_frobenius_bound"]
     check_bound(got, ref, "page example")
 
 
@@ -248,12 +256,17 @@ def _forward_case(wl, T, path=0, on_device_rng=False, sample=None, gptoss=None):
     torch.cuda.synchronize()
     got = bf16_to_np(out)
     gids = ids.cpu().numpy()
-    rows = np.arange(T) if sample is None else np.asarray(sample)
+    if callable(sample):                      # chosen from the GPU's routing
+        rows = sample(gids)
+    else:
+        rows = np.arange(T) if sample is None else np.asarray(sample)
+    print(f"[parity] {wl.name} T={T} path={path}: comparing {len(rows)} tokens", flush=True)
+    prefetch_experts(o_layer, np.unique(gids[rows]))
     L64 = O.router_logits(xb[rows], o_layer["router_w"], o_layer["router_b"])
     nties = check_routing_near_ties(gids[rows], L64, wl.top_k, bool(wl.renormalize))
     ref = O.moe_forward(o_layer, xb[rows], topk_ids_override=gids[rows])
     ratio = check_bound(got[rows], ref, f"{wl.name} T={T} path={path}")
-    return dict(out=out, ratio=ratio, near_ties=nties, layer=dev_layer, x=x)
+    return dict(out=out, ratio=ratio, near_ties=nties, layer=dev_layer, x=x, rows=rows, ids=gids)
 
 
 SMALL = [
@@ -370,6 +383,22 @@ def test_forward_zero_tokens():
 
 
 # --------------------------------------------------------------------- full-size workloads
+# Sampled full-size parity: the tokens compared are chosen from the GPU's own
+# routing so that every expert group's first row, last row and partial last
+# MFMA tile are among them (tile height from the routed rows per expert: 64
+# when the groups average at most 48 rows, else 128), topped up with seeded
+# random tokens.
+def _tile_rows(R, E):
+    return 64 if R <= 48 * min(R, E) else 128
+
+
+def _covering(E, k, T, n, seed, experts=None):
+    def pick(gids):
+        allowed = None if experts is None else np.all(np.isin(gids, experts), axis=1)
+        return coverage_tokens(gids, E, _tile_rows(T * k, E), n, seed, allowed)
+    return pick
+
+
 @pytest.mark.slow
 def test_full_olmoe_decode():
     _forward_case(S.WORKLOADS["olmoe_decode"], 1, on_device_rng=True)
@@ -378,25 +407,117 @@ def test_full_olmoe_decode():
 @pytest.mark.slow
 def test_full_olmoe_prefill_sampled():
     wl = S.WORKLOADS["olmoe_prefill"]
-    _forward_case(wl, 4096, on_device_rng=True, sample=[0, 4095])
+    r = _forward_case(wl, 4096, on_device_rng=True, sample=_covering(64, 8, 4096, 256, seed=2))
+    assert len(r["rows"]) >= 256 and np.unique(r["ids"][r["rows"]]).size == 64
 
 
 @pytest.mark.slow
-@pytest.mark.parametrize("T,sample", [(1, None), (16, [0, 15]), (512, [0, 511])])
-def test_full_qwen3_zipf(T, sample):
-    _forward_case(S.WORKLOADS["qwen3_zipf"], T, on_device_rng=True, sample=sample)
+@pytest.mark.parametrize("T,n", [(1, None), (16, None), (512, 128)])
+def test_full_qwen3_zipf(T, n):
+    wl = S.WORKLOADS["qwen3_zipf"]
+    r = _forward_case(wl, T, on_device_rng=True, sample=None if n is None else _covering(128, 8, T, n, seed=3))
+    if n is not None:      # every expert the GPU routed to is among the compared rows
+        assert len(r["rows"]) >= n and np.array_equal(np.unique(r["ids"][r["rows"]]), np.unique(r["ids"]))
+
+
+# gpt-oss-shaped: the oracle quantizes each touched expert (5760 x 2880 and
+# 2880 x 2880 MXFP4) itself, so the 128 compared tokens are drawn from those
+# routed only to a seeded set of 72 of the 128 experts.
+_GPTOSS_SET = np.sort(np.random.default_rng(4).permutation(128)[:72])
 
 
 @pytest.mark.slow
-@pytest.mark.parametrize("T,sample", [(1, None), (2048, [2047])])
-def test_full_gptoss_mxfp4(T, sample):
-    _forward_case(S.WORKLOADS["gptoss_mxfp4"], T, on_device_rng=True, sample=sample)
+@pytest.mark.parametrize("T", [1, 2048])
+def test_full_gptoss_mxfp4(T):
+    sample = None if T == 1 else _covering(128, 4, T, 128, seed=4, experts=_GPTOSS_SET)
+    r = _forward_case(S.WORKLOADS["gptoss_mxfp4"], T, on_device_rng=True, sample=sample)
+    assert T == 1 or len(r["rows"]) >= 128
 
 
 @pytest.mark.slow
-@pytest.mark.parametrize("T,sample", [(1, None), (2048, [0, 2047])])
-def test_full_gptoss_mxfp4_clamped_glu(T, sample):
+@pytest.mark.parametrize("T", [1, 2048])
+def test_full_gptoss_mxfp4_clamped_glu(T):
     """The gpt-oss-120b-shaped MXFP4 layer in its own expert form: clamped GLU
     (alpha 1.702, limit 7), per-expert biases, interleaved gate / up rows."""
-    _forward_case(S.WORKLOADS["gptoss_mxfp4"], T, on_device_rng=True, sample=sample,
-                  gptoss=dict(alpha=1.702, limit=7.0, interleaved=True))
+    sample = None if T == 1 else _covering(128, 4, T, 128, seed=5, experts=_GPTOSS_SET)
+    r = _forward_case(S.WORKLOADS["gptoss_mxfp4"], T, on_device_rng=True, sample=sample,
+                      gptoss=dict(alpha=1.702, limit=7.0, interleaved=True))
+    assert T == 1 or len(r["rows"]) >= 128
+
+
+# --------------------------------------------------------------------- stacks past 2 GiB
+# Every expert base offset is formed in 64 bits (the pages' "Limitations" and
+# "Correctness contracts": int64 expert-base offsets, observed past the 2^31
+# boundary). An NF4 gate_up-shaped stack of 544 experts x 4096 rows x 2048
+# columns holds 2.28 GB of codes; experts 512 and up start past 2^31 bytes.
+_BIG = S.custom(E=544, top_k=4, H=2048, I=2048, wid=90)
+
+
+@pytest.fixture(scope="module")
+def big_stack():
+    w13 = S.make_stack_torch(_BIG, 0, "w13", DEV)              # fp32 [544, 4096, 2048] on the device
+    p13, s13 = M.quantize(w13, O.FMT_NF4)
+    assert p13.numel() > 2 ** 31 and p13[512].data_ptr() - p13.data_ptr() >= 2 ** 31
+    yield w13, p13, s13
+    del w13, p13, s13
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("path", [M.PATH_SMALL_M, M.PATH_MFMA])
+def test_grouped_gemm_stack_past_2gib(big_stack, path):
+    from gpu_helpers import LazyStack
+    w13, p13, s13 = big_stack
+    N, K = 2 * _BIG.I, _BIG.H
+    experts = [3, 511, 512, 530, 543]
+    sizes = [2, 3, 1, 5, 4] if path == M.PATH_SMALL_M else [40, 3, 70, 1, 33]
+    R = sum(sizes)
+    off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    rng = np.random.default_rng(91)
+    ab = S.f32_to_bf16_bits(rng.standard_normal((R, K)).astype(np.float32))
+    print(f"[parity] 2.28 GB NF4 stack, experts {experts}, path={path}", flush=True)
+    c = M.grouped_gemm(bits_to_torch_bf16(ab), p13, s13, torch.from_numpy(off).to(DEV), K, R,
+                       group_experts=torch.from_numpy(np.array(experts, np.int32)).to(DEV),
+                       fmt=O.FMT_NF4, path=path)
+    got = c.cpu().numpy().astype(np.float64)
+    st = LazyStack(O.FMT_NF4, w13)
+    st.prefetch(experts)
+    ref = O.grouped_gemm(O.bf16_bits_to_f64(ab), None, O.FMT_NF4, st.packed(), st.scale(), N, K, off, experts)
+    check_bound(got, ref, f"stack past 2 GiB path={path}")
+    for e in (512, 543):        # the codes the kernel read past 2^31 are the oracle's codes
+        assert np.array_equal(p13[e].cpu().numpy(), st.packed()[e])
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("T", [6, 40])
+def test_forward_stack_past_2gib(big_stack, T):
+    """A whole layer whose router sends every token to experts past the 2^31
+    byte boundary of the gate_up stack (and one below it): T = 6 runs the
+    small-M kernels, T = 40 the MFMA kernels."""
+    from gpu_helpers import LazyStack
+    w13, p13, s13 = big_stack
+    wl = _BIG
+    W_r, _ = S.make_router(wl)
+    b = np.zeros(wl.E, np.float32)
+    hot = [100, 512, 520, 530, 543]
+    b[hot] = 8.0
+    w2 = S.make_stack_torch(wl, 0, "w2", DEV)
+    p2, s2 = M.quantize(w2, O.FMT_NF4)
+    layer = M.MoELayer(fmt=O.FMT_NF4, E=wl.E, H=wl.H, I=wl.I, top_k=wl.top_k, w13=p13, w13_scale=s13,
+                       w2=p2, w2_scale=s2, router_w=torch.from_numpy(W_r).to(DEV),
+                       router_b=torch.from_numpy(b).to(DEV))
+    xb = S.make_x(wl, T)
+    print(f"[parity] layer with a 2.28 GB gate_up stack, T={T}", flush=True)
+    out, ids, _ = M.moe_forward(layer, bits_to_torch_bf16(xb), return_routing=True)
+    gids = ids.cpu().numpy()
+    assert set(np.unique(gids).tolist()) <= set(hot) and np.any(gids >= 512)
+    st13, st2 = LazyStack(O.FMT_NF4, w13), LazyStack(O.FMT_NF4, w2)
+    st13.prefetch(np.unique(gids)); st2.prefetch(np.unique(gids))
+    o_layer = dict(fmt=O.FMT_NF4, E=wl.E, H=wl.H, I=wl.I, top_k=wl.top_k, renormalize=1,
+                   w13=st13.packed(), w13_scale=st13.scale(), w2=st2.packed(), w2_scale=st2.scale(),
+                   router_w=W_r, router_b=b)
+    L64 = O.router_logits(xb, W_r, b)
+    check_routing_near_ties(gids, L64, wl.top_k)
+    ref = O.moe_forward(o_layer, xb, topk_ids_override=gids)
+    check_bound(bf16_to_np(out), ref, f"stack past 2 GiB T={T}")
+    del w2, p2, s2
