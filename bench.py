@@ -422,11 +422,12 @@ def measure(wl, T, nlayers, args, dev, headline_steps, warmup, gptoss_form=False
     return run, res
 
 
-def stream_ceiling(dev, sizes, launches=32):
+def stream_ceiling(dev, sizes, launches=32, shapes=(2, 4, 8, 16)):
     """Measured single-launch HBM read rate (nf4moe_stream_read) at given byte
-    counts: each launch reads a different slice of a 2 GiB buffer (so the bytes
-    are not cache-resident), queued back to back behind a spin kernel, each
-    timed by its own HIP events; median per size."""
+    counts, the fastest of several launch shapes (16-byte loads per thread):
+    each launch reads a different slice of a 2 GiB buffer (so the bytes are not
+    cache-resident), queued back to back behind a spin kernel, each timed by its
+    own HIP events; the median per shape, the best shape per size."""
     import numpy as np
     import torch
     import bit_quantized_moe_expert_amd as M
@@ -436,22 +437,28 @@ def stream_ceiling(dev, sizes, launches=32):
     out = {}
     for name, nbytes in sizes.items():
         nbytes = nbytes // 16 * 16
-        sink = torch.empty(M.stream_read_sink_words(nbytes), dtype=torch.int32, device=dev)
         nslice = max(1, (1 << 31) // nbytes)
-        views = [buf[(i % nslice) * nbytes:(i % nslice + 1) * nbytes] for i in range(launches + 4)]
-        for v in views[:4]:
-            M.stream_read(v, nbytes, sink)
-        torch.cuda.synchronize()
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(launches)]
-        torch.cuda._sleep(spin_cycles_for(0.0002 * launches + 0.01, stream))
-        for (a, b), v in zip(evs, views[4:]):
-            a.record(stream)
-            M.stream_read(v, nbytes, sink)
-            b.record(stream)
-        torch.cuda.synchronize()
-        t = float(np.median([a.elapsed_time(b) for a, b in evs]))
+        per_shape = {}
+        for loads in shapes:
+            sink = torch.empty(M.stream_read_sink_words(nbytes, loads), dtype=torch.int32, device=dev)
+            views = [buf[(i % nslice) * nbytes:(i % nslice + 1) * nbytes] for i in range(launches + 4)]
+            for v in views[:4]:
+                M.stream_read(v, nbytes, sink, loads)
+            torch.cuda.synchronize()
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(launches)]
+            torch.cuda._sleep(spin_cycles_for(0.0002 * launches + 0.01, stream))
+            for (a, b), v in zip(evs, views[4:]):
+                a.record(stream)
+                M.stream_read(v, nbytes, sink, loads)
+                b.record(stream)
+            torch.cuda.synchronize()
+            per_shape[loads] = float(np.median([a.elapsed_time(b) for a, b in evs]))
+        best = min(per_shape, key=per_shape.get)
+        t = per_shape[best]
         out[name] = {"bytes": nbytes, "ms": t, "GBps": nbytes / (t * 1e-3) / 1e9,
-                     "frac_of_spec": nbytes / (t * 1e-3) / 1e9 / HBM_PEAK_GBS}
+                     "frac_of_spec": nbytes / (t * 1e-3) / 1e9 / HBM_PEAK_GBS, "loads_per_thread": best,
+                     "ms_by_loads_per_thread": per_shape}
     del buf
     torch.cuda.empty_cache()
     return out

@@ -81,8 +81,8 @@ def lib() -> ctypes.CDLL:
         "nf4moe_moe_forward_profiled": [ctypes.POINTER(Layer), vp, i32, vp, vp, sz, vp,
                                         ctypes.POINTER(ctypes.c_void_p)],
         "nf4moe_codebook": [ctypes.c_int, ctypes.POINTER(ctypes.c_float)],
-        "nf4moe_stream_read_sink_words": [i64],
-        "nf4moe_stream_read": [vp, i64, vp, vp],
+        "nf4moe_stream_read_sink_words": [i64, i32],
+        "nf4moe_stream_read": [vp, i64, i32, vp, vp],
         "nf4moe_status_string": [ctypes.c_int],
         "nf4moe_last_error": [],
         "nf4moe_version": [],
@@ -174,21 +174,21 @@ def _scale_dtype(fmt):
     return {FMT_NF4: torch.float32, FMT_MXFP4: torch.uint8, FMT_NF4_BF16ABS: torch.int16}[fmt]
 
 
-def stream_read(buf, nbytes: int, sink):
+def stream_read(buf, nbytes: int, sink, loads_per_thread: int = 4):
     """Measurement aid: one launch reading the first nbytes of buf (device) once
-    with 16-byte loads; sink is a device int32 tensor of at least
-    stream_read_sink_words(nbytes) elements."""
+    with 16-byte loads, loads_per_thread per thread; sink is a device int32
+    tensor of at least stream_read_sink_words(nbytes, loads_per_thread) elements."""
     _dev(buf, "buf")
     _dev(sink, "sink")
     if nbytes > buf.numel() * buf.element_size():
         raise ValueError(f"nbytes={nbytes} exceeds the buffer")
-    if sink.numel() * sink.element_size() < 4 * stream_read_sink_words(nbytes):
+    if sink.numel() * sink.element_size() < 4 * stream_read_sink_words(nbytes, loads_per_thread):
         raise ValueError("sink too small")
-    _check(lib().nf4moe_stream_read(_ptr(buf), nbytes, _ptr(sink), _stream()))
+    _check(lib().nf4moe_stream_read(_ptr(buf), nbytes, loads_per_thread, _ptr(sink), _stream()))
 
 
-def stream_read_sink_words(nbytes: int) -> int:
-    return int(lib().nf4moe_stream_read_sink_words(nbytes))
+def stream_read_sink_words(nbytes: int, loads_per_thread: int = 4) -> int:
+    return int(lib().nf4moe_stream_read_sink_words(nbytes, loads_per_thread))
 
 
 def quantize(w, fmt: int = FMT_NF4):
@@ -234,7 +234,7 @@ def absmax_to_bf16(absmax):
 def router_logits(x, router_w, router_b=None, matrix_cores: bool = True):
     """x bf16 [T, H], W_r fp32 [E, H] (+ b [E]) -> logits fp32 [T, E].
     matrix_cores: hand the library the workspace that enables its MFMA kernel
-    (used for T > 32, H % 32 == 0); False keeps the vector-ALU kernels."""
+    (used for T > 256, H % 32 == 0); False keeps the vector-ALU kernels."""
     torch = _torch()
     _shape(x, "x", (None, None))
     T, H = x.shape

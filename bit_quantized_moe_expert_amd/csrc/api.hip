@@ -97,7 +97,7 @@ void carve_route_scratch(Carve &cv, const RoutePlan &rp, int E, RouteBufs &rb) {
 
 struct ForwardCarve {
   float *logits;
-  uint16_t *rsplit;  // router weight bf16 planes (T >= kMfmaLogitsT), else null
+  uint16_t *rsplit;  // router weight bf16 planes (T > kRowsLogitsMaxT), else null
   RouteBufs rb;
   float *h;
   float *slotbuf;
@@ -116,7 +116,7 @@ ForwardCarve carve_forward(void *ws, const nf4moe_layer_t &L, int T) {
   carve_route_scratch(cv, rp, L.E, fc.rb);
   fc.h = cv.take<float>((size_t)(rp.R > 0 ? rp.R : 1) * L.I);
   fc.slotbuf = cv.take<float>((size_t)(rp.R > 0 ? rp.R : 1) * L.H);
-  fc.rsplit = T >= kMfmaLogitsT ? cv.take<uint16_t>(router_split_bytes(L.E, L.H) / sizeof(uint16_t)) : nullptr;
+  fc.rsplit = T > kRowsLogitsMaxT ? cv.take<uint16_t>(router_split_bytes(L.E, L.H) / sizeof(uint16_t)) : nullptr;
   fc.bytes = align_up(cv.off);
   return fc;
 }
@@ -578,16 +578,20 @@ nf4moe_status_t nf4moe_moe_forward_profiled(const nf4moe_layer_t *layer, const u
   return forward_impl(layer, x, T, out, nullptr, nullptr, ws, ws_bytes, stream, events);
 }
 
-int64_t nf4moe_stream_read_sink_words(int64_t bytes) {
-  return bytes > 0 && bytes % 16 == 0 ? stream_read_grid(bytes) : 0;
+int64_t nf4moe_stream_read_sink_words(int64_t bytes, int32_t loads_per_thread) {
+  return bytes > 0 && bytes % 16 == 0 && stream_read_loads_ok(loads_per_thread)
+             ? stream_read_grid(bytes, loads_per_thread) : 0;
 }
 
-nf4moe_status_t nf4moe_stream_read(const void *buf, int64_t bytes, uint32_t *sink, void *stream) {
+nf4moe_status_t nf4moe_stream_read(const void *buf, int64_t bytes, int32_t loads_per_thread, uint32_t *sink,
+                                   void *stream) {
   if (bytes <= 0 || bytes % 16) return fail(NF4MOE_ERR_INVALID_ARG, "bytes=%lld must be a positive multiple of 16", (long long)bytes);
-  if (stream_read_grid(bytes) > 0x7fffffff) return fail(NF4MOE_ERR_UNSUPPORTED, "bytes=%lld too large", (long long)bytes);
+  if (!stream_read_loads_ok(loads_per_thread))
+    return fail(NF4MOE_ERR_INVALID_ARG, "loads_per_thread=%d must be 1, 2, 4, 8 or 16", loads_per_thread);
+  if (stream_read_grid(bytes, loads_per_thread) > 0x7fffffff) return fail(NF4MOE_ERR_UNSUPPORTED, "bytes=%lld too large", (long long)bytes);
   if (!buf || !sink) return fail(NF4MOE_ERR_INVALID_ARG, "NULL pointer");
   if (!aligned(buf, 16) || !aligned(sink, 4)) return fail(NF4MOE_ERR_INVALID_ARG, "misaligned pointer");
-  return hip_status(launch_stream_read(buf, bytes, sink, (hipStream_t)stream), "stream read launch");
+  return hip_status(launch_stream_read(buf, bytes, loads_per_thread, sink, (hipStream_t)stream), "stream read launch");
 }
 
 }  // extern "C"

@@ -37,10 +37,12 @@ hipError_t launch_dequantize(int fmt, const uint8_t *packed, const void *scale, 
 hipError_t launch_absmax_bf16(const float *a, int64_t n, uint16_t *out, int32_t *inexact, hipStream_t s);
 
 // Router logits. With split_ws (>= router_split_bytes(E, H) bytes, 256-byte
-// aligned) and T >= kMfmaLogitsT, H % 32 == 0: the matrix-core kernel.
+// aligned) and T > kRowsLogitsMaxT, H % 32 == 0: the matrix-core kernel.
 // rows_only: the one-workgroup-per-expert kernel for every T, so each token's
 // logits have the same bits whatever T (the small-M path's contract).
-constexpr int kMfmaLogitsT = 33;
+// Up to this many tokens every router call uses the one-workgroup-per-expert
+// kernel (the small-M path uses it for every T).
+constexpr int kRowsLogitsMaxT = 256;
 size_t router_split_bytes(int E, int H);
 hipError_t launch_router_logits(const uint16_t *x, int T, int H, const float *W, const float *b,
                                 int E, float *logits, void *split_ws, hipStream_t s,
@@ -96,15 +98,18 @@ struct GemmArgs {
   // epilogue: SwiGLU before the activation, slot before the routing weight.
   const float *bias;
   // MFMA path: rows per tile of the tile table (128, or 64 for routed batches
-  // with few rows per expert); 0 means 128.
+  // with few rows per expert; 0 means 128). Each workgroup runs a 64-row body
+  // for a tile of at most 64 rows.
   int tile_rows;
 };
 
 // Rows per MFMA tile for R routed rows over at most G groups: 64-row tiles
-// when the groups average at most 48 rows, else 128. (Measured: 64-row tiles
-// take 14-29 % off Qwen3-shaped T = 128 / 512 and OLMoE-shaped T = 64 layers;
-// at 64 rows per group, gpt-oss-shaped T = 2048, they cost 8 %: half the
-// MFMAs per decoded weight.)
+// when the groups average at most 48 rows, else 128. More, shorter tiles put
+// more workgroups on the chip when a batch has few rows per expert (measured:
+// Qwen3-shaped T = 128 / 512 172 / 306 us against 205 / 323 us with 128-row
+// tables); with many rows per expert, 128-row tiles decode each weight tile
+// half as often. Within a 128-row table, a last tile of at most 64 rows runs
+// the 64-row body.
 inline int mfma_tile_rows(int64_t R, int64_t G) {
   const int64_t groups = R < G ? R : G;
   return (groups > 0 && R <= 48 * groups) ? 64 : 128;
@@ -133,9 +138,11 @@ hipError_t launch_gemv_down_combine(int fmt, const float *h, const int32_t *slot
 // out[t] = bf16(sum_j slotbuf[t*k + j]) in j order.
 hipError_t launch_combine(const float *slotbuf, int T, int k, int H, uint16_t *out, hipStream_t s);
 
-// Plain streaming read of `bytes` (a multiple of 16) with one XOR word per
-// workgroup written to sink[stream_read_grid(bytes)]: a measurement aid.
-int64_t stream_read_grid(int64_t bytes);
-hipError_t launch_stream_read(const void *src, int64_t bytes, uint32_t *sink, hipStream_t s);
+// Plain streaming read of `bytes` (a multiple of 16), `loads` 16-byte loads
+// per thread, with one XOR word per workgroup written to
+// sink[stream_read_grid(bytes, loads)]: a measurement aid.
+bool stream_read_loads_ok(int loads);
+int64_t stream_read_grid(int64_t bytes, int loads);
+hipError_t launch_stream_read(const void *src, int64_t bytes, int loads, uint32_t *sink, hipStream_t s);
 
 }  // namespace nf4moe

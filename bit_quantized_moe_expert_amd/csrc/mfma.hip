@@ -70,33 +70,27 @@ __device__ inline void build_mfma_table(uint4 *tab) {
   }
 }
 
-// AM: activation operand mode. 0: bf16 A; 2: an fp32 A given as 32-bit
-// (hi, lo) bf16 pairs, its truncated bf16 hi and the RNE bf16 of the rest
-// (the SwiGLU epilogue writes h so), each weight product taking three MFMAs.
-// XF: the extended gate_up / down epilogue (clamped GLU, interleaved gate and
-// up rows, per-expert biases); XF = 0 instantiates the plain kernel.
-// MB: 32-row blocks per tile (4: 128-row tiles; 2: 64-row tiles, for routed
-// batches with few rows per expert, where 128-row tiles would be mostly empty).
+// LDS bytes of one workgroup: the decode table and the A buffers of the
+// 128-row body (hi[2], and lo[2] for an fp32 A).
+template <int AM>
+constexpr int mfma_lds_bytes() { return kTabBytes + (AM != 0 ? 4 : 2) * 128 * kApad * 2; }
+
+// One output tile: rows [trow0, trow0 + trows) of expert e against weight-row
+// tile nt. AM: activation operand mode. 0: bf16 A; 2: an fp32 A given as
+// 32-bit (hi, lo) bf16 pairs, its truncated bf16 hi and the RNE bf16 of the
+// rest (the SwiGLU epilogue writes h so), each weight product taking three
+// MFMAs. XF: the extended gate_up / down epilogue (clamped GLU, interleaved
+// gate and up rows, per-expert biases); XF = 0 instantiates the plain kernel.
+// MB: 32-row blocks (4: up to 128 rows; 2: up to 64 rows, half the MFMAs and
+// A traffic for the tiles of small groups and the last tiles of large ones).
 template <int FMT, int EPI, int AM, int XF, int MB>
-__global__ __launch_bounds__(512) void k_mfma(GemmArgs p, int ntn, int per) {
+__device__ __forceinline__ void mfma_tile(const GemmArgs &p, uint8_t *smem, int nt, int e, int trow0,
+                                          int trows) {
   static_assert(AM == 0 || AM == 2, "operand mode");
   static_assert(MB == 4 || MB == 2, "row blocks");
   constexpr bool AF32 = AM != 0;                      // a lo part exists
   constexpr int kBM = 32 * MB;                        // rows per tile
   constexpr int ABUF = kBM * kApad * 2;               // bytes per A buffer
-  constexpr int NBUF = AF32 ? 4 : 2;                  // hi[2] (+ lo[2])
-  __shared__ __attribute__((aligned(16))) uint8_t smem[kTabBytes + NBUF * ABUF];
-
-  // XCD-aware order: hardware XCD = blockIdx.x % 8; give each XCD a contiguous
-  // run of (n-tile major, tile minor) work, so the M-tiles of one expert and
-  // one weight tile share that XCD's L2.
-  const int L = blockIdx.x;
-  const int Lp = (L & 7) * per + (L >> 3);
-  if (Lp >= p.max_tiles * ntn) return;
-  const int nt = Lp / p.max_tiles, ti = Lp % p.max_tiles;
-  if (ti >= *p.n_tiles) return;
-  const int4 tile = p.tiles[ti];  // expert, row0, rows, rows of the whole group
-  const int e = tile.x, trow0 = tile.y, trows = tile.z;
 
   build_mfma_table<FMT>(reinterpret_cast<uint4 *>(smem));
   auto abuf = [&](int hi_lo, int buf) -> uint16_t * {
@@ -132,7 +126,8 @@ __global__ __launch_bounds__(512) void k_mfma(GemmArgs p, int ntn, int per) {
 
   // A-tile slice owned by this thread for the LDS fill: row am, EPT elements
   // starting at k0 + EPT * aq. Rows past the tile read a valid row (the tile's
-  // first) and are zeroed when stored.
+  // first) and are zeroed when stored (measured: storing them unmasked, which
+  // the results would allow, made the 64-row kernels 2-3 % slower).
   constexpr int TPR = 512 / kBM;                      // fill threads per row
   constexpr int EPT = 64 / TPR;                       // elements per thread: 16 or 8
   const int am = tid / TPR, aq = tid % TPR;
@@ -380,23 +375,49 @@ __global__ __launch_bounds__(512) void k_mfma(GemmArgs p, int ntn, int per) {
   }
 }
 
-template <int FMT, int EPI, int AM, int XF, int MB>
-static hipError_t launch_mfma_mb(const GemmArgs &g, hipStream_t s) {
+// One workgroup per (weight-row tile, row tile) of the device tile table.
+// TR = 128: tiles of up to 128 rows of one expert; a tile of at most 64 rows
+// runs the 64-row body, a larger one the 128-row body (the choice is uniform
+// over the workgroup, and a row's arithmetic is the same in both). TR = 64:
+// tiles of up to 64 rows, all on the 64-row body, in a kernel holding only
+// that body (measured 4-5 % faster than the two-body kernel on such tables).
+template <int FMT, int EPI, int AM, int XF, int TR>
+__global__ __launch_bounds__(512) void k_mfma(GemmArgs p, int ntn, int per) {
+  static_assert(TR == 64 || TR == 128, "tile rows");
+  __shared__ __attribute__((aligned(16))) uint8_t smem[TR == 64 ? kTabBytes + (AM != 0 ? 4 : 2) * 64 * kApad * 2
+                                                                 : mfma_lds_bytes<AM>()];
+  // XCD-aware order: hardware XCD = blockIdx.x % 8; give each XCD a contiguous
+  // run of (n-tile major, tile minor) work, so the M-tiles of one expert and
+  // one weight tile share that XCD's L2.
+  const int L = blockIdx.x;
+  const int Lp = (L & 7) * per + (L >> 3);
+  if (Lp >= p.max_tiles * ntn) return;
+  const int nt = Lp / p.max_tiles, ti = Lp % p.max_tiles;
+  if (ti >= *p.n_tiles) return;
+  const int4 tile = p.tiles[ti];  // expert, row0, rows, rows of the whole group
+  const int rows = __builtin_amdgcn_readfirstlane(tile.z);
+  if constexpr (TR == 128) {
+    if (rows > 64) {
+      mfma_tile<FMT, EPI, AM, XF, 4>(p, smem, nt, tile.x, tile.y, rows);
+      return;
+    }
+  }
+  mfma_tile<FMT, EPI, AM, XF, 2>(p, smem, nt, tile.x, tile.y, rows);
+}
+
+template <int FMT, int EPI, int AM, int XF = 0>
+static hipError_t launch_mfma_t(const GemmArgs &g, hipStream_t s) {
+  if (g.tile_rows != 0 && g.tile_rows != 64 && g.tile_rows != kMfmaBM) return hipErrorInvalidValue;
   const int64_t ncol = (EPI == EPI_SWIGLU) ? g.N / 2 : g.N;
   const int ntn = (int)((EPI == EPI_SWIGLU) ? cdiv(ncol, 128) : cdiv(ncol, 256));
   const int64_t total = (int64_t)g.max_tiles * ntn;
   const int64_t padded = cdiv(total, 8) * 8;
   const int per = (int)(padded / 8);
-  NF4MOE_LAUNCH(g, (k_mfma<FMT, EPI, AM, XF, MB>), dim3((unsigned)padded), dim3(512), s, g, ntn, per);
+  if (g.tile_rows == 64)
+    NF4MOE_LAUNCH(g, (k_mfma<FMT, EPI, AM, XF, 64>), dim3((unsigned)padded), dim3(512), s, g, ntn, per);
+  else
+    NF4MOE_LAUNCH(g, (k_mfma<FMT, EPI, AM, XF, 128>), dim3((unsigned)padded), dim3(512), s, g, ntn, per);
   return hipGetLastError();
-}
-
-// The tile table's row count (GemmArgs::tile_rows, 128 unless set) picks MB.
-template <int FMT, int EPI, int AM, int XF = 0>
-static hipError_t launch_mfma_t(const GemmArgs &g, hipStream_t s) {
-  if (g.tile_rows == 64) return launch_mfma_mb<FMT, EPI, AM, XF, 2>(g, s);
-  if (g.tile_rows == 0 || g.tile_rows == 128) return launch_mfma_mb<FMT, EPI, AM, XF, 4>(g, s);
-  return hipErrorInvalidValue;
 }
 
 // Instantiated operand modes: SwiGLU (gate_up) and plain outputs bf16 A; slot

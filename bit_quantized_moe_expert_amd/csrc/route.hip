@@ -240,7 +240,10 @@ hipError_t launch_router_logits(const uint16_t *x, int T, int H, const float *W,
   if (T <= 0) return hipSuccess;
   if (T == 1) {  // one token: no idle token slots (the same per-token order)
     hipLaunchKernelGGL(k_logits_rows<1>, dim3(E), dim3(256), 0, s, x, T, H, W, b, E, logits);
-  } else if (rows_only) {  // the per-token order of k_logits_rows for every T
+  } else if (rows_only || T <= kRowsLogitsMaxT) {
+    // the per-token order of k_logits_rows: for every T on the small-M path,
+    // and up to kRowsLogitsMaxT tokens everywhere (below that, one launch
+    // with x read from L2 beats splitting W_r for the matrix cores)
     if (T <= 2)
       hipLaunchKernelGGL(k_logits_rows<2>, dim3(E), dim3(256), 0, s, x, T, H, W, b, E, logits);
     else if (T <= 4)
@@ -250,7 +253,7 @@ hipError_t launch_router_logits(const uint16_t *x, int T, int H, const float *W,
     else
       hipLaunchKernelGGL(k_logits_rows<32>, dim3(E, (unsigned)cdiv(T, 32)), dim3(256), 0, s, x, T, H, W,
                          b, E, logits);
-  } else if (split_ws && T >= kMfmaLogitsT && H % 32 == 0) {
+  } else if (split_ws && H % 32 == 0) {
     uint16_t *planes = reinterpret_cast<uint16_t *>(split_ws);
     const int64_t n = (int64_t)E * H;
     hipLaunchKernelGGL(k_split3, dim3((unsigned)cdiv(n, 256)), dim3(256), 0, s, W, n, planes);
@@ -525,22 +528,22 @@ __global__ __launch_bounds__(256) void k_group_scatter(const int32_t *__restrict
 }
 
 // ---------------------------------------------------------------------------
-// Small-batch routing tail (T <= kSmallT tokens, E <= kSmallE experts,
-// T * E <= kSmallTE, T * k <= 1024) in one workgroup of 1024 threads: the
-// token's logits copied to LDS, top-k + softmax by wave_topk (one wave per
+// Routing in one workgroup of 1024 threads for up to 1024 routed slots and
+// E <= kSmallE experts: the tokens' logits copied to LDS when they fit
+// (T * E <= kSmallTE, else read from L2), top-k + softmax by wave_topk (one wave per
 // token, as k_topk), then one block scan for the expert offsets, the
 // non-empty expert list and the MFMA tiles, and stable ranks by ballots.
 // ---------------------------------------------------------------------------
-constexpr int kSmallT = 32;
+constexpr int kSmallR = 1024;   // routed slots: one per thread
 constexpr int kSmallE = 256;
-constexpr int kSmallTE = 4096;  // bounds the LDS copy of the logits
+constexpr int kSmallTE = 4096;  // bounds the LDS copy of the logits (else read from L2)
 
 __global__ __launch_bounds__(1024) void k_route_tail_small(const float *__restrict__ L, int T, int E,
                                                            int k, int renorm, int bm, int max_tiles,
                                                            RouteBufs o) {
   __shared__ __attribute__((aligned(16))) float Ls[kSmallTE];
-  __shared__ int sel_id[kSmallT * kMaxTopK];
-  __shared__ float sel_w[kSmallT * kMaxTopK];
+  __shared__ int sel_id[kSmallR];
+  __shared__ float sel_w[kSmallR];
   __shared__ int cnt[kSmallE];
   __shared__ int offs[kSmallE];
   __shared__ int wcnt[16][kSmallE];  // per wave: slots routed to each expert
@@ -548,9 +551,12 @@ __global__ __launch_bounds__(1024) void k_route_tail_small(const float *__restri
   const int tid = threadIdx.x;
   const int R = T * k;
   const int Ep = (E + 3) & ~3;  // LDS row stride: 16-byte rows, padded with -inf
-  for (int i = tid; i < T * Ep; i += 1024) {
-    const int t = i / Ep, f = i - t * Ep;
-    Ls[i] = f < E ? L[(int64_t)t * E + f] : -__builtin_inff();
+  const bool in_lds = T * Ep <= kSmallTE;  // uniform
+  if (in_lds) {
+    for (int i = tid; i < T * Ep; i += 1024) {
+      const int t = i / Ep, f = i - t * Ep;
+      Ls[i] = f < E ? L[(int64_t)t * E + f] : -__builtin_inff();
+    }
   }
   for (int e = tid; e < E; e += 1024) cnt[e] = 0;
   __syncthreads();
@@ -560,12 +566,13 @@ __global__ __launch_bounds__(1024) void k_route_tail_small(const float *__restri
     for (int t = wave; t < T; t += 16) {
       int my_id;
       float wgt;
+      const float *row = in_lds ? Ls + t * Ep : L + (int64_t)t * E;
       if (E <= 64)
-        wave_topk<1>(Ls + t * Ep, E, k, renorm, my_id, wgt);
+        wave_topk<1>(row, E, k, renorm, my_id, wgt);
       else if (E <= 128)
-        wave_topk<2>(Ls + t * Ep, E, k, renorm, my_id, wgt);
+        wave_topk<2>(row, E, k, renorm, my_id, wgt);
       else
-        wave_topk<4>(Ls + t * Ep, E, k, renorm, my_id, wgt);
+        wave_topk<4>(row, E, k, renorm, my_id, wgt);
       if (lane < k) {
         sel_id[t * k + lane] = my_id;
         sel_w[t * k + lane] = wgt;
@@ -630,7 +637,7 @@ __global__ __launch_bounds__(1024) void k_route_tail_small(const float *__restri
 hipError_t launch_route(const float *logits, int T, int E, int k, int renorm, const RouteBufs &rb,
                         int bm, hipStream_t s) {
   const int R = T * k;
-  if (T <= kSmallT && E <= kSmallE && T * ((E + 3) & ~3) <= kSmallTE && R <= 1024) {
+  if (E <= kSmallE && R <= kSmallR) {
     const int max_tiles = (int)cdiv(R, bm) + (R < E ? R : E);
     hipLaunchKernelGGL(k_route_tail_small, dim3(1), dim3(1024), 0, s, logits, T, E, k, renorm, bm,
                        max_tiles, rb);

@@ -72,9 +72,11 @@ typedef enum { NF4MOE_DT_F32 = 0, NF4MOE_DT_BF16 = 1 } nf4moe_dtype_t;
 
 /* Which grouped-GEMM kernel family runs. AUTO picks from the routed row count
  * known on the host (R = T * top_k): R <= 64 (with H, I <= 4096) runs the
- * bandwidth-bound decode kernels, larger R the MFMA kernels (with 64-row tiles
- * when the groups average at most 48 rows, else 128). The other values force one family (for
- * A/B measurement and tests); the result must satisfy the same tolerance. */
+ * bandwidth-bound decode kernels, larger R the MFMA kernels (tiles of up to
+ * 64 rows of one expert when the groups average at most 48 rows, else up to
+ * 128, where a last tile of at most 64 rows runs a 64-row body). The other
+ * values force one family (for A/B measurement and tests); the result must
+ * satisfy the same tolerance. */
 typedef enum { NF4MOE_PATH_AUTO = 0, NF4MOE_PATH_SMALL_M = 1, NF4MOE_PATH_MFMA = 2 } nf4moe_path_t;
 
 /* The gate_up epilogue. SWIGLU: h = silu(g) * u, silu(g) = g / (1 + exp(-g)).
@@ -165,9 +167,10 @@ size_t nf4moe_router_workspace_bytes(int32_t E, int32_t H);
  * [T, E] (all device); fp32-accurate accumulation. The first step of the routed
  * layer (the router, outside the kernel on the pages' "Why it happens" dataflow,
  * inside this library). ws (device, caller-owned, 256-byte aligned) may be NULL;
- * with ws_bytes >= nf4moe_router_workspace_bytes(E, H), T > 32 and H % 32 == 0
+ * with ws_bytes >= nf4moe_router_workspace_bytes(E, H), T > 256 and H % 32 == 0
  * the product runs on the matrix cores (x exact in bf16, each weight as the
- * exact sum of three bf16 parts, fp32 accumulation), else on the vector ALUs.
+ * exact sum of three bf16 parts, fp32 accumulation), else on the vector ALUs
+ * (one workgroup per expert, a token's sum in the same order for every T).
  * Errors: INVALID_ARG for T < 0, E outside 1..1024, H <= 0 or H % 8, null or
  * misaligned pointers; WORKSPACE for a non-NULL ws smaller than required. */
 nf4moe_status_t nf4moe_router_logits(const uint16_t *x, int32_t T, int32_t H,
@@ -271,7 +274,8 @@ size_t nf4moe_workspace_bytes(const nf4moe_layer_t *layer, int32_t T_max);
  * Row-count invariance (the pages' STATUS page, kernel section): on the small-M
  * path (AUTO picks it for T * top_k <= 64) a token's outputs and routing carry
  * the same bits whatever the other tokens of the call; on the MFMA path, among
- * calls of 33 tokens or more; across the two they differ in summation order.
+ * calls of up to 256 tokens and among calls of more than 256 (the two router
+ * kernels); across paths they differ in summation order.
  * Errors: INVALID_ARG (layer fields, sizes, pointers), WORKSPACE (ws_bytes <
  * nf4moe_workspace_bytes(layer, T)). T == 0 is a no-op. */
 nf4moe_status_t nf4moe_moe_forward(const nf4moe_layer_t *layer, const uint16_t *x, int32_t T,
@@ -292,13 +296,16 @@ nf4moe_status_t nf4moe_moe_forward_profiled(const nf4moe_layer_t *layer, const u
 
 /* nf4moe_stream_read -- a measurement aid, not part of the layer: one launch
  * that reads `bytes` bytes of `buf` (device, 16-byte aligned, bytes a positive
- * multiple of 16) once with 16-byte loads and writes one 32-bit XOR per
- * workgroup to sink (device, nf4moe_stream_read_sink_words(bytes) words). Its
- * duration gives the plain HBM read rate of a single launch of that size, the
- * measured ceiling the decode kernels are set beside. Errors: INVALID_ARG for
- * a bad size, NULL or misaligned pointers; UNSUPPORTED past 2^31 workgroups. */
-int64_t nf4moe_stream_read_sink_words(int64_t bytes);
-nf4moe_status_t nf4moe_stream_read(const void *buf, int64_t bytes, uint32_t *sink, void *stream);
+ * multiple of 16) once with 16-byte loads, loads_per_thread (1, 2, 4, 8 or 16)
+ * of them per thread of 256-thread workgroups, and writes one 32-bit XOR per
+ * workgroup to sink (device, nf4moe_stream_read_sink_words(bytes,
+ * loads_per_thread) words). Its duration gives the plain HBM read rate of a
+ * single launch of that size, the measured ceiling the decode kernels are set
+ * beside. Errors: INVALID_ARG for a bad size or loads_per_thread, NULL or
+ * misaligned pointers; UNSUPPORTED past 2^31 workgroups. */
+int64_t nf4moe_stream_read_sink_words(int64_t bytes, int32_t loads_per_thread);
+nf4moe_status_t nf4moe_stream_read(const void *buf, int64_t bytes, int32_t loads_per_thread, uint32_t *sink,
+                                   void *stream);
 
 /* nf4moe_codebook -- host copy of the 16 fp32 decode values the kernels use for
  * `fmt` (index = 4-bit code). No device access. Returns INVALID_ARG for a bad fmt

@@ -232,9 +232,12 @@ def test_binding_refuses_mismatched_shapes():
 
 
 def test_stream_read_validation():
-    assert L.nf4moe_stream_read_sink_words(16 * 1024) == 1
-    assert L.nf4moe_stream_read_sink_words(18) == 0
-    assert L.nf4moe_stream_read(FAKE, 0, FAKE, STREAM) == INVALID
-    assert L.nf4moe_stream_read(FAKE, 24, FAKE, STREAM) == INVALID
-    assert L.nf4moe_stream_read(FAKE + 8, 32, FAKE, STREAM) == INVALID
-    assert L.nf4moe_stream_read(None, 32, FAKE, STREAM) == INVALID
+    assert L.nf4moe_stream_read_sink_words(16 * 1024, 4) == 1
+    assert L.nf4moe_stream_read_sink_words(16 * 1024, 1) == 4
+    assert L.nf4moe_stream_read_sink_words(18, 4) == 0
+    assert L.nf4moe_stream_read_sink_words(16 * 1024, 3) == 0
+    assert L.nf4moe_stream_read(FAKE, 0, 4, FAKE, STREAM) == INVALID
+    assert L.nf4moe_stream_read(FAKE, 24, 4, FAKE, STREAM) == INVALID
+    assert L.nf4moe_stream_read(FAKE, 32, 5, FAKE, STREAM) == INVALID
+    assert L.nf4moe_stream_read(FAKE + 8, 32, 4, FAKE, STREAM) == INVALID
+    assert L.nf4moe_stream_read(None, 32, 4, FAKE, STREAM) == INVALID

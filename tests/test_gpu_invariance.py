@@ -10,7 +10,8 @@ per-token order (router logits one workgroup per expert, a fixed softmax
 denominator order, GEMV rows independent of the batch, the fused token-centric
 down + combine taking the same steps as the GEMV slot output + combine), so
 the property holds for every T; on the MFMA path it holds among calls that use
-the matrix-core router (T >= 33). A property of the path at any size: the test
+the same router kernel (T <= 256: the per-token kernel; T > 256: the matrix
+cores). A property of the path at any size: the test
 compares the path with itself; the oracle bound is checked once per case.
 """
 import numpy as np
@@ -103,14 +104,19 @@ def test_olmoe_shape_row_count_invariance():
 
 
 @pytest.mark.parametrize("wl", CASES[:3], ids=lambda w: w.name)
-def test_mfma_row_count_invariance_from_33(wl):
-    """Forced MFMA path: calls of 33 tokens and more share the router kernel,
-    and a routed row's MFMA result does not depend on the rows sharing its tile."""
+def test_mfma_row_count_invariance_per_router_window(wl):
+    """Forced MFMA path: calls of up to 256 tokens share the per-token router
+    kernel (and calls of more than 256 the matrix-core router), and a routed
+    row's MFMA result does not depend on the rows sharing its tile or on the
+    tile height (64- or 128-row bodies)."""
     layer, _, _ = build_layers(wl, 0, DEV, path=M.PATH_MFMA)
-    X = S.make_x(wl, 300)
+    X = S.make_x(wl, 600)
+    upto = _run(layer, X[:256])
+    for T in (1, 33, 40, 177):
+        _same(_run(layer, X[:T]), tuple(f[:T] for f in upto), f"{wl.name} MFMA: first {T} of 256")
     full = _run(layer, X)
-    for T in (33, 40, 177):
-        _same(_run(layer, X[:T]), tuple(f[:T] for f in full), f"{wl.name} MFMA: first {T} of 300")
+    for T in (257, 300, 411):
+        _same(_run(layer, X[:T]), tuple(f[:T] for f in full), f"{wl.name} MFMA: first {T} of 600")
 
 
 def test_small_m_grouped_gemm_rows_independent():

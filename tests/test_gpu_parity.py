@@ -341,9 +341,11 @@ def test_forward_rejects_bad_glu():
 @pytest.mark.parametrize("fmt", [O.FMT_NF4, O.FMT_MXFP4])
 @pytest.mark.parametrize("T", [800, 1000])
 def test_forward_mfma_tile_heights(fmt, T):
-    """Both MFMA tile heights: ~200 and ~250 rows per expert take 128-row tiles,
-    the same shapes with 16x the experts take 64-row tiles."""
-    for E in (4, 64):
+    """Both MFMA tile bodies: 3 or 4 experts (about 170-330 rows each) take a
+    128-row table, with full tiles on the 128-row body and last tiles on
+    either body; 64 experts take a 64-row table, every tile on the 64-row
+    body."""
+    for E in (3, 4, 64):
         wl = S.custom(E=E, top_k=1, H=256, I=128, fmt=fmt, wid=70 + E)
         _forward_case(wl, T, M.PATH_MFMA, sample=[0, T // 2, T - 1])
 
