@@ -78,6 +78,7 @@ def lib() -> ctypes.CDLL:
         "nf4moe_grouped_dgrad": [ctypes.c_int, vp, vp, vp, i32, i64, i64, i32, vp, vp, i32, vp,
                                  ctypes.c_int, vp, sz, vp],
         "nf4moe_moe_forward": [ctypes.POINTER(Layer), vp, i32, vp, vp, vp, vp, sz, vp],
+        "nf4moe_moe_forward_noalloc": [ctypes.POINTER(Layer), vp, i32, vp, vp, vp, vp],
         "nf4moe_moe_forward_profiled": [ctypes.POINTER(Layer), vp, i32, vp, vp, sz, vp,
                                         ctypes.POINTER(ctypes.c_void_p)],
         "nf4moe_codebook": [ctypes.c_int, ctypes.POINTER(ctypes.c_float)],
@@ -473,6 +474,26 @@ def check_forward_args(layer: MoELayer, x, out=None, topk_ids=None, topk_w=None)
     _shape(out, "out", (T, layer.H))
     _shape(topk_ids, "topk_ids", (T, layer.top_k))
     _shape(topk_w, "topk_w", (T, layer.top_k))
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20
+
+
+def moe_forward_noalloc(layer: MoELayer, x, out, topk_ids=None, topk_w=None):
+    """The layer through nf4moe_moe_forward_noalloc: no workspace, the library's
+    per-device scratch (NOALLOC_SCRATCH_BYTES); the caller passes every output."""
+    torch = _torch()
+    check_forward_args(layer, x, out, topk_ids, topk_w)
+    st = layer.struct()
+    _dev(x, "x", torch.bfloat16)
+    _dev(out, "out", torch.bfloat16)
+    if topk_ids is not None:
+        _dev(topk_ids, "topk_ids", torch.int32)
+    if topk_w is not None:
+        _dev(topk_w, "topk_w", torch.float32)
+    _check(lib().nf4moe_moe_forward_noalloc(ctypes.byref(st), _ptr(x), x.shape[0], _ptr(out), _ptr(topk_ids),
+                                            _ptr(topk_w), _stream()))
+    return out
 
 
 def moe_forward(layer: MoELayer, x, return_routing: bool = False):

@@ -5,12 +5,20 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/nf4moe.h"
 #include "common.h"
 #include "dgrad.h"
 #include "internal.h"
 
 using namespace nf4moe;
+
+// Scratch of the allocation-free forward (nf4moe_moe_forward_noalloc): a
+// file-scope device array that every GPU the library runs on holds until the
+// process ends. Host code never uses its name as an address; it uses the
+// per-device address hipGetSymbolAddress returns.
+static __device__ __align__(256) uint8_t scratch[NF4MOE_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -154,6 +162,29 @@ nf4moe_status_t check_layer(const nf4moe_layer_t *L) {
     return fail(NF4MOE_ERR_INVALID_ARG, "glu_interleaved must be 0 or 1");
   if ((L->b13 && !aligned(L->b13, 4)) || (L->b2 && !aligned(L->b2, 4)))
     return fail(NF4MOE_ERR_INVALID_ARG, "b13/b2 must be 4-byte aligned");
+  return NF4MOE_OK;
+}
+
+// Device address of `scratch` on the current device, looked up once per device
+// (with that device current) and kept.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+nf4moe_status_t noalloc_scratch(void **out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(NF4MOE_ERR_UNSUPPORTED, "device %d beyond %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress(scratch)");
+    if (!ptr || !aligned(ptr, 256)) return fail(NF4MOE_ERR_HIP, "scratch address %p not 256-byte aligned", ptr);
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
   return NF4MOE_OK;
 }
 
@@ -569,6 +600,29 @@ nf4moe_status_t nf4moe_moe_forward(const nf4moe_layer_t *layer, const uint16_t *
                                    uint16_t *out, int32_t *topk_ids_out, float *topk_w_out,
                                    void *ws, size_t ws_bytes, void *stream) {
   return forward_impl(layer, x, T, out, topk_ids_out, topk_w_out, ws, ws_bytes, stream, nullptr);
+}
+
+nf4moe_status_t nf4moe_moe_forward_noalloc(const nf4moe_layer_t *layer, const uint16_t *x, int32_t T,
+                                           uint16_t *out, int32_t *topk_ids_out, float *topk_w_out,
+                                           void *stream) {
+  nf4moe_status_t st = check_layer(layer);
+  if (st != NF4MOE_OK) return st;
+  if (T < 0) return fail(NF4MOE_ERR_INVALID_ARG, "T=%d < 0", T);
+  if (T == 0) return NF4MOE_OK;
+  if ((int64_t)T * layer->top_k > (int64_t)1 << 30) return fail(NF4MOE_ERR_UNSUPPORTED, "T*top_k too large");
+  const size_t need = carve_forward(nullptr, *layer, T).bytes;
+  if (need > (size_t)NF4MOE_NOALLOC_SCRATCH_BYTES)
+    return fail(NF4MOE_ERR_WORKSPACE,
+                "this layer at T=%d needs %zu bytes of scratch; the allocation-free forward holds %zu "
+                "(call nf4moe_moe_forward with a workspace instead)",
+                T, need, (size_t)NF4MOE_NOALLOC_SCRATCH_BYTES);
+  void *ws = nullptr;
+  st = noalloc_scratch(&ws);
+  if (st != NF4MOE_OK) return st;
+  // Nothing in the scratch needs to start at zero: within one call every
+  // kernel writes what it later reads.
+  return forward_impl(layer, x, T, out, topk_ids_out, topk_w_out, ws, NF4MOE_NOALLOC_SCRATCH_BYTES, stream,
+                      nullptr);
 }
 
 nf4moe_status_t nf4moe_moe_forward_profiled(const nf4moe_layer_t *layer, const uint16_t *x,

@@ -282,6 +282,28 @@ nf4moe_status_t nf4moe_moe_forward(const nf4moe_layer_t *layer, const uint16_t *
                                    uint16_t *out, int32_t *topk_ids_out, float *topk_w_out,
                                    void *ws, size_t ws_bytes, void *stream);
 
+/* nf4moe_moe_forward_noalloc -- nf4moe_moe_forward for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): no workspace argument; the scratch is a
+ * library-owned device array of NF4MOE_NOALLOC_SCRATCH_BYTES (32 MiB) that each
+ * GPU the library runs on holds until the process ends, looked up on the
+ * first call on that device. The call allocates nothing and uses the scratch
+ * of the device current on the calling thread (the stream must belong to it).
+ * Same kernels and the same results, bit for bit, as nf4moe_moe_forward with a
+ * workspace; nothing in the scratch has to start at zero.
+ * Limit: layers and token counts with nf4moe_workspace_bytes(layer, T) <=
+ * NF4MOE_NOALLOC_SCRATCH_BYTES (an OLMoE-1B-7B-shaped layer, E=64, top_k=8,
+ * H=2048, I=1024, up to 331 tokens); larger calls return WORKSPACE and enqueue
+ * nothing.
+ * Every call on one GPU shares that GPU's scratch, which keeps the last call's
+ * contents: calls on one stream are ordered, but calls that can overlap on one
+ * GPU (several streams or threads) race and must be serialised by the caller.
+ * Errors as for nf4moe_moe_forward. */
+#define NF4MOE_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+nf4moe_status_t nf4moe_moe_forward_noalloc(const nf4moe_layer_t *layer, const uint16_t *x, int32_t T,
+                                           uint16_t *out, int32_t *topk_ids_out, float *topk_w_out,
+                                           void *stream);
+
 /* nf4moe_moe_forward_profiled -- nf4moe_moe_forward (same kernels, same result,
  * no topk copies) that also uses six caller-created timing HIP events
  * (hipEvent_t, hipEventDefault flags) on `stream`: events[0] is recorded before
