@@ -298,6 +298,9 @@ nf4moe_status_t nf4moe_moe_forward(const nf4moe_layer_t *layer, const uint16_t *
  * Every call on one GPU shares that GPU's scratch, which keeps the last call's
  * contents: calls on one stream are ordered, but calls that can overlap on one
  * GPU (several streams or threads) race and must be serialised by the caller.
+ * The scratch address lookup is a runtime query, not a stream operation; a
+ * caller that captures this call into a graph can make one eager call on each
+ * device first so that the capture holds kernel launches only.
  * Errors as for nf4moe_moe_forward. */
 #define NF4MOE_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
 nf4moe_status_t nf4moe_moe_forward_noalloc(const nf4moe_layer_t *layer, const uint16_t *x, int32_t T,
