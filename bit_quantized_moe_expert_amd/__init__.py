@@ -68,7 +68,7 @@ def lib() -> ctypes.CDLL:
         "nf4moe_dequantize": [ctypes.c_int, vp, vp, i64, i64, vp, vp],
         "nf4moe_absmax_to_bf16": [vp, i64, vp, vp, vp],
         "nf4moe_router_logits": [vp, i32, i32, vp, vp, i32, vp, vp, sz, vp],
-        "nf4moe_router_workspace_bytes": [i32, i32],
+        "nf4moe_router_workspace_bytes": [i32, i32, i32],
         "nf4moe_route_workspace_bytes": [i32, i32, i32],
         "nf4moe_route_permute": [vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp],
         "nf4moe_gemm_workspace_bytes": [i32, i32],
@@ -235,7 +235,8 @@ def absmax_to_bf16(absmax):
 def router_logits(x, router_w, router_b=None, matrix_cores: bool = True):
     """x bf16 [T, H], W_r fp32 [E, H] (+ b [E]) -> logits fp32 [T, E].
     matrix_cores: hand the library the workspace that enables its MFMA kernel
-    (used for T > 256, H % 32 == 0); False keeps the vector-ALU kernels."""
+    (H % 16 == 0; the logits the forward's MFMA path routes on); False keeps
+    the vector-ALU kernels (the small-M path's logits up to 256 tokens)."""
     torch = _torch()
     _shape(x, "x", (None, None))
     T, H = x.shape
@@ -248,9 +249,10 @@ def router_logits(x, router_w, router_b=None, matrix_cores: bool = True):
         _dev(router_b, "router_b", torch.float32)
     out = torch.empty(T, E, dtype=torch.float32, device=x.device)
     ws, nb = None, 0
-    if matrix_cores:
-        nb = lib().nf4moe_router_workspace_bytes(E, H)
-        ws = torch.empty(nb, dtype=torch.uint8, device=x.device)
+    if matrix_cores and T > 0:
+        nb = lib().nf4moe_router_workspace_bytes(T, E, H)
+        if nb:
+            ws = torch.empty(nb, dtype=torch.uint8, device=x.device)
     _check(lib().nf4moe_router_logits(_ptr(x), T, H, _ptr(router_w), _ptr(router_b), E, _ptr(out),
                                       _ptr(ws), nb, _stream()))
     return out

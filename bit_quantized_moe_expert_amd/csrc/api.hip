@@ -104,8 +104,8 @@ void carve_route_scratch(Carve &cv, const RoutePlan &rp, int E, RouteBufs &rb) {
 }
 
 struct ForwardCarve {
-  float *logits;
-  uint16_t *rsplit;  // router weight bf16 planes (T > kRowsLogitsMaxT), else null
+  float *logits;     // [T, E] logits (small-M path), or the first of the router's
+  float *partials;   //   partial sums [S][T][E] (MFMA path): the same memory
   RouteBufs rb;
   float *h;
   float *slotbuf;
@@ -116,7 +116,8 @@ ForwardCarve carve_forward(void *ws, const nf4moe_layer_t &L, int T) {
   ForwardCarve fc;
   const RoutePlan rp = route_plan(T, L.E, L.top_k);
   Carve cv(ws);
-  fc.logits = cv.take<float>((size_t)(T > 0 ? T : 1) * L.E);
+  fc.partials = cv.take<float>(router_partials_bytes(T, L.E, L.H) / sizeof(float));
+  fc.logits = fc.partials;
   fc.rb.topk_ids = cv.take<int32_t>(rp.R > 0 ? rp.R : 1);
   fc.rb.topk_w = cv.take<float>(rp.R > 0 ? rp.R : 1);
   fc.rb.expert_offsets = cv.take<int32_t>(L.E + 1);
@@ -124,7 +125,6 @@ ForwardCarve carve_forward(void *ws, const nf4moe_layer_t &L, int T) {
   carve_route_scratch(cv, rp, L.E, fc.rb);
   fc.h = cv.take<float>((size_t)(rp.R > 0 ? rp.R : 1) * L.I);
   fc.slotbuf = cv.take<float>((size_t)(rp.R > 0 ? rp.R : 1) * L.H);
-  fc.rsplit = T > kRowsLogitsMaxT ? cv.take<uint16_t>(router_split_bytes(L.E, L.H) / sizeof(uint16_t)) : nullptr;
   fc.bytes = align_up(cv.off);
   return fc;
 }
@@ -261,9 +261,9 @@ nf4moe_status_t nf4moe_dequantize(nf4moe_format_t fmt, const uint8_t *packed, co
                     "dequantize launch");
 }
 
-size_t nf4moe_router_workspace_bytes(int32_t E, int32_t H) {
-  if (E < 1 || H <= 0) return 0;
-  return align_up(router_split_bytes(E, H));
+size_t nf4moe_router_workspace_bytes(int32_t T, int32_t E, int32_t H) {
+  if (T < 1 || E < 1 || H <= 0 || H % 16) return 0;
+  return align_up(router_partials_bytes(T, E, H));
 }
 
 nf4moe_status_t nf4moe_router_logits(const uint16_t *x, int32_t T, int32_t H,
@@ -276,12 +276,14 @@ nf4moe_status_t nf4moe_router_logits(const uint16_t *x, int32_t T, int32_t H,
   if (!x || !router_w || !logits) return fail(NF4MOE_ERR_INVALID_ARG, "NULL pointer");
   if (!aligned(x, 16) || !aligned(router_w, 16) || !aligned(logits, 4))
     return fail(NF4MOE_ERR_INVALID_ARG, "misaligned pointer");
-  if (ws) {
-    if (ws_bytes < router_split_bytes(E, H))
-      return fail(NF4MOE_ERR_WORKSPACE, "workspace %zu bytes < %zu required", ws_bytes, router_split_bytes(E, H));
+  float *partials = nullptr;
+  if (ws && H % 16 == 0) {
+    const size_t need = router_partials_bytes(T, E, H);
+    if (ws_bytes < need) return fail(NF4MOE_ERR_WORKSPACE, "workspace %zu bytes < %zu required", ws_bytes, need);
     if (!aligned(ws, 256)) return fail(NF4MOE_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+    partials = static_cast<float *>(ws);
   }
-  return hip_status(launch_router_logits(x, T, H, router_w, router_b, E, logits, ws, (hipStream_t)stream),
+  return hip_status(launch_router_logits(x, T, H, router_w, router_b, E, logits, partials, (hipStream_t)stream),
                     "router launch");
 }
 
@@ -496,14 +498,22 @@ static nf4moe_status_t forward_impl(const nf4moe_layer_t *layer, const uint16_t 
   if ((e = mark(0)) != hipSuccess) return hip_status(e, "event record");
   // The small-M path keeps each token's bits independent of T: per-token
   // router logits for every T, and kernels whose per-row order is fixed.
+  // Routing logits: the rows kernel on the small-M path and for few tokens on
+  // the MFMA path, else the matrix-core router; each has a fixed per-token
+  // order (the latter sums fixed chunks of H in order), so a token's bits do
+  // not depend on T within each of them.
   const bool small = use == NF4MOE_PATH_SMALL_M;
-  e = launch_router_logits(x, T, L.H, L.router_w, L.router_b, L.E, fc.logits, fc.rsplit, s, small);
+  const bool rows_router = small || T <= kMfmaRowsRouterMaxT;
+  e = rows_router ? launch_router_rows(x, T, L.H, L.router_w, L.router_b, L.E, fc.logits, s)
+                  : launch_router_partials(x, T, L.H, L.router_w, L.E, fc.partials, s);
   if (e != hipSuccess) return hip_status(e, "router launch");
   // One decode token on the small-M path: top-k and grouping happen inside the
   // gate_up kernel; otherwise they are their own launches.
   const bool fused_route = use == NF4MOE_PATH_SMALL_M && T == 1 && L.E <= 128;
   if (!fused_route) {
-    e = launch_route(fc.logits, T, L.E, L.top_k, L.renormalize, fc.rb, rp.tile_rows, s);
+    e = rows_router ? launch_route(fc.logits, T, L.E, L.top_k, L.renormalize, fc.rb, rp.tile_rows, s)
+                    : launch_route_partials(fc.partials, router_split(L.H), L.router_b, T, L.E, L.top_k,
+                                            L.renormalize, fc.rb, rp.tile_rows, s);
     if (e != hipSuccess) return hip_status(e, "route launch");
   }
   if ((e = mark(1)) != hipSuccess) return hip_status(e, "event record");

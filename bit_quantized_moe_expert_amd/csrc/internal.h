@@ -36,20 +36,37 @@ hipError_t launch_dequantize(int fmt, const uint8_t *packed, const void *scale, 
                              int64_t K, float *out, hipStream_t s);
 hipError_t launch_absmax_bf16(const float *a, int64_t n, uint16_t *out, int32_t *inexact, hipStream_t s);
 
-// Router logits. With split_ws (>= router_split_bytes(E, H) bytes, 256-byte
-// aligned) and T > kRowsLogitsMaxT, H % 32 == 0: the matrix-core kernel.
-// rows_only: the one-workgroup-per-expert kernel for every T, so each token's
-// logits have the same bits whatever T (the small-M path's contract).
-// Up to this many tokens every router call uses the one-workgroup-per-expert
-// kernel (the small-M path uses it for every T).
+// Router logits. launch_router_rows: one workgroup per expert (and 32-token
+// chunk), each token's sum in the same order for every T (the small-M path's
+// router). launch_router_partials: the matrix-core router, H split into
+// router_split(H) chunks of router_chunk(H) (H % 16 == 0), writing the partial
+// sums P[s][t][e] (router_partials_bytes); a token's partials depend on its
+// own row only. launch_router_logits: logits [T, E] from the partials
+// (summed in chunk order, then the bias) when `partials` is given, else from
+// the rows kernel up to kRowsLogitsMaxT tokens and an fp32 tiled kernel above.
+constexpr int kRouterSplit = 8;
+// The MFMA path routes up to this many tokens on the rows kernel (router +
+// one-workgroup top-k and grouping: two launches; measured at 16 Qwen3-shaped
+// tokens, 17 us of routing against 23 us for the matrix-core router, its
+// partial sums and the same grouping); above it, on the matrix-core router.
+constexpr int kMfmaRowsRouterMaxT = 16;
 constexpr int kRowsLogitsMaxT = 256;
-size_t router_split_bytes(int E, int H);
+int router_split(int H);
+int router_chunk(int H);
+size_t router_partials_bytes(int T, int E, int H);
+hipError_t launch_router_rows(const uint16_t *x, int T, int H, const float *W, const float *b, int E,
+                              float *logits, hipStream_t s);
+hipError_t launch_router_partials(const uint16_t *x, int T, int H, const float *W, int E, float *P,
+                                  hipStream_t s);
 hipError_t launch_router_logits(const uint16_t *x, int T, int H, const float *W, const float *b,
-                                int E, float *logits, void *split_ws, hipStream_t s,
-                                bool rows_only = false);
-// top-k + softmax, then grouping. Fills every RouteBufs field.
+                                int E, float *logits, float *partials, hipStream_t s);
+// top-k + softmax, then grouping. Fills every RouteBufs field. From given
+// logits [T, E], or from router partials (S of them, T * E apart, summed in
+// order, then + bias).
 hipError_t launch_route(const float *logits, int T, int E, int k, int renorm, const RouteBufs &rb,
                         int bm, hipStream_t s);
+hipError_t launch_route_partials(const float *partials, int S, const float *bias, int T, int E, int k,
+                                 int renorm, const RouteBufs &rb, int bm, hipStream_t s);
 // Fill n int32 with v (a kernel, so the sequence stays graph-capturable).
 hipError_t launch_fill_i32(int32_t *p, int n, int v, hipStream_t s);
 // Groups and tiles from caller-given group offsets / experts.

@@ -139,19 +139,23 @@ __device__ __forceinline__ void mfma_tile(const GemmArgs &p, uint8_t *smem, int 
     arow = arow < 0 ? 0 : (arow < p.a_rows ? arow : p.a_rows - 1);  // a bad index cannot read past a
   }
   constexpr int AW = EPT * (AF32 ? 4 : 2) / 16;       // 16-byte words per thread
-  uint4 areg[AW];
-  bool a_ok = false;
-  auto load_a = [&](int64_t k0) {
+  // Two register sets: the slice for K-step k + 2 is loaded while the one for
+  // k + 1 (loaded a step earlier) waits to be stored to LDS.
+  uint4 aregs[2][AW];
+  bool aoks[2] = {false, false};
+  auto load_a = [&](int64_t k0, int set) {
     const int64_t kk = k0 + EPT * aq;
-    a_ok = arow_ok && kk < K;
+    aoks[set] = arow_ok && kk < K;
     const int64_t kc = kk < K ? kk : 0;
     // AM 0: EPT bf16; AM 2: EPT (hi, lo) bf16 pairs, 4 bytes each
     const uint4 *src = reinterpret_cast<const uint4 *>(reinterpret_cast<const uint8_t *>(p.a) +
                                                        (arow * K + kc) * (AM == 2 ? 4 : 2));
 #pragma unroll
-    for (int i = 0; i < AW; ++i) areg[i] = src[i];
+    for (int i = 0; i < AW; ++i) aregs[set][i] = src[i];
   };
-  auto store_a = [&](int buf) {
+  auto store_a = [&](int buf, int set) {
+    const uint4 *areg = aregs[set];
+    const bool a_ok = aoks[set];
     uint16_t *dh = abuf(0, buf) + am * kApad + EPT * aq;
     if (AM == 2) {  // de-interleave the pairs into the hi and lo tiles
       uint16_t *dl = abuf(1, buf) + am * kApad + EPT * aq;
@@ -195,15 +199,17 @@ __device__ __forceinline__ void mfma_tile(const GemmArgs &p, uint8_t *smem, int 
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) C[mb] = zero16;
 
-  // One K-step on LDS buffer `cur` with codes bq and scale bs, prefetching
-  // the next step into (bqn, brn, bokn) and the other LDS buffer.
-  auto step = [&](int64_t k0, int cur, const uint4 &bq, float bs, uint4 &bqn, uint32_t &brn, bool &bokn) {
-    // Next step's loads fly while this step computes. They are issued (from
-    // clamped, valid addresses) and stored even after the last step, so no
-    // branch splits the load/wait bookkeeping; the extra buffer is unused.
+  // One K-step on LDS buffer `cur` with codes bq and scale bs. Loads run two
+  // steps ahead: the activation slice of step k + 2 into register set `aset`
+  // at the start, the codes and scale of step k + 2 into bq / br / bok once
+  // this step's lookups have read bq; the slice of step k + 1 (set aset ^ 1)
+  // goes to the other LDS buffer at the end.
+  auto step = [&](int64_t k0, int cur, int aset, uint4 &bq, float bs, uint32_t &br, bool &bok) {
+    // Loads are issued (from clamped, valid addresses) and stored even past
+    // the last step, so no branch splits the load/wait bookkeeping; the
+    // extra data is unused.
     const bool more = k0 + kBK < K;
-    load_a(k0 + kBK);
-    load_b(k0 + kBK, bqn, brn, bokn);
+    load_a(k0 + 2 * kBK, aset);
     __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the MFMAs
     const uint16_t *Ah = abuf(0, cur);
     const uint16_t *Al = abuf(1, AF32 ? cur : 0);
@@ -235,6 +241,10 @@ __device__ __forceinline__ void mfma_tile(const GemmArgs &p, uint8_t *smem, int 
           t[sn & 1][q] = *reinterpret_cast<const uint2 *>(smem + tab_offset(word, lanebyte, q));
       }
       __builtin_amdgcn_sched_barrier(0);
+      if (u == 3) {  // every lookup of this step has read bq: reuse it for step k + 2
+        load_b(k0 + 2 * kBK, bq, br, bok);
+        __builtin_amdgcn_sched_barrier(0);
+      }
       if (u >= 0) {
         const int s = u;
         if (AF32) read_a(s, ah[0], al[0]);
@@ -285,7 +295,7 @@ __device__ __forceinline__ void mfma_tile(const GemmArgs &p, uint8_t *smem, int 
         for (int v = 0; v < 16; ++v) C[mb][v] = fmaf(bs, P[mb][v], C[mb][v]);
     }
     __builtin_amdgcn_sched_barrier(0);  // the A store waits for its loads: keep it last
-    store_a(cur ^ 1);
+    store_a(cur ^ 1, aset ^ 1);
     lds_barrier();
     return more;
   };
@@ -293,17 +303,21 @@ __device__ __forceinline__ void mfma_tile(const GemmArgs &p, uint8_t *smem, int 
   uint4 bq0, bq1;
   uint32_t br0, br1;
   bool bok0, bok1;
-  load_a(0);
+  load_a(0, 0);
   load_b(0, bq0, br0, bok0);
-  store_a(0);
+  load_a(kBK, 1);
+  load_b(kBK, bq1, br1, bok1);
+  store_a(0, 0);
   lds_barrier();
   float bs0 = scale_of(br0, bok0), bs1;
 
-  // Unrolled by two so the register sets alternate without copies.
+  // Unrolled by two so the register sets alternate without copies: step k
+  // computes on B set k % 2 and LDS buffer k % 2, loads A(k + 2) into set
+  // k % 2 and stores A(k + 1) from set (k + 1) % 2.
   for (int64_t k0 = 0;; k0 += 2 * kBK) {
-    if (!step(k0, 0, bq0, bs0, bq1, br1, bok1)) break;
+    if (!step(k0, 0, 0, bq0, bs0, br0, bok0)) break;
     bs1 = scale_of(br1, bok1);
-    if (!step(k0 + kBK, 1, bq1, bs1, bq0, br0, bok0)) break;
+    if (!step(k0 + kBK, 1, 1, bq1, bs1, br1, bok1)) break;
     bs0 = scale_of(br0, bok0);
   }
 

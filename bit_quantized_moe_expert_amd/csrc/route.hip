@@ -82,90 +82,145 @@ __global__ __launch_bounds__(256) void k_logits_rows(const uint16_t *__restrict_
 }
 
 // ---------------------------------------------------------------------------
-// Router logits, many tokens, on the matrix cores. x is bf16, an exact MFMA
-// operand. Each fp32 router weight is split exactly into three bf16 parts
-// w = w1 + w2 + w3 (w1 = w truncated to bf16, w2 = the remainder truncated,
-// w3 = what is left, at most 8 significant bits), so three bf16 products
-// accumulated in fp32 give the fp32 dot product.
-// k_split3: the three planes [3][E][H] (bf16 bits) from router_w.
-// k_logits_mfma: 32 tokens x 32 experts per workgroup, eight waves taking one
-// eighth of H each, loads issued eight k-steps ahead (their partial sums meet
-// in LDS, in a fixed order).
+// Router logits on the matrix cores, H split into S chunks. Each wave takes
+// one unit (32 tokens, 32 experts, one chunk) and writes the chunk's partial
+// sums P[s][t][e]; a consumer adds the S partials in chunk order (then the
+// bias), so a token's logit depends on its own row only: the same bits for
+// every T and every tile position. x is bf16, an exact MFMA operand; each fp32
+// router weight is split in registers into three bf16 parts w = w1 + w2 + w3
+// (w1 = w truncated to bf16, w2 = the remainder truncated, w3 = what is left,
+// at most 8 significant bits: exact for weights of normal range), and the
+// three products accumulate in fp32 in three accumulators, added at the end.
+// The four waves of a workgroup are consecutive units (expert tile fastest),
+// so with E <= 128 they share one x chunk through L1.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_split3(const float *__restrict__ W, int64_t n,
-                                                uint16_t *__restrict__ planes) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= n) return;
-  const uint32_t w = __float_as_uint(W[i]);
-  const uint32_t p1 = w >> 16;
-  const float r1 = __uint_as_float(w) - __uint_as_float(p1 << 16);
-  const uint32_t p2 = __float_as_uint(r1) >> 16;
-  const float r2 = r1 - __uint_as_float(p2 << 16);
-  planes[i] = (uint16_t)p1;
-  planes[n + i] = (uint16_t)p2;
-  planes[2 * n + i] = (uint16_t)(__float_as_uint(r2) >> 16);
-}
-
 typedef __bf16 lg_bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float lg_f32x16_t __attribute__((ext_vector_type(16)));
 
-__global__ __launch_bounds__(512) void k_logits_mfma(const uint16_t *__restrict__ x, int T, int H,
-                                                     const uint16_t *__restrict__ planes,
-                                                     const float *__restrict__ b, int E,
-                                                     float *__restrict__ L) {
-  constexpr int NW = 8, BATCH = 8;
-  __shared__ float red[NW - 1][16][64];
+int router_split(int H) {
+  const int steps = H / 16;                       // H % 16 == 0
+  const int s = steps < kRouterSplit ? steps : kRouterSplit;
+  const int chunk = (int)cdiv(steps, s) * 16;
+  return (int)cdiv(H, chunk);
+}
+int router_chunk(int H) {
+  const int steps = H / 16;
+  const int s = steps < kRouterSplit ? steps : kRouterSplit;
+  return (int)cdiv(steps, s) * 16;
+}
+
+// (hi halves of a and b) as one word: the truncated bf16 of two floats
+__device__ inline uint32_t pack_hi16(uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_perm(b, a, 0x07060302u);
+}
+
+__global__ __launch_bounds__(256) void k_logits_ks(const uint16_t *__restrict__ x, int T, int H,
+                                                   const float *__restrict__ W, int E, int chunk,
+                                                   int S, float *__restrict__ P) {
+  constexpr int B = 8;  // k-steps of 16 whose loads are issued together
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int ET = (E + 31) >> 5;
+  const int64_t u = (int64_t)blockIdx.x * 4 + wave;
+  const int et = (int)(u % ET);
+  const int64_t r = u / ET;
+  const int s = (int)(r % S);
+  const int64_t tt = r / S;
+  if (tt * 32 >= T) return;  // uniform over the wave
   const int g = lane >> 5, l32 = lane & 31;
-  const int t = blockIdx.x * 32 + l32, e = blockIdx.y * 32 + l32;
-  const int64_t xrow = t < T ? t : 0, wrow = e < E ? e : 0;
-  const int64_t n = (int64_t)E * H;
-  // wave w takes k-steps [s0, s1) of 16 (H % 32 == 0)
-  const int nsteps = H / 16;
-  const int s0 = wave * nsteps / NW, s1 = (wave + 1) * nsteps / NW;
+  const int64_t t = tt * 32 + l32;
+  const int e = et * 32 + l32;
+  const int64_t xrow = t < T ? t : T - 1;   // rows past the end compute on a valid row, never stored
+  const int64_t wrow = e < E ? e : E - 1;
+  const int kb = s * chunk, ke = kb + chunk < H ? kb + chunk : H;
   const uint16_t *xa = x + xrow * H + 8 * g;
-  const uint16_t *wa = planes + wrow * H + 8 * g;
-  lg_f32x16_t acc = {};
-  for (int sb = s0; sb < s1; sb += BATCH) {
-    uint4 a[BATCH], b1[BATCH], b2[BATCH], b3[BATCH];
+  const float *wa = W + wrow * H + 8 * g;
+  lg_f32x16_t c1 = {}, c2 = {}, c3 = {};
+  for (int k0 = kb; k0 < ke; k0 += 16 * B) {
+    uint4 av[B];
+    float4 w0[B], w1[B];
 #pragma unroll
-    for (int i = 0; i < BATCH; ++i) {      // the batch's loads first (clamped to the range)
-      const int st = sb + i < s1 ? sb + i : s1 - 1;
-      a[i] = *reinterpret_cast<const uint4 *>(xa + 16 * st);
-      b1[i] = *reinterpret_cast<const uint4 *>(wa + 16 * st);
-      b2[i] = *reinterpret_cast<const uint4 *>(wa + n + 16 * st);
-      b3[i] = *reinterpret_cast<const uint4 *>(wa + 2 * n + 16 * st);
+    for (int i = 0; i < B; ++i) {  // clamped to the chunk's last step: always in bounds
+      const int k = k0 + 16 * i < ke ? k0 + 16 * i : ke - 16;
+      av[i] = *reinterpret_cast<const uint4 *>(xa + k);
+      w0[i] = *reinterpret_cast<const float4 *>(wa + k);
+      w1[i] = *reinterpret_cast<const float4 *>(wa + k + 4);
+    }
+    // Every step of the batch is computed; a step past the chunk (the last
+    // batch of a chunk that is not a multiple of 16 * B) has its activation
+    // operand zeroed. The mask is opaque to the compiler: with a branch per
+    // step instead, it sinks each step's loads into the branch, and the
+    // steps become one memory round trip each.
+#pragma unroll
+    for (int i = 0; i < B; ++i) {
+      uint32_t keep = k0 + 16 * i < ke ? 0xffffffffu : 0u;
+      asm volatile("" : "+v"(keep));
+      av[i].x &= keep;
+      av[i].y &= keep;
+      av[i].z &= keep;
+      av[i].w &= keep;
     }
 #pragma unroll
-    for (int i = 0; i < BATCH; ++i) {
-      if (sb + i < s1) {
-        const lg_bf16x8_t av = __builtin_bit_cast(lg_bf16x8_t, a[i]);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, __builtin_bit_cast(lg_bf16x8_t, b1[i]), acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, __builtin_bit_cast(lg_bf16x8_t, b2[i]), acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, __builtin_bit_cast(lg_bf16x8_t, b3[i]), acc, 0, 0, 0);
+    for (int i = 0; i < B; ++i) {
+      const float wf[8] = {w0[i].x, w0[i].y, w0[i].z, w0[i].w, w1[i].x, w1[i].y, w1[i].z, w1[i].w};
+      uint32_t q1[8], q2[8], q3[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t b0 = __float_as_uint(wf[j]);
+        const float r1 = wf[j] - __uint_as_float(b0 & 0xffff0000u);
+        const uint32_t b1 = __float_as_uint(r1);
+        const float r2 = r1 - __uint_as_float(b1 & 0xffff0000u);
+        q1[j] = b0;
+        q2[j] = b1;
+        q3[j] = __float_as_uint(r2);
       }
+      uint4 p1, p2, p3;
+      p1.x = pack_hi16(q1[0], q1[1]); p1.y = pack_hi16(q1[2], q1[3]);
+      p1.z = pack_hi16(q1[4], q1[5]); p1.w = pack_hi16(q1[6], q1[7]);
+      p2.x = pack_hi16(q2[0], q2[1]); p2.y = pack_hi16(q2[2], q2[3]);
+      p2.z = pack_hi16(q2[4], q2[5]); p2.w = pack_hi16(q2[6], q2[7]);
+      p3.x = pack_hi16(q3[0], q3[1]); p3.y = pack_hi16(q3[2], q3[3]);
+      p3.z = pack_hi16(q3[4], q3[5]); p3.w = pack_hi16(q3[6], q3[7]);
+      const lg_bf16x8_t a = __builtin_bit_cast(lg_bf16x8_t, av[i]);
+      c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(lg_bf16x8_t, p1), c1, 0, 0, 0);
+      c2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(lg_bf16x8_t, p2), c2, 0, 0, 0);
+      c3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(lg_bf16x8_t, p3), c3, 0, 0, 0);
     }
   }
   // 32x32 accumulator: lane holds expert column l32, token rows
-  // 8 * (v / 4) + 4 * g + (v % 4). Partial sums meet in wave order.
-  if (wave > 0) {
-#pragma unroll
-    for (int v = 0; v < 16; ++v) red[wave - 1][v][lane] = acc[v];
-  }
-  __syncthreads();
-  if (wave > 0 || e >= E) return;
-  const float bias = b ? b[e] : 0.0f;
+  // 8 * (v / 4) + 4 * g + (v % 4).
+  if (e >= E) return;
+  float *Ps = P + (int64_t)s * T * E;
 #pragma unroll
   for (int v = 0; v < 16; ++v) {
-    float sum = acc[v];
-#pragma unroll
-    for (int w = 0; w < NW - 1; ++w) sum += red[w][v][lane];
-    const int tt = blockIdx.x * 32 + 8 * (v >> 2) + 4 * g + (v & 3);
-    if (tt < T) L[(int64_t)tt * E + e] = sum + bias;
+    const int64_t tr = tt * 32 + 8 * (v >> 2) + 4 * g + (v & 3);
+    if (tr < T) Ps[tr * E + e] = (c1[v] + c2[v]) + c3[v];
   }
 }
 
-size_t router_split_bytes(int E, int H) { return (size_t)3 * E * H * sizeof(uint16_t); }
+// L[t][e] = (sum over s of P[s][t][e], in s order) + b[e]: the same bits as
+// the top-k kernels' own sum of the partials.
+__global__ __launch_bounds__(256) void k_logits_sum(const float *__restrict__ P, int S, int64_t n, int E,
+                                                    const float *__restrict__ b, float *__restrict__ L) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  float v = P[i];
+  for (int s = 1; s < S; ++s) v += P[(int64_t)s * n + i];
+  if (b) v += b[i % E];
+  L[i] = v;
+}
+
+size_t router_partials_bytes(int T, int E, int H) {
+  return (size_t)router_split(H) * (size_t)(T > 0 ? T : 1) * (size_t)E * sizeof(float);
+}
+
+hipError_t launch_router_partials(const uint16_t *x, int T, int H, const float *W, int E, float *P,
+                                  hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  const int S = router_split(H), chunk = router_chunk(H);
+  const int64_t units = cdiv(T, 32) * (int64_t)S * cdiv(E, 32);
+  hipLaunchKernelGGL(k_logits_ks, dim3((unsigned)cdiv(units, 4)), dim3(256), 0, s, x, T, H, W, E, chunk, S, P);
+  return hipGetLastError();
+}
 
 // ---------------------------------------------------------------------------
 // Router logits, many tokens: 32 tokens x 64 experts per workgroup, H in
@@ -235,38 +290,37 @@ __global__ __launch_bounds__(256) void k_logits_tiled(const uint16_t *__restrict
   }
 }
 
-hipError_t launch_router_logits(const uint16_t *x, int T, int H, const float *W, const float *b,
-                                int E, float *logits, void *split_ws, hipStream_t s, bool rows_only) {
+hipError_t launch_router_rows(const uint16_t *x, int T, int H, const float *W, const float *b, int E,
+                              float *logits, hipStream_t s) {
   if (T <= 0) return hipSuccess;
-  if (T == 1) {  // one token: no idle token slots (the same per-token order)
+  if (T == 1)  // one token: no idle token slots (the same per-token order)
     hipLaunchKernelGGL(k_logits_rows<1>, dim3(E), dim3(256), 0, s, x, T, H, W, b, E, logits);
-  } else if (rows_only || T <= kRowsLogitsMaxT) {
-    // the per-token order of k_logits_rows: for every T on the small-M path,
-    // and up to kRowsLogitsMaxT tokens everywhere (below that, one launch
-    // with x read from L2 beats splitting W_r for the matrix cores)
-    if (T <= 2)
-      hipLaunchKernelGGL(k_logits_rows<2>, dim3(E), dim3(256), 0, s, x, T, H, W, b, E, logits);
-    else if (T <= 4)
-      hipLaunchKernelGGL(k_logits_rows<4>, dim3(E), dim3(256), 0, s, x, T, H, W, b, E, logits);
-    else if (T <= 8)
-      hipLaunchKernelGGL(k_logits_rows<8>, dim3(E), dim3(256), 0, s, x, T, H, W, b, E, logits);
-    else
-      hipLaunchKernelGGL(k_logits_rows<32>, dim3(E, (unsigned)cdiv(T, 32)), dim3(256), 0, s, x, T, H, W,
-                         b, E, logits);
-  } else if (split_ws && H % 32 == 0) {
-    uint16_t *planes = reinterpret_cast<uint16_t *>(split_ws);
-    const int64_t n = (int64_t)E * H;
-    hipLaunchKernelGGL(k_split3, dim3((unsigned)cdiv(n, 256)), dim3(256), 0, s, W, n, planes);
-    hipLaunchKernelGGL(k_logits_mfma, dim3((unsigned)cdiv(T, 32), (unsigned)cdiv(E, 32)), dim3(512), 0, s,
-                       x, T, H, planes, b, E, logits);
-  } else if (T <= 8) {
+  else if (T <= 2)
+    hipLaunchKernelGGL(k_logits_rows<2>, dim3(E), dim3(256), 0, s, x, T, H, W, b, E, logits);
+  else if (T <= 4)
+    hipLaunchKernelGGL(k_logits_rows<4>, dim3(E), dim3(256), 0, s, x, T, H, W, b, E, logits);
+  else if (T <= 8)
     hipLaunchKernelGGL(k_logits_rows<8>, dim3(E), dim3(256), 0, s, x, T, H, W, b, E, logits);
-  } else if (T <= 32) {
-    hipLaunchKernelGGL(k_logits_rows<32>, dim3(E), dim3(256), 0, s, x, T, H, W, b, E, logits);
-  } else {
-    hipLaunchKernelGGL(k_logits_tiled, dim3((unsigned)cdiv(T, 32), (unsigned)cdiv(E, 64)),
-                       dim3(256), 0, s, x, T, H, W, b, E, logits);
+  else
+    hipLaunchKernelGGL(k_logits_rows<32>, dim3(E, (unsigned)cdiv(T, 32)), dim3(256), 0, s, x, T, H, W, b,
+                       E, logits);
+  return hipGetLastError();
+}
+
+hipError_t launch_router_logits(const uint16_t *x, int T, int H, const float *W, const float *b,
+                                int E, float *logits, float *partials, hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  if (partials) {
+    hipError_t e = launch_router_partials(x, T, H, W, E, partials, s);
+    if (e != hipSuccess) return e;
+    const int64_t n = (int64_t)T * E;
+    hipLaunchKernelGGL(k_logits_sum, dim3((unsigned)cdiv(n, 256)), dim3(256), 0, s, partials,
+                       router_split(H), n, E, b, logits);
+    return hipGetLastError();
   }
+  if (T <= kRowsLogitsMaxT) return launch_router_rows(x, T, H, W, b, E, logits, s);
+  hipLaunchKernelGGL(k_logits_tiled, dim3((unsigned)cdiv(T, 32), (unsigned)cdiv(E, 64)), dim3(256), 0, s,
+                     x, T, H, W, b, E, logits);
   return hipGetLastError();
 }
 
@@ -300,15 +354,33 @@ __device__ inline float lane_value(float v, int l) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
 }
 
-template <int EPL>
-__device__ inline void wave_topk(const float *Lrow, int E, int k, int renorm, int &my_id, float &wgt) {
+// Where a token's logits come from: P[t * E + e] summed with the partials
+// P[s * stride + t * E + e], s = 1 .. S-1, in s order, then + bias[e] (S = 1
+// and no bias: given logits).
+struct LogitSrc {
+  const float *P;
+  int64_t stride;
+  int S;
+  const float *bias;
+};
+
+__device__ inline float logit_at(const LogitSrc &L, int64_t i, int e) {
+  float v = L.P[i];
+  for (int s = 1; s < L.S; ++s) v += L.P[(int64_t)s * L.stride + i];
+  if (L.bias) v += L.bias[e];
+  return v;
+}
+
+// get(e): logit of expert e (e < E) of this wave's token.
+template <int EPL, class Get>
+__device__ inline void wave_topk(Get get, int E, int k, int renorm, int &my_id, float &wgt) {
   const int lane = threadIdx.x & 63;
   float v[EPL];
   uint32_t key[EPL];  // 0: no expert, or already picked (below every logit's key)
 #pragma unroll
   for (int j = 0; j < EPL; ++j) {
     const int e = lane + 64 * j;
-    v[j] = e < E ? Lrow[e] : -__builtin_inff();
+    v[j] = e < E ? get(e) : -__builtin_inff();
     // key 0 belongs to one NaN bit pattern only; it ties with key 1 (another
     // NaN) instead, so that 0 stays the marker
     key[j] = e < E ? max(float_order_key(v[j]), 1u) : 0u;
@@ -356,15 +428,15 @@ __device__ inline void wave_topk(const float *Lrow, int E, int k, int renorm, in
 }
 
 template <int EPL>
-__global__ __launch_bounds__(256) void k_topk(const float *__restrict__ L, int T, int E, int k,
-                                              int renorm, int32_t *__restrict__ ids,
-                                              float *__restrict__ wts) {
+__global__ __launch_bounds__(256) void k_topk(LogitSrc L, int T, int E, int k, int renorm,
+                                              int32_t *__restrict__ ids, float *__restrict__ wts) {
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
   const int lane = threadIdx.x & 63;
   int my_id;
   float wgt;
-  wave_topk<EPL>(L + (int64_t)t * E, E, k, renorm, my_id, wgt);
+  const int64_t row = (int64_t)t * E;
+  wave_topk<EPL>([&](int e) { return logit_at(L, row + e, e); }, E, k, renorm, my_id, wgt);
   if (lane < k) {
     ids[(int64_t)t * k + lane] = my_id;
     wts[(int64_t)t * k + lane] = wgt;
@@ -529,50 +601,58 @@ __global__ __launch_bounds__(256) void k_group_scatter(const int32_t *__restrict
 
 // ---------------------------------------------------------------------------
 // Routing in one workgroup of 1024 threads for up to 1024 routed slots and
-// E <= kSmallE experts: the tokens' logits copied to LDS when they fit
-// (T * E <= kSmallTE, else read from L2), top-k + softmax by wave_topk (one wave per
-// token, as k_topk), then one block scan for the expert offsets, the
-// non-empty expert list and the MFMA tiles, and stable ranks by ballots.
+// E <= kSmallE experts. TOPK: the tokens' logits are copied to LDS when they
+// fit (T * E <= kSmallTE, else read from L2) and ranked by wave_topk (one
+// wave per token, as k_topk), weights included; otherwise the ids come from
+// topk_ids, written by k_topk before. Then one block scan gives the expert
+// offsets, the non-empty expert list and the MFMA tiles, and ballots the
+// stable ranks.
 // ---------------------------------------------------------------------------
 constexpr int kSmallR = 1024;   // routed slots: one per thread
 constexpr int kSmallE = 256;
 constexpr int kSmallTE = 4096;  // bounds the LDS copy of the logits (else read from L2)
+// Up to this many tokens the one-workgroup kernel also ranks the experts;
+// above it the ranking runs in parallel (k_topk, one wave per token) first:
+// a single workgroup ranking 128 tokens took 27 us against ~5 us.
+constexpr int kTailTopkMaxT = 16;
 
-__global__ __launch_bounds__(1024) void k_route_tail_small(const float *__restrict__ L, int T, int E,
-                                                           int k, int renorm, int bm, int max_tiles,
-                                                           RouteBufs o) {
-  __shared__ __attribute__((aligned(16))) float Ls[kSmallTE];
+template <bool TOPK>
+__global__ __launch_bounds__(1024) void k_route_tail_small(LogitSrc L, int T, int E, int k, int renorm,
+                                                           int bm, int max_tiles, RouteBufs o) {
+  __shared__ __attribute__((aligned(16))) float Ls[TOPK ? kSmallTE : 4];
   __shared__ int sel_id[kSmallR];
-  __shared__ float sel_w[kSmallR];
+  __shared__ float sel_w[TOPK ? kSmallR : 4];
   __shared__ int cnt[kSmallE];
   __shared__ int offs[kSmallE];
   __shared__ int wcnt[16][kSmallE];  // per wave: slots routed to each expert
   __shared__ int s_total;
   const int tid = threadIdx.x;
   const int R = T * k;
-  const int Ep = (E + 3) & ~3;  // LDS row stride: 16-byte rows, padded with -inf
-  const bool in_lds = T * Ep <= kSmallTE;  // uniform
-  if (in_lds) {
-    for (int i = tid; i < T * Ep; i += 1024) {
-      const int t = i / Ep, f = i - t * Ep;
-      Ls[i] = f < E ? L[(int64_t)t * E + f] : -__builtin_inff();
-    }
-  }
   for (int e = tid; e < E; e += 1024) cnt[e] = 0;
-  __syncthreads();
-  // top k of each token: one wave per token (wave_topk), weights included
-  {
+  if constexpr (TOPK) {
+    const int Ep = (E + 3) & ~3;  // LDS row stride: 16-byte rows, padded with -inf
+    const bool in_lds = T * Ep <= kSmallTE;  // uniform
+    if (in_lds) {
+      for (int i = tid; i < T * Ep; i += 1024) {
+        const int t = i / Ep, f = i - t * Ep;
+        Ls[i] = f < E ? logit_at(L, (int64_t)t * E + f, f) : -__builtin_inff();
+      }
+    }
+    __syncthreads();
+    // top k of each token: one wave per token (wave_topk), weights included
     const int wave = tid >> 6, lane = tid & 63;
     for (int t = wave; t < T; t += 16) {
       int my_id;
       float wgt;
-      const float *row = in_lds ? Ls + t * Ep : L + (int64_t)t * E;
+      const float *lrow = Ls + t * Ep;
+      const int64_t grow = (int64_t)t * E;
+      auto get = [&](int e) { return in_lds ? lrow[e] : logit_at(L, grow + e, e); };
       if (E <= 64)
-        wave_topk<1>(row, E, k, renorm, my_id, wgt);
+        wave_topk<1>(get, E, k, renorm, my_id, wgt);
       else if (E <= 128)
-        wave_topk<2>(row, E, k, renorm, my_id, wgt);
+        wave_topk<2>(get, E, k, renorm, my_id, wgt);
       else
-        wave_topk<4>(row, E, k, renorm, my_id, wgt);
+        wave_topk<4>(get, E, k, renorm, my_id, wgt);
       if (lane < k) {
         sel_id[t * k + lane] = my_id;
         sel_w[t * k + lane] = wgt;
@@ -581,9 +661,16 @@ __global__ __launch_bounds__(1024) void k_route_tail_small(const float *__restri
   }
   __syncthreads();
   if (tid < R) {
-    o.topk_ids[tid] = sel_id[tid];
-    o.topk_w[tid] = sel_w[tid];
-    atomicAdd(&cnt[sel_id[tid]], 1);
+    int id;
+    if constexpr (TOPK) {
+      id = sel_id[tid];
+      o.topk_ids[tid] = id;
+      o.topk_w[tid] = sel_w[tid];
+    } else {
+      id = o.topk_ids[tid];  // from k_topk: always in [0, E)
+      sel_id[tid] = id;
+    }
+    atomicAdd(&cnt[id], 1);
   }
   // zero the per-wave expert counts of the stable ranking below
   for (int i = tid; i < 16 * E; i += 1024) wcnt[i / E][i % E] = 0;
@@ -634,36 +721,58 @@ __global__ __launch_bounds__(1024) void k_route_tail_small(const float *__restri
   }
 }
 
-hipError_t launch_route(const float *logits, int T, int E, int k, int renorm, const RouteBufs &rb,
-                        int bm, hipStream_t s) {
+static hipError_t launch_topk(const LogitSrc &L, int T, int E, int k, int renorm, const RouteBufs &rb,
+                              hipStream_t s) {
+  const dim3 tk((unsigned)cdiv(T, 4));
+  if (E <= 64)
+    hipLaunchKernelGGL(k_topk<1>, tk, dim3(256), 0, s, L, T, E, k, renorm, rb.topk_ids, rb.topk_w);
+  else if (E <= 128)
+    hipLaunchKernelGGL(k_topk<2>, tk, dim3(256), 0, s, L, T, E, k, renorm, rb.topk_ids, rb.topk_w);
+  else if (E <= 256)
+    hipLaunchKernelGGL(k_topk<4>, tk, dim3(256), 0, s, L, T, E, k, renorm, rb.topk_ids, rb.topk_w);
+  else if (E <= 512)
+    hipLaunchKernelGGL(k_topk<8>, tk, dim3(256), 0, s, L, T, E, k, renorm, rb.topk_ids, rb.topk_w);
+  else
+    hipLaunchKernelGGL(k_topk<16>, tk, dim3(256), 0, s, L, T, E, k, renorm, rb.topk_ids, rb.topk_w);
+  return hipGetLastError();
+}
+
+static hipError_t launch_route_src(const LogitSrc &L, int T, int E, int k, int renorm, const RouteBufs &rb,
+                                   int bm, hipStream_t s) {
   const int R = T * k;
-  if (E <= kSmallE && R <= kSmallR) {
-    const int max_tiles = (int)cdiv(R, bm) + (R < E ? R : E);
-    hipLaunchKernelGGL(k_route_tail_small, dim3(1), dim3(1024), 0, s, logits, T, E, k, renorm, bm,
+  const bool one_wg = E <= kSmallE && R <= kSmallR;
+  const int max_tiles = (int)cdiv(R, bm) + (R < E ? R : E);
+  if (one_wg && T <= kTailTopkMaxT) {
+    hipLaunchKernelGGL(k_route_tail_small<true>, dim3(1), dim3(1024), 0, s, L, T, E, k, renorm, bm,
                        max_tiles, rb);
     return hipGetLastError();
   }
-  const dim3 tk((unsigned)cdiv(T, 4));
-  if (E <= 64)
-    hipLaunchKernelGGL(k_topk<1>, tk, dim3(256), 0, s, logits, T, E, k, renorm, rb.topk_ids, rb.topk_w);
-  else if (E <= 128)
-    hipLaunchKernelGGL(k_topk<2>, tk, dim3(256), 0, s, logits, T, E, k, renorm, rb.topk_ids, rb.topk_w);
-  else if (E <= 256)
-    hipLaunchKernelGGL(k_topk<4>, tk, dim3(256), 0, s, logits, T, E, k, renorm, rb.topk_ids, rb.topk_w);
-  else if (E <= 512)
-    hipLaunchKernelGGL(k_topk<8>, tk, dim3(256), 0, s, logits, T, E, k, renorm, rb.topk_ids, rb.topk_w);
-  else
-    hipLaunchKernelGGL(k_topk<16>, tk, dim3(256), 0, s, logits, T, E, k, renorm, rb.topk_ids, rb.topk_w);
+  hipError_t e = launch_topk(L, T, E, k, renorm, rb, s);
+  if (e != hipSuccess) return e;
+  if (one_wg) {
+    hipLaunchKernelGGL(k_route_tail_small<false>, dim3(1), dim3(1024), 0, s, L, T, E, k, renorm, bm,
+                       max_tiles, rb);
+    return hipGetLastError();
+  }
   const int nchunks = (int)cdiv(R, kChunk);
   hipLaunchKernelGGL(k_group_hist, dim3(nchunks), dim3(256), 0, s, rb.topk_ids, R, E, nchunks,
                      rb.chunk_hist);
-  const int max_tiles = (int)cdiv(R, bm) + (R < E ? R : E);
   hipLaunchKernelGGL(k_group_scan, dim3(1), dim3(1024), 0, s, rb.chunk_hist, E, nchunks, R, bm,
                      max_tiles, rb.expert_offsets, rb.grp_expert, rb.grp_row0, rb.grp_rows, rb.counters,
                      rb.tiles);
   hipLaunchKernelGGL(k_group_scatter, dim3(nchunks), dim3(256), 0, s, rb.topk_ids, R, E, nchunks,
                      rb.chunk_hist, rb.sorted_slots, rb.slot_pos);
   return hipGetLastError();
+}
+
+hipError_t launch_route(const float *logits, int T, int E, int k, int renorm, const RouteBufs &rb,
+                        int bm, hipStream_t s) {
+  return launch_route_src(LogitSrc{logits, (int64_t)T * E, 1, nullptr}, T, E, k, renorm, rb, bm, s);
+}
+
+hipError_t launch_route_partials(const float *partials, int S, const float *bias, int T, int E, int k,
+                                 int renorm, const RouteBufs &rb, int bm, hipStream_t s) {
+  return launch_route_src(LogitSrc{partials, (int64_t)T * E, S, bias}, T, E, k, renorm, rb, bm, s);
 }
 
 // Caller-given groups (the grouped GEMM entry point): group g = rows

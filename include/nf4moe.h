@@ -158,21 +158,26 @@ nf4moe_status_t nf4moe_absmax_to_bf16(const float *absmax, int64_t n, uint16_t *
                                       void *stream);
 
 /* nf4moe_router_workspace_bytes -- workspace that lets nf4moe_router_logits use
- * the matrix cores (3 * E * H * 2 bytes: router_w split exactly into three bf16
- * planes); 0 for E < 1 or H <= 0. */
-size_t nf4moe_router_workspace_bytes(int32_t E, int32_t H);
+ * the matrix cores for T tokens (the partial sums over 8 chunks of H: 4 * S * T
+ * * E bytes, S = min(8, H / 16)); 0 for T < 1, E < 1, or H not a positive
+ * multiple of 16 (the vector path needs none). */
+size_t nf4moe_router_workspace_bytes(int32_t T, int32_t E, int32_t H);
 
 /* nf4moe_router_logits -- logits[t, e] = sum_h x[t, h] * router_w[e, h] (+ router_b[e]),
  * x bf16 [T, H], router_w fp32 [E, H], optional router_b fp32 [E], logits fp32
  * [T, E] (all device); fp32-accurate accumulation. The first step of the routed
  * layer (the router, outside the kernel on the pages' "Why it happens" dataflow,
- * inside this library). ws (device, caller-owned, 256-byte aligned) may be NULL;
- * with ws_bytes >= nf4moe_router_workspace_bytes(E, H), T > 256 and H % 32 == 0
- * the product runs on the matrix cores (x exact in bf16, each weight as the
- * exact sum of three bf16 parts, fp32 accumulation), else on the vector ALUs
- * (one workgroup per expert, a token's sum in the same order for every T).
+ * inside this library). ws (device, caller-owned, 256-byte aligned) may be NULL.
+ * With ws and H % 16 == 0 the product runs on the matrix cores: x exact in
+ * bf16, each weight as the exact sum of three bf16 parts (weights of normal
+ * range), fp32 partial sums over S chunks of H added in chunk order, then the
+ * bias; these are the bits nf4moe_moe_forward routes on when it takes the MFMA
+ * path. Without ws: the vector ALUs (one workgroup per expert, a token's sum in
+ * the same order for every T, up to 256 tokens; a tiled kernel above). Either
+ * way a token's logits carry the same bits whatever the other tokens.
  * Errors: INVALID_ARG for T < 0, E outside 1..1024, H <= 0 or H % 8, null or
- * misaligned pointers; WORKSPACE for a non-NULL ws smaller than required. */
+ * misaligned pointers; WORKSPACE for a non-NULL ws (H % 16 == 0) smaller than
+ * nf4moe_router_workspace_bytes(T, E, H). */
 nf4moe_status_t nf4moe_router_logits(const uint16_t *x, int32_t T, int32_t H,
                                      const float *router_w, const float *router_b, int32_t E,
                                      float *logits, void *ws, size_t ws_bytes, void *stream);
@@ -273,9 +278,10 @@ size_t nf4moe_workspace_bytes(const nf4moe_layer_t *layer, int32_t T_max);
  * affected tokens are then unspecified.
  * Row-count invariance (the pages' STATUS page, kernel section): on the small-M
  * path (AUTO picks it for T * top_k <= 64) a token's outputs and routing carry
- * the same bits whatever the other tokens of the call; on the MFMA path, among
- * calls of up to 256 tokens and among calls of more than 256 (the two router
- * kernels); across paths they differ in summation order.
+ * the same bits whatever the other tokens of the call, for every T; on the
+ * MFMA path, among calls of up to 16 tokens (routed on the vector router's
+ * logits) and among calls of more than 16 (the matrix-core router's); across
+ * these they differ in summation order.
  * Errors: INVALID_ARG (layer fields, sizes, pointers), WORKSPACE (ws_bytes <
  * nf4moe_workspace_bytes(layer, T)). T == 0 is a no-op. */
 nf4moe_status_t nf4moe_moe_forward(const nf4moe_layer_t *layer, const uint16_t *x, int32_t T,
@@ -293,7 +299,7 @@ nf4moe_status_t nf4moe_moe_forward(const nf4moe_layer_t *layer, const uint16_t *
  * workspace; nothing in the scratch has to start at zero.
  * Limit: layers and token counts with nf4moe_workspace_bytes(layer, T) <=
  * NF4MOE_NOALLOC_SCRATCH_BYTES (an OLMoE-1B-7B-shaped layer, E=64, top_k=8,
- * H=2048, I=1024, up to 331 tokens); larger calls return WORKSPACE and enqueue
+ * H=2048, I=1024, up to 333 tokens); larger calls return WORKSPACE and enqueue
  * nothing.
  * Every call on one GPU shares that GPU's scratch, which keeps the last call's
  * contents: calls on one stream are ordered, but calls that can overlap on one

@@ -10,8 +10,10 @@ per-token order (router logits one workgroup per expert, a fixed softmax
 denominator order, GEMV rows independent of the batch, the fused token-centric
 down + combine taking the same steps as the GEMV slot output + combine), so
 the property holds for every T; on the MFMA path it holds among calls that use
-the same router kernel (T <= 256: the per-token kernel; T > 256: the matrix
-cores). A property of the path at any size: the test
+the same router kernel (T <= 16: the per-token kernel; T > 16: the
+matrix-core one, which sums a token's logit over fixed chunks of H in chunk
+order), as an MFMA row's result does not depend on the rows sharing its tile.
+A property of the path at any size: the test
 compares the path with itself; the oracle bound is checked once per case.
 """
 import numpy as np
@@ -105,18 +107,26 @@ def test_olmoe_shape_row_count_invariance():
 
 @pytest.mark.parametrize("wl", CASES[:3], ids=lambda w: w.name)
 def test_mfma_row_count_invariance_per_router_window(wl):
-    """Forced MFMA path: calls of up to 256 tokens share the per-token router
-    kernel (and calls of more than 256 the matrix-core router), and a routed
-    row's MFMA result does not depend on the rows sharing its tile or on the
-    tile height (64- or 128-row bodies)."""
-    layer, _, _ = build_layers(wl, 0, DEV, path=M.PATH_MFMA)
+    """Forced MFMA path: calls of up to 16 tokens share the per-token router
+    (with top-k and grouping in one workgroup), calls of more than 16 the
+    matrix-core router (top-k in parallel; grouping in one workgroup up to
+    1024 routed slots, in three kernels above); and a routed row's MFMA result
+    does not depend on the rows sharing its tile or on the tile height (64- or
+    128-row tables and bodies)."""
+    layer, o_layer, _ = build_layers(wl, 0, DEV, path=M.PATH_MFMA)
     X = S.make_x(wl, 600)
-    upto = _run(layer, X[:256])
-    for T in (1, 33, 40, 177):
-        _same(_run(layer, X[:T]), tuple(f[:T] for f in upto), f"{wl.name} MFMA: first {T} of 256")
     full = _run(layer, X)
-    for T in (257, 300, 411):
+    rows = [0, 599]
+    ref = O.moe_forward(o_layer, X[rows], topk_ids_override=full[1][rows])
+    check_bound(O.bf16_bits_to_f64(full[0][rows].view(np.uint16)), ref, f"{wl.name} MFMA")
+    for T in (17, 33, 177, 256, 257, 411):
         _same(_run(layer, X[:T]), tuple(f[:T] for f in full), f"{wl.name} MFMA: first {T} of 600")
+    perm = np.array([599, 3, 300, 0, 1] + list(range(100, 120)))  # 25 tokens, another order
+    _same(_run(layer, np.ascontiguousarray(X[perm])), tuple(f[perm] for f in full), f"{wl.name} MFMA: permuted")
+    upto = _run(layer, X[:16])
+    for T in (1, 2, 9, 15):
+        _same(_run(layer, X[:T]), tuple(f[:T] for f in upto), f"{wl.name} MFMA: first {T} of 16")
+    _same(_run(layer, X[7:8]), tuple(f[7:8] for f in upto), f"{wl.name} MFMA: token 7 alone")
 
 
 def test_small_m_grouped_gemm_rows_independent():
