@@ -125,8 +125,8 @@ struct GemmArgs {
 // more workgroups on the chip when a batch has few rows per expert (measured:
 // Qwen3-shaped T = 128 / 512 172 / 306 us against 205 / 323 us with 128-row
 // tables); with many rows per expert, 128-row tiles decode each weight tile
-// half as often. Within a 128-row table, a last tile of at most 64 rows runs
-// the 64-row body.
+// half as often. Each tile runs the 128-, 64- or 32-row body by its own row
+// count.
 inline int mfma_tile_rows(int64_t R, int64_t G) {
   const int64_t groups = R < G ? R : G;
   return (groups > 0 && R <= 48 * groups) ? 64 : 128;

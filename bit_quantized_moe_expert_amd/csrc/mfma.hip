@@ -70,24 +70,20 @@ __device__ inline void build_mfma_table(uint4 *tab) {
   }
 }
 
-// LDS bytes of one workgroup: the decode table and the A buffers of the
-// 128-row body (hi[2], and lo[2] for an fp32 A).
-template <int AM>
-constexpr int mfma_lds_bytes() { return kTabBytes + (AM != 0 ? 4 : 2) * 128 * kApad * 2; }
-
 // One output tile: rows [trow0, trow0 + trows) of expert e against weight-row
 // tile nt. AM: activation operand mode. 0: bf16 A; 2: an fp32 A given as
 // 32-bit (hi, lo) bf16 pairs, its truncated bf16 hi and the RNE bf16 of the
 // rest (the SwiGLU epilogue writes h so), each weight product taking three
 // MFMAs. XF: the extended gate_up / down epilogue (clamped GLU, interleaved
 // gate and up rows, per-expert biases); XF = 0 instantiates the plain kernel.
-// MB: 32-row blocks (4: up to 128 rows; 2: up to 64 rows, half the MFMAs and
-// A traffic for the tiles of small groups and the last tiles of large ones).
+// MB: 32-row blocks (4: up to 128 rows; 2: up to 64 rows; 1: up to 32 rows:
+// fewer MFMAs and less A traffic for the tiles of small groups and the last
+// tiles of large ones).
 template <int FMT, int EPI, int AM, int XF, int MB>
 __device__ __forceinline__ void mfma_tile(const GemmArgs &p, uint8_t *smem, int nt, int e, int trow0,
                                           int trows) {
   static_assert(AM == 0 || AM == 2, "operand mode");
-  static_assert(MB == 4 || MB == 2, "row blocks");
+  static_assert(MB == 4 || MB == 2 || MB == 1, "row blocks");
   constexpr bool AF32 = AM != 0;                      // a lo part exists
   constexpr int kBM = 32 * MB;                        // rows per tile
   constexpr int ABUF = kBM * kApad * 2;               // bytes per A buffer
@@ -128,8 +124,11 @@ __device__ __forceinline__ void mfma_tile(const GemmArgs &p, uint8_t *smem, int 
   // starting at k0 + EPT * aq. Rows past the tile read a valid row (the tile's
   // first) and are zeroed when stored (measured: storing them unmasked, which
   // the results would allow, made the 64-row kernels 2-3 % slower).
-  constexpr int TPR = 512 / kBM;                      // fill threads per row
-  constexpr int EPT = 64 / TPR;                       // elements per thread: 16 or 8
+  // A 32-row bf16 tile is 256 16-byte words: there the first 256 threads fill
+  // it (NFILL) and the other waves skip the store.
+  constexpr int TPR = (MB == 1 && !AF32) ? 8 : 512 / kBM;  // fill threads per row
+  constexpr int EPT = 64 / TPR;                       // elements per thread: 16, 8 or 4
+  constexpr int NFILL = kBM * TPR;                    // threads that fill the tile
   const int am = tid / TPR, aq = tid % TPR;
   const bool arow_ok = am < trows;
   int64_t arow;
@@ -154,10 +153,20 @@ __device__ __forceinline__ void mfma_tile(const GemmArgs &p, uint8_t *smem, int 
     for (int i = 0; i < AW; ++i) aregs[set][i] = src[i];
   };
   auto store_a = [&](int buf, int set) {
+    if (NFILL < 512 && tid >= NFILL) return;  // whole waves
     const uint4 *areg = aregs[set];
     const bool a_ok = aoks[set];
     uint16_t *dh = abuf(0, buf) + am * kApad + EPT * aq;
-    if (AM == 2) {  // de-interleave the pairs into the hi and lo tiles
+    if (AM == 2 && EPT == 4) {  // four pairs: 8 bytes into each tile
+      uint16_t *dl = abuf(1, buf) + am * kApad + EPT * aq;
+      const uint4 u = areg[0];
+      const uint32_t h0 = a_ok ? __builtin_amdgcn_perm(u.y, u.x, 0x05040100u) : 0u;
+      const uint32_t h1 = a_ok ? __builtin_amdgcn_perm(u.w, u.z, 0x05040100u) : 0u;
+      const uint32_t l0 = a_ok ? __builtin_amdgcn_perm(u.y, u.x, 0x07060302u) : 0u;
+      const uint32_t l1 = a_ok ? __builtin_amdgcn_perm(u.w, u.z, 0x07060302u) : 0u;
+      *reinterpret_cast<uint2 *>(dh) = make_uint2(h0, h1);
+      *reinterpret_cast<uint2 *>(dl) = make_uint2(l0, l1);
+    } else if (AM == 2) {  // de-interleave the pairs into the hi and lo tiles
       uint16_t *dl = abuf(1, buf) + am * kApad + EPT * aq;
 #pragma unroll
       for (int i = 0; i < EPT / 8; ++i) {
@@ -390,16 +399,21 @@ __device__ __forceinline__ void mfma_tile(const GemmArgs &p, uint8_t *smem, int 
 }
 
 // One workgroup per (weight-row tile, row tile) of the device tile table.
-// TR = 128: tiles of up to 128 rows of one expert; a tile of at most 64 rows
-// runs the 64-row body, a larger one the 128-row body (the choice is uniform
-// over the workgroup, and a row's arithmetic is the same in both). TR = 64:
-// tiles of up to 64 rows, all on the 64-row body, in a kernel holding only
-// that body (measured 4-5 % faster than the two-body kernel on such tables).
+// TR = 128: tiles of up to 128 rows of one expert; a tile runs the 128-, 64-
+// or 32-row body by its row count (the choice is uniform over the workgroup,
+// and a row's arithmetic is the same in all; the 32-row body took 6-16 % off
+// batches of 16-512 tokens whose groups are mostly small). TR = 64: tiles of
+// up to 64 rows, in a kernel without the 128-row body (measured 4-5 % faster
+// than the kernel holding it on such tables). A kernel holding only the
+// 32-row body fits two workgroups per CU, but was slower or equal: the
+// LDS-bound decode gains nothing from the second workgroup, and the pairs
+// leave CUs idle when the workgroups number about one per CU.
 template <int FMT, int EPI, int AM, int XF, int TR>
 __global__ __launch_bounds__(512) void k_mfma(GemmArgs p, int ntn, int per) {
   static_assert(TR == 64 || TR == 128, "tile rows");
-  __shared__ __attribute__((aligned(16))) uint8_t smem[TR == 64 ? kTabBytes + (AM != 0 ? 4 : 2) * 64 * kApad * 2
-                                                                 : mfma_lds_bytes<AM>()];
+  // the decode table and the A buffers of the tallest body (hi[2], and lo[2]
+  // for an fp32 A)
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kTabBytes + (AM != 0 ? 4 : 2) * TR * kApad * 2];
   // XCD-aware order: hardware XCD = blockIdx.x % 8; give each XCD a contiguous
   // run of (n-tile major, tile minor) work, so the M-tiles of one expert and
   // one weight tile share that XCD's L2.
@@ -416,7 +430,11 @@ __global__ __launch_bounds__(512) void k_mfma(GemmArgs p, int ntn, int per) {
       return;
     }
   }
-  mfma_tile<FMT, EPI, AM, XF, 2>(p, smem, nt, tile.x, tile.y, rows);
+  if (rows > 32) {
+    mfma_tile<FMT, EPI, AM, XF, 2>(p, smem, nt, tile.x, tile.y, rows);
+    return;
+  }
+  mfma_tile<FMT, EPI, AM, XF, 1>(p, smem, nt, tile.x, tile.y, rows);
 }
 
 template <int FMT, int EPI, int AM, int XF = 0>

@@ -341,13 +341,16 @@ def test_forward_rejects_bad_glu():
 @pytest.mark.parametrize("fmt", [O.FMT_NF4, O.FMT_MXFP4])
 @pytest.mark.parametrize("T", [800, 1000])
 def test_forward_mfma_tile_heights(fmt, T):
-    """Both MFMA tile bodies: 3 or 4 experts (about 170-330 rows each) take a
-    128-row table, with full tiles on the 128-row body and last tiles on
-    either body; 64 experts take a 64-row table, every tile on the 64-row
-    body."""
-    for E in (3, 4, 64):
+    """Every MFMA tile body: 3 or 4 experts (about 170-330 rows each) take a
+    128-row table, with full tiles on the 128-row body and last tiles on any
+    body; 64 experts (about 12-16 rows each) take a 64-row table, tiles on the
+    32-row body; 20 experts (40-50 rows each) on the 64-row body; and a call of
+    32 tokens over 4 experts tiles of 11-21 rows."""
+    for E in (3, 4, 20, 64):
         wl = S.custom(E=E, top_k=1, H=256, I=128, fmt=fmt, wid=70 + E)
         _forward_case(wl, T, M.PATH_MFMA, sample=[0, T // 2, T - 1])
+    wl = S.custom(E=4, top_k=2, H=256, I=128, fmt=fmt, wid=75)
+    _forward_case(wl, 32, M.PATH_MFMA)
 
 
 def test_forward_deterministic():
