@@ -220,7 +220,8 @@ class Run:
         self.optr = ctypes.c_void_p(self.out.data_ptr())
         self.srefs = [ctypes.byref(s) for s in self.structs]
         R = T * wl.top_k
-        self.small = (path == M.PATH_SMALL_M) or (path == M.PATH_AUTO and R <= 64 and max(wl.H, wl.I) <= 4096)
+        self.small = (path == M.PATH_SMALL_M) or (path == M.PATH_AUTO and
+                                                   M.auto_path(wl.fmt, R, max(wl.H, wl.I)) == M.PATH_SMALL_M)
 
     def step(self, i, stream_ptr=None):
         n = self.nlayers

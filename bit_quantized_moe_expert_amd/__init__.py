@@ -82,6 +82,7 @@ def lib() -> ctypes.CDLL:
         "nf4moe_moe_forward_profiled": [ctypes.POINTER(Layer), vp, i32, vp, vp, sz, vp,
                                         ctypes.POINTER(ctypes.c_void_p)],
         "nf4moe_codebook": [ctypes.c_int, ctypes.POINTER(ctypes.c_float)],
+        "nf4moe_auto_path": [ctypes.c_int, i64, i64],
         "nf4moe_stream_read_sink_words": [i64, i32],
         "nf4moe_stream_read": [vp, i64, i32, vp, vp],
         "nf4moe_status_string": [ctypes.c_int],
@@ -230,6 +231,11 @@ def absmax_to_bf16(absmax):
     bad = torch.zeros(1, dtype=torch.int32, device=absmax.device)
     _check(lib().nf4moe_absmax_to_bf16(_ptr(absmax), absmax.numel(), _ptr(out), _ptr(bad), _stream()))
     return out, int(bad.item())
+
+
+def auto_path(fmt: int, R: int, K_max: int) -> int:
+    """The kernel family AUTO runs for R routed rows (PATH_SMALL_M or PATH_MFMA)."""
+    return int(lib().nf4moe_auto_path(fmt, R, K_max))
 
 
 def router_logits(x, router_w, router_b=None, matrix_cores: bool = True):

@@ -44,7 +44,16 @@ int fmt_block(nf4moe_format_t f) { return fmt_nf4(f) ? 64 : 32; }
 bool fmt_ok(nf4moe_format_t f) { return fmt_nf4(f) || f == NF4MOE_FMT_MXFP4_B32; }
 int scale_align(nf4moe_format_t f) { return f == NF4MOE_FMT_NF4_B64 ? 4 : f == NF4MOE_FMT_NF4_B64_BF16ABS ? 2 : 1; }
 
-constexpr int kSmallR = 64;        // routed rows up to which AUTO picks the small-M kernels
+// Routed rows up to which AUTO picks the small-M kernels: 64 for NF4, 48 for
+// MXFP4, whose MFMA path makes one product per weight instead of two and
+// overtakes sooner (same box: gpt-oss-shaped T = 12 / 16 small-M 340 / 420 us,
+// MFMA 351 / 380 us). The crossover follows the rows per active expert, which
+// the host cannot see: Qwen3-shaped Zipf batches want the MFMA path from
+// 12 tokens (96 rows), OLMoE-shaped uniform ones the small-M path up to 16
+// (128 rows); 64 serves the skewed case.
+constexpr int kSmallR = 64;
+constexpr int kSmallRMxfp4 = 48;
+static int auto_small_rows(int fmt) { return fmt == NF4MOE_FMT_MXFP4_B32 ? kSmallRMxfp4 : kSmallR; }
 // Tokens up to which the small-M path's down projection is token-centric (fused
 // with the combine: no slot buffer, no combine launch). Each token re-reads the
 // weights of its experts, which pays at these sizes: same box, against the
@@ -201,6 +210,10 @@ GemmArgs base_args(nf4moe_format_t fmt) {
 extern "C" {
 
 const char *nf4moe_version(void) { return "nf4moe 0.1.0 (gfx950)"; }
+
+int32_t nf4moe_auto_path(nf4moe_format_t fmt, int64_t R, int64_t K_max) {
+  return (R <= auto_small_rows((int)fmt) && K_max <= kSmallMaxK) ? NF4MOE_PATH_SMALL_M : NF4MOE_PATH_MFMA;
+}
 
 const char *nf4moe_status_string(nf4moe_status_t st) {
   switch (st) {
@@ -369,7 +382,7 @@ nf4moe_status_t nf4moe_grouped_gemm(nf4moe_format_t fmt, const uint16_t *a, cons
     return fail(NF4MOE_ERR_WORKSPACE, "workspace %zu bytes < %zu required", ws_bytes, need);
   if (!aligned(ws, 256)) return fail(NF4MOE_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
   int use = path;
-  if (use == NF4MOE_PATH_AUTO) use = (R <= kSmallR && K <= kSmallMaxK) ? NF4MOE_PATH_SMALL_M : NF4MOE_PATH_MFMA;
+  if (use == NF4MOE_PATH_AUTO) use = nf4moe_auto_path(fmt, R, K);
   if (use == NF4MOE_PATH_SMALL_M && K > kSmallMaxK)
     return fail(NF4MOE_ERR_UNSUPPORTED, "small-M path needs K <= %lld", (long long)kSmallMaxK);
   if (R == 0) return NF4MOE_OK;
@@ -485,7 +498,7 @@ static nf4moe_status_t forward_impl(const nf4moe_layer_t *layer, const uint16_t 
   const RoutePlan rp = route_plan(T, L.E, L.top_k);
   int use = L.path;
   const int64_t maxK = L.H > L.I ? L.H : L.I;
-  if (use == NF4MOE_PATH_AUTO) use = (rp.R <= kSmallR && maxK <= kSmallMaxK) ? NF4MOE_PATH_SMALL_M : NF4MOE_PATH_MFMA;
+  if (use == NF4MOE_PATH_AUTO) use = nf4moe_auto_path(L.fmt, rp.R, maxK);
   if (use == NF4MOE_PATH_SMALL_M && maxK > kSmallMaxK)
     return fail(NF4MOE_ERR_UNSUPPORTED, "small-M path needs H, I <= %lld", (long long)kSmallMaxK);
 

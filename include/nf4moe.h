@@ -71,13 +71,18 @@ typedef enum {
 typedef enum { NF4MOE_DT_F32 = 0, NF4MOE_DT_BF16 = 1 } nf4moe_dtype_t;
 
 /* Which grouped-GEMM kernel family runs. AUTO picks from the routed row count
- * known on the host (R = T * top_k): R <= 64 (with H, I <= 4096) runs the
- * bandwidth-bound decode kernels, larger R the MFMA kernels (tiles of up to
- * 64 rows of one expert when the groups average at most 48 rows, else up to
- * 128, where a last tile of at most 64 rows runs a 64-row body). The other
- * values force one family (for A/B measurement and tests); the result must
- * satisfy the same tolerance. */
+ * known on the host (R = T * top_k): R <= 64 for NF4 and R <= 48 for MXFP4
+ * (with H, I <= 4096) runs the bandwidth-bound decode kernels, larger R the
+ * MFMA kernels (tiles of up to 64 rows of one expert when the groups average
+ * at most 48 rows, else up to 128; each tile runs a 128-, 64- or 32-row body
+ * by its row count). The other values force one family (for A/B measurement
+ * and tests); the result must satisfy the same tolerance. */
 typedef enum { NF4MOE_PATH_AUTO = 0, NF4MOE_PATH_SMALL_M = 1, NF4MOE_PATH_MFMA = 2 } nf4moe_path_t;
+
+/* nf4moe_auto_path -- the family AUTO runs for a grouped GEMM of R routed rows
+ * whose K (for a forward: max(H, I)) is K_max, in format fmt: NF4MOE_PATH_SMALL_M
+ * or NF4MOE_PATH_MFMA. Host only; no errors. */
+int32_t nf4moe_auto_path(nf4moe_format_t fmt, int64_t R, int64_t K_max);
 
 /* The gate_up epilogue. SWIGLU: h = silu(g) * u, silu(g) = g / (1 + exp(-g)).
  * CLAMPED: the gpt-oss expert form the experts4bit-qlora page names without
@@ -277,7 +282,7 @@ size_t nf4moe_workspace_bytes(const nf4moe_layer_t *layer, int32_t T_max);
  * whichever kernel routes), so no index leaves its buffer; the outputs of the
  * affected tokens are then unspecified.
  * Row-count invariance (the pages' STATUS page, kernel section): on the small-M
- * path (AUTO picks it for T * top_k <= 64) a token's outputs and routing carry
+ * path (AUTO picks it for T * top_k <= 64, 48 for MXFP4) a token's outputs and routing carry
  * the same bits whatever the other tokens of the call, for every T; on the
  * MFMA path, among calls of up to 16 tokens (routed on the vector router's
  * logits) and among calls of more than 16 (the matrix-core router's); across

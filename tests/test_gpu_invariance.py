@@ -84,8 +84,11 @@ def test_small_m_row_count_invariance(wl):
 
 @pytest.mark.parametrize("wl", CASES, ids=lambda w: w.name)
 def test_auto_decode_sizes_row_count_invariance(wl):
-    """AUTO picks the small-M path while T * top_k <= 64: every such T agrees."""
-    tmax = 64 // wl.top_k
+    """AUTO picks the small-M path while T * top_k <= 64 (48 for MXFP4): every
+    such T agrees."""
+    tmax = 1
+    while M.auto_path(wl.fmt, (tmax + 1) * wl.top_k, max(wl.H, wl.I)) == M.PATH_SMALL_M:
+        tmax += 1                                  # the largest call AUTO keeps on the small-M path
     _check_invariance(wl, M.PATH_AUTO, list(range(1, tmax)), [1, tmax - 1], tmax)
 
 
