@@ -114,10 +114,12 @@ __device__ inline uint32_t pack_hi16(uint32_t a, uint32_t b) {
   return __builtin_amdgcn_perm(b, a, 0x07060302u);
 }
 
+template <int MB, int B>
 __global__ __launch_bounds__(256) void k_logits_ks(const uint16_t *__restrict__ x, int T, int H,
                                                    const float *__restrict__ W, int E, int chunk,
                                                    int S, float *__restrict__ P) {
-  constexpr int B = 8;  // k-steps of 16 whose loads are issued together
+  // MB: 32-token blocks per wave (each weight split once for all of them);
+  // B: k-steps of 16 whose loads are issued together.
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int ET = (E + 31) >> 5;
   const int64_t u = (int64_t)blockIdx.x * 4 + wave;
@@ -125,48 +127,47 @@ __global__ __launch_bounds__(256) void k_logits_ks(const uint16_t *__restrict__ 
   const int64_t r = u / ET;
   const int s = (int)(r % S);
   const int64_t tt = r / S;
-  if (tt * 32 >= T) return;  // uniform over the wave
+  if (tt * 32 * MB >= T) return;  // uniform over the wave
   const int g = lane >> 5, l32 = lane & 31;
-  const int64_t t = tt * 32 + l32;
   const int e = et * 32 + l32;
-  const int64_t xrow = t < T ? t : T - 1;   // rows past the end compute on a valid row, never stored
   const int64_t wrow = e < E ? e : E - 1;
   const int kb = s * chunk, ke = kb + chunk < H ? kb + chunk : H;
-  const uint16_t *xa = x + xrow * H + 8 * g;
+  const uint16_t *xa[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    const int64_t t = (tt * MB + mb) * 32 + l32;
+    xa[mb] = x + (t < T ? t : T - 1) * H + 8 * g;  // rows past the end compute on a valid row, never stored
+  }
   const float *wa = W + wrow * H + 8 * g;
-  lg_f32x16_t c1 = {}, c2 = {}, c3 = {};
+  lg_f32x16_t acc[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) acc[mb] = lg_f32x16_t{};
   for (int k0 = kb; k0 < ke; k0 += 16 * B) {
-    uint4 av[B];
+    uint4 av[B][MB];
     float4 w0[B], w1[B];
 #pragma unroll
     for (int i = 0; i < B; ++i) {  // clamped to the chunk's last step: always in bounds
       const int k = k0 + 16 * i < ke ? k0 + 16 * i : ke - 16;
-      av[i] = *reinterpret_cast<const uint4 *>(xa + k);
       w0[i] = *reinterpret_cast<const float4 *>(wa + k);
       w1[i] = *reinterpret_cast<const float4 *>(wa + k + 4);
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) av[i][mb] = *reinterpret_cast<const uint4 *>(xa[mb] + k);
     }
     // Every step of the batch is computed; a step past the chunk (the last
-    // batch of a chunk that is not a multiple of 16 * B) has its activation
-    // operand zeroed. The mask is opaque to the compiler: with a branch per
+    // batch of a chunk that is not a multiple of 16 * B) has its weight
+    // operands zeroed. The mask is opaque to the compiler: with a branch per
     // step instead, it sinks each step's loads into the branch, and the
     // steps become one memory round trip each.
 #pragma unroll
     for (int i = 0; i < B; ++i) {
       uint32_t keep = k0 + 16 * i < ke ? 0xffffffffu : 0u;
       asm volatile("" : "+v"(keep));
-      av[i].x &= keep;
-      av[i].y &= keep;
-      av[i].z &= keep;
-      av[i].w &= keep;
-    }
-#pragma unroll
-    for (int i = 0; i < B; ++i) {
       const float wf[8] = {w0[i].x, w0[i].y, w0[i].z, w0[i].w, w1[i].x, w1[i].y, w1[i].z, w1[i].w};
       uint32_t q1[8], q2[8], q3[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const uint32_t b0 = __float_as_uint(wf[j]);
-        const float r1 = wf[j] - __uint_as_float(b0 & 0xffff0000u);
+        const uint32_t b0 = __float_as_uint(wf[j]) & keep;
+        const float r1 = __uint_as_float(b0) - __uint_as_float(b0 & 0xffff0000u);
         const uint32_t b1 = __float_as_uint(r1);
         const float r2 = r1 - __uint_as_float(b1 & 0xffff0000u);
         q1[j] = b0;
@@ -180,20 +181,32 @@ __global__ __launch_bounds__(256) void k_logits_ks(const uint16_t *__restrict__ 
       p2.z = pack_hi16(q2[4], q2[5]); p2.w = pack_hi16(q2[6], q2[7]);
       p3.x = pack_hi16(q3[0], q3[1]); p3.y = pack_hi16(q3[2], q3[3]);
       p3.z = pack_hi16(q3[4], q3[5]); p3.w = pack_hi16(q3[6], q3[7]);
-      const lg_bf16x8_t a = __builtin_bit_cast(lg_bf16x8_t, av[i]);
-      c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(lg_bf16x8_t, p1), c1, 0, 0, 0);
-      c2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(lg_bf16x8_t, p2), c2, 0, 0, 0);
-      c3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(lg_bf16x8_t, p3), c3, 0, 0, 0);
+      const lg_bf16x8_t b1v = __builtin_bit_cast(lg_bf16x8_t, p1);
+      const lg_bf16x8_t b2v = __builtin_bit_cast(lg_bf16x8_t, p2);
+      const lg_bf16x8_t b3v = __builtin_bit_cast(lg_bf16x8_t, p3);
+      // a row's sum: per k-step w1, w2, w3 in that order into one accumulator
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+        acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(lg_bf16x8_t, av[i][mb]), b1v, acc[mb], 0, 0, 0);
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+        acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(lg_bf16x8_t, av[i][mb]), b2v, acc[mb], 0, 0, 0);
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+        acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(lg_bf16x8_t, av[i][mb]), b3v, acc[mb], 0, 0, 0);
     }
   }
   // 32x32 accumulator: lane holds expert column l32, token rows
-  // 8 * (v / 4) + 4 * g + (v % 4).
+  // 8 * (v / 4) + 4 * g + (v % 4) of each 32-token block.
   if (e >= E) return;
   float *Ps = P + (int64_t)s * T * E;
 #pragma unroll
-  for (int v = 0; v < 16; ++v) {
-    const int64_t tr = tt * 32 + 8 * (v >> 2) + 4 * g + (v & 3);
-    if (tr < T) Ps[tr * E + e] = (c1[v] + c2[v]) + c3[v];
+  for (int mb = 0; mb < MB; ++mb) {
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int64_t tr = (tt * MB + mb) * 32 + 8 * (v >> 2) + 4 * g + (v & 3);
+      if (tr < T) Ps[tr * E + e] = acc[mb][v];
+    }
   }
 }
 
@@ -217,8 +230,20 @@ hipError_t launch_router_partials(const uint16_t *x, int T, int H, const float *
                                   hipStream_t s) {
   if (T <= 0) return hipSuccess;
   const int S = router_split(H), chunk = router_chunk(H);
-  const int64_t units = cdiv(T, 32) * (int64_t)S * cdiv(E, 32);
-  hipLaunchKernelGGL(k_logits_ks, dim3((unsigned)cdiv(units, 4)), dim3(256), 0, s, x, T, H, W, E, chunk, S, P);
+  // 128 tokens per wave from 1024 tokens on (each weight split and read once
+  // per 128 tokens; gpt-oss-shaped T = 2048: 27.5 against 38 us), 32 below
+  // (more waves for the latency-bound smaller calls; Qwen3-shaped T = 256 /
+  // 512: 9 us less routing than with 128). A row's arithmetic is the same
+  // either way.
+  if (T >= 1024) {
+    const int64_t units = cdiv(T, 128) * (int64_t)S * cdiv(E, 32);
+    hipLaunchKernelGGL((k_logits_ks<4, 4>), dim3((unsigned)cdiv(units, 4)), dim3(256), 0, s, x, T, H, W, E,
+                       chunk, S, P);
+  } else {
+    const int64_t units = cdiv(T, 32) * (int64_t)S * cdiv(E, 32);
+    hipLaunchKernelGGL((k_logits_ks<1, 8>), dim3((unsigned)cdiv(units, 4)), dim3(256), 0, s, x, T, H, W, E,
+                       chunk, S, P);
+  }
   return hipGetLastError();
 }
 
@@ -516,6 +541,11 @@ __device__ void build_tiles(const int32_t *grp_expert, const int32_t *grp_row0,
 
 // Grouping, stage 2 (single workgroup): flat exclusive scan of the histogram,
 // expert offsets, the compacted list of non-empty experts, and the MFMA tiles.
+// A histogram of up to kScanLdsN entries is scanned in LDS (one round of
+// coalesced loads; the group list also stays in LDS for the tiles), a larger
+// one in place in global memory.
+constexpr int kScanLdsN = 16384;
+
 __global__ __launch_bounds__(1024) void k_group_scan(int32_t *__restrict__ hist, int E, int nchunks,
                                                      int R, int bm, int max_tiles,
                                                      int32_t *__restrict__ off,
@@ -524,44 +554,61 @@ __global__ __launch_bounds__(1024) void k_group_scan(int32_t *__restrict__ hist,
                                                      int32_t *__restrict__ grp_rows,
                                                      int32_t *__restrict__ counters,
                                                      int4 *__restrict__ tiles) {
+  __shared__ int sh[kScanLdsN];
+  __shared__ int g_e[kMaxE], g_r0[kMaxE], g_n[kMaxE];
   __shared__ int s_total;
+  const int tid = threadIdx.x;
   const int64_t n = (int64_t)E * nchunks;
+  const bool in_lds = n <= kScanLdsN;  // uniform
+  int *h = in_lds ? sh : hist;
+  if (in_lds) {
+    for (int i = tid; i < n; i += 1024) sh[i] = hist[i];
+    __syncthreads();
+  }
+  // each thread scans a contiguous slice; the slice totals are block-scanned
   const int64_t per = (n + 1023) / 1024;
-  const int64_t i0 = per * threadIdx.x, i1 = min(n, i0 + per);
+  const int64_t i0 = per * tid, i1 = min(n, i0 + per);
   int sum = 0;
-  for (int64_t i = i0; i < i1; ++i) sum += hist[i];
+  for (int64_t i = i0; i < i1; ++i) sum += h[i];
   int run = block_scan_1024(sum, &s_total);
   for (int64_t i = i0; i < i1; ++i) {
-    const int v = hist[i];
-    hist[i] = run;
+    const int v = h[i];
+    h[i] = run;
     run += v;
   }
   __syncthreads();
+  if (in_lds) {
+    for (int i = tid; i < n; i += 1024) hist[i] = sh[i];
+  }
   // expert offsets and the compacted non-empty experts (ascending id)
   int cnt_total = 0;
   for (int e0 = 0; e0 < E; e0 += 1024) {
-    const int e = e0 + threadIdx.x;
+    const int e = e0 + tid;
     int o = 0, c = 0;
     if (e < E) {
-      o = hist[(int64_t)e * nchunks];
-      c = (e + 1 < E ? hist[(int64_t)(e + 1) * nchunks] : R) - o;
+      o = h[(int64_t)e * nchunks];
+      c = (e + 1 < E ? h[(int64_t)(e + 1) * nchunks] : R) - o;
       off[e] = o;
     }
     const int slot = block_scan_1024(c > 0 ? 1 : 0, &s_total);
     if (c > 0 && cnt_total + slot < E) {
-      grp_expert[cnt_total + slot] = e;
-      grp_row0[cnt_total + slot] = o;
-      grp_rows[cnt_total + slot] = c;
+      const int gi = cnt_total + slot;
+      grp_expert[gi] = e;
+      grp_row0[gi] = o;
+      grp_rows[gi] = c;
+      g_e[gi] = e;
+      g_r0[gi] = o;
+      g_n[gi] = c;
     }
     cnt_total += s_total;
     __syncthreads();
   }
-  if (threadIdx.x == 0) {
+  if (tid == 0) {
     off[E] = R;
     counters[0] = cnt_total;
   }
   __syncthreads();
-  build_tiles(grp_expert, grp_row0, grp_rows, cnt_total, bm, max_tiles, tiles, counters + 1);
+  build_tiles(g_e, g_r0, g_n, cnt_total, bm, max_tiles, tiles, counters + 1);
 }
 
 // Grouping, stage 3: stable scatter. Within a chunk, a slot's rank among equal
