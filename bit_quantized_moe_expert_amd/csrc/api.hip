@@ -118,6 +118,7 @@ struct ForwardCarve {
   RouteBufs rb;
   float *h;
   float *slotbuf;
+  uint8_t *xq;  // MXFP4: x as the block-scaled MFMA operand (launch_e4m3_split), else null
   size_t bytes;
 };
 
@@ -134,6 +135,7 @@ ForwardCarve carve_forward(void *ws, const nf4moe_layer_t &L, int T) {
   carve_route_scratch(cv, rp, L.E, fc.rb);
   fc.h = cv.take<float>((size_t)(rp.R > 0 ? rp.R : 1) * L.I);
   fc.slotbuf = cv.take<float>((size_t)(rp.R > 0 ? rp.R : 1) * L.H);
+  fc.xq = L.fmt == NF4MOE_FMT_MXFP4_B32 ? cv.take<uint8_t>(e4m3_split_bytes(T > 0 ? T : 1, L.H)) : nullptr;
   fc.bytes = align_up(cv.off);
   return fc;
 }
@@ -536,6 +538,11 @@ static nf4moe_status_t forward_impl(const nf4moe_layer_t *layer, const uint16_t 
   GemmArgs g = base_args(L.fmt);
   g.a = x;
   g.a_is_f32 = 0;
+  if (use == NF4MOE_PATH_MFMA && fc.xq) {  // MXFP4: block-scaled MFMAs on an e4m3 split of x
+    if ((e = launch_e4m3_split(x, T, L.H, fc.xq, s)) != hipSuccess) return hip_status(e, "split launch");
+    g.a = fc.xq;
+    g.a_is_f32 = 3;
+  }
   g.a_row_of = fc.rb.sorted_slots;
   g.a_div = L.top_k;
   g.a_rows = T;

@@ -77,8 +77,9 @@ hipError_t launch_groups_from_offsets(const int32_t *goff, const int32_t *gexp, 
 enum Epi { EPI_SWIGLU = 0, EPI_PLAIN_F32 = 1, EPI_PLAIN_BF16 = 2, EPI_SLOT = 3 };
 struct GemmArgs {
   int fmt;
-  const void *a;            // bf16 [*, K] (a_is_f32 = 0), fp32 [*, K] (1), or 32-bit
-  int a_is_f32;             //   (bf16 hi, bf16 lo) pairs [*, K] (2: MFMA path only)
+  const void *a;            // bf16 [*, K] (a_is_f32 = 0), fp32 [*, K] (1), 32-bit
+  int a_is_f32;             //   (bf16 hi, bf16 lo) pairs [*, K] (2: MFMA path only), or
+                            //   the e4m3 split of launch_e4m3_split (3: MXFP4 MFMA SwiGLU only)
   const int32_t *a_row_of;  // row r reads a[a_row_of[r]] or, with a_div > 1, a[a_row_of[r] / a_div]
   int a_div;
   int a_rows;               // rows of a: a gathered row index is clamped into [0, a_rows)
@@ -142,6 +143,11 @@ inline int mfma_tile_rows(int64_t R, int64_t G) {
       hipLaunchKernelGGL(KERNEL, GRID, BLOCK, 0, STREAM, __VA_ARGS__);                            \
   } while (0)
 hipError_t launch_gemv_grouped(const GemmArgs &g, int ms_hint, hipStream_t s);
+// bf16 [rows, K] (K % 32 == 0) -> the block-scaled operand of the MXFP4 MFMA
+// kernels: e4m3 planes a1, a2 [rows, K] and e8m0 scales [rows, K / 32], with
+// x = 2^(scale - 127) * (a1 + a2).
+size_t e4m3_split_bytes(int64_t rows, int K);
+hipError_t launch_e4m3_split(const uint16_t *x, int64_t rows, int K, uint8_t *q, hipStream_t s);
 hipError_t launch_mfma_grouped(const GemmArgs &g, hipStream_t s);
 
 // Token-centric down projection + combine for a handful of tokens; the same

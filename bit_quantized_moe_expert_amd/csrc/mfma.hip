@@ -26,6 +26,8 @@
 //    and meet through LDS in the epilogue.
 // Workgroups are remapped so consecutive tiles sharing a weight tile land on
 // the same XCD (its L2), with tiles of one expert adjacent.
+#include <type_traits>
+
 #include "common.h"
 #include "internal.h"
 
@@ -36,6 +38,9 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 constexpr int kBK = 64;
 constexpr int kApad = 72;     // bf16 per LDS row of A (64 + 8 padding)
+constexpr int kQrow = 144;    // bytes per LDS row of an e4m3-split A: two 64-byte planes, 2 scale bytes, pad
+
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
 
 __device__ inline bf16x8_t as_bf16x8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
   const uint4 v = make_uint4(a, b, c, d);
@@ -82,15 +87,16 @@ __device__ inline void build_mfma_table(uint4 *tab) {
 template <int FMT, int EPI, int AM, int XF, int MB>
 __device__ __forceinline__ void mfma_tile(const GemmArgs &p, uint8_t *smem, int nt, int e, int trow0,
                                           int trows) {
-  static_assert(AM == 0 || AM == 2, "operand mode");
+  static_assert(AM == 0 || AM == 2 || (AM == 3 && FMT == 1), "operand mode");
   static_assert(MB == 4 || MB == 2 || MB == 1, "row blocks");
-  constexpr bool AF32 = AM != 0;                      // a lo part exists
+  constexpr bool AF32 = AM == 2;                      // a lo part exists
+  constexpr bool AQ8 = AM == 3;                       // A as e4m3 planes: block-scaled MFMAs, no decode
   constexpr int kBM = 32 * MB;                        // rows per tile
-  constexpr int ABUF = kBM * kApad * 2;               // bytes per A buffer
+  constexpr int ABUF = AQ8 ? kBM * kQrow : kBM * kApad * 2;  // bytes per A buffer
 
-  build_mfma_table<FMT>(reinterpret_cast<uint4 *>(smem));
-  auto abuf = [&](int hi_lo, int buf) -> uint16_t * {
-    return reinterpret_cast<uint16_t *>(smem + kTabBytes + (hi_lo * 2 + buf) * ABUF);
+  if constexpr (!AQ8) build_mfma_table<FMT>(reinterpret_cast<uint4 *>(smem));
+  auto abuf = [&](int hi_lo, int buf) __attribute__((always_inline)) -> uint16_t * {
+    return reinterpret_cast<uint16_t *>(smem + (AQ8 ? 0 : kTabBytes) + (hi_lo * 2 + buf) * ABUF);
   };
 
   const int tid = threadIdx.x;
@@ -125,8 +131,10 @@ __device__ __forceinline__ void mfma_tile(const GemmArgs &p, uint8_t *smem, int 
   // first) and are zeroed when stored (measured: storing them unmasked, which
   // the results would allow, made the 64-row kernels 2-3 % slower).
   // A 32-row bf16 tile is 256 16-byte words: there the first 256 threads fill
-  // it (NFILL) and the other waves skip the store.
-  constexpr int TPR = (MB == 1 && !AF32) ? 8 : 512 / kBM;  // fill threads per row
+  // it (NFILL) and the other waves skip the store. An e4m3-split row is 128
+  // bytes of planes (+ 2 scale bytes): 4 threads of 32 bytes (128-row tiles)
+  // or 8 of 16.
+  constexpr int TPR = AQ8 ? (MB == 4 ? 4 : 8) : (MB == 1 && !AF32) ? 8 : 512 / kBM;  // fill threads per row
   constexpr int EPT = 64 / TPR;                       // elements per thread: 16, 8 or 4
   constexpr int NFILL = kBM * TPR;                    // threads that fill the tile
   const int am = tid / TPR, aq = tid % TPR;
@@ -137,12 +145,30 @@ __device__ __forceinline__ void mfma_tile(const GemmArgs &p, uint8_t *smem, int 
     arow = p.a_row_of ? (int64_t)(p.a_row_of[r] / p.a_div) : (int64_t)r;
     arow = arow < 0 ? 0 : (arow < p.a_rows ? arow : p.a_rows - 1);  // a bad index cannot read past a
   }
-  constexpr int AW = EPT * (AF32 ? 4 : 2) / 16;       // 16-byte words per thread
+  constexpr int AW = AQ8 ? 128 / TPR / 16 : EPT * (AF32 ? 4 : 2) / 16;  // 16-byte words per thread
   // Two register sets: the slice for K-step k + 2 is loaded while the one for
   // k + 1 (loaded a step earlier) waits to be stored to LDS.
-  uint4 aregs[2][AW];
-  bool aoks[2] = {false, false};
-  auto load_a = [&](int64_t k0, int set) {
+  // Register sets of the A slice: two (the slice of step k + 2 loads while
+  // that of k + 1 waits to be stored), four for AQ8 (loads four steps ahead).
+  constexpr int NSET = AQ8 ? 4 : 2;
+  uint4 aregs[NSET][AW];
+  bool aoks[NSET] = {};
+  uint32_t ascl[NSET] = {};  // AQ8: the row's two e8m0 scale bytes of the step
+  auto load_a = [&](int64_t k0, int set) __attribute__((always_inline)) {
+    if constexpr (AQ8) {
+      // planes a1 [a_rows][K], a2 [a_rows][K], then scales [a_rows][K / 32]
+      const int plane = aq / (TPR / 2), part = aq % (TPR / 2);
+      const int64_t kc = k0 < K ? k0 : 0;
+      aoks[set] = arow_ok && k0 < K;
+      const uint8_t *q8 = reinterpret_cast<const uint8_t *>(p.a);
+      const uint4 *src = reinterpret_cast<const uint4 *>(q8 + (int64_t)plane * p.a_rows * K + arow * K + kc +
+                                                         part * (AW * 16));
+#pragma unroll
+      for (int i = 0; i < AW; ++i) aregs[set][i] = src[i];
+      if (aq == 0)
+        ascl[set] = *reinterpret_cast<const uint16_t *>(q8 + 2 * (int64_t)p.a_rows * K + arow * (K / 32) + kc / 32);
+      return;
+    }
     const int64_t kk = k0 + EPT * aq;
     aoks[set] = arow_ok && kk < K;
     const int64_t kc = kk < K ? kk : 0;
@@ -152,10 +178,19 @@ __device__ __forceinline__ void mfma_tile(const GemmArgs &p, uint8_t *smem, int 
 #pragma unroll
     for (int i = 0; i < AW; ++i) aregs[set][i] = src[i];
   };
-  auto store_a = [&](int buf, int set) {
+  auto store_a = [&](int buf, int set) __attribute__((always_inline)) {
     if (NFILL < 512 && tid >= NFILL) return;  // whole waves
     const uint4 *areg = aregs[set];
     const bool a_ok = aoks[set];
+    if constexpr (AQ8) {  // rows past the tile (or K) as zeros with scale 2^0
+      const int plane = aq / (TPR / 2), part = aq % (TPR / 2);
+      uint8_t *row = reinterpret_cast<uint8_t *>(abuf(0, buf)) + am * kQrow;
+#pragma unroll
+      for (int i = 0; i < AW; ++i)
+        *reinterpret_cast<uint4 *>(row + plane * 64 + part * (AW * 16) + 16 * i) = a_ok ? areg[i] : make_uint4(0, 0, 0, 0);
+      if (aq == 0) *reinterpret_cast<uint16_t *>(row + 128) = (uint16_t)(a_ok ? ascl[set] : 0x7f7fu);
+      return;
+    }
     uint16_t *dh = abuf(0, buf) + am * kApad + EPT * aq;
     if (AM == 2 && EPT == 4) {  // four pairs: 8 bytes into each tile
       uint16_t *dl = abuf(1, buf) + am * kApad + EPT * aq;
@@ -190,7 +225,7 @@ __device__ __forceinline__ void mfma_tile(const GemmArgs &p, uint8_t *smem, int 
   // B: one 16-byte chunk of codes per lane, k in [k0 + 32 g, +32), plus the
   // raw scale and whether it counts. The scale is masked only when it is
   // consumed, a K-step later, so nothing waits on these loads early.
-  auto load_b = [&](int64_t k0, uint4 &bq, uint32_t &braw, bool &bok) {
+  auto load_b = [&](int64_t k0, uint4 &bq, uint32_t &braw, bool &bok) __attribute__((always_inline)) {
     const int64_t kk = k0 + 32 * g;
     bok = nvalid && kk < K;
     const int64_t kc = kk < K ? kk : 0;
@@ -198,7 +233,7 @@ __device__ __forceinline__ void mfma_tile(const GemmArgs &p, uint8_t *smem, int 
     const int64_t sidx = Fmt<FMT>::kNF4 ? (k0 < K ? k0 / 64 : 0) : kc / 32;
     braw = Fmt<FMT>::raw(p.B_scale, sc_base + nrow_c * sc_per_row + sidx);
   };
-  auto scale_of = [&](uint32_t raw, bool ok) -> float {
+  auto scale_of = [&](uint32_t raw, bool ok) __attribute__((always_inline)) -> float {
     const float v = Fmt<FMT>::value(raw);
     return ok ? v : 0.0f;
   };
@@ -213,7 +248,7 @@ __device__ __forceinline__ void mfma_tile(const GemmArgs &p, uint8_t *smem, int 
   // at the start, the codes and scale of step k + 2 into bq / br / bok once
   // this step's lookups have read bq; the slice of step k + 1 (set aset ^ 1)
   // goes to the other LDS buffer at the end.
-  auto step = [&](int64_t k0, int cur, int aset, uint4 &bq, float bs, uint32_t &br, bool &bok) {
+  auto step = [&](int64_t k0, int cur, int aset, uint4 &bq, float bs, uint32_t &br, bool &bok) __attribute__((always_inline)) {
     // Loads are issued (from clamped, valid addresses) and stored even past
     // the last step, so no branch splits the load/wait bookkeeping; the
     // extra data is unused.
@@ -230,7 +265,7 @@ __device__ __forceinline__ void mfma_tile(const GemmArgs &p, uint8_t *smem, int 
     constexpr int NA = AF32 ? 1 : 2;
     uint2 t[2][4];
     bf16x8_t ah[NA][MB], al[NA][MB];
-    auto read_a = [&](int sa, bf16x8_t *dh, bf16x8_t *dl) {
+    auto read_a = [&](int sa, bf16x8_t *dh, bf16x8_t *dl) __attribute__((always_inline)) {
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
         const int row = mb * 32 + l32;
@@ -309,25 +344,157 @@ __device__ __forceinline__ void mfma_tile(const GemmArgs &p, uint8_t *smem, int 
     return more;
   };
 
-  uint4 bq0, bq1;
-  uint32_t br0, br1;
-  bool bok0, bok1;
-  load_a(0, 0);
-  load_b(0, bq0, br0, bok0);
-  load_a(kBK, 1);
-  load_b(kBK, bq1, br1, bok1);
-  store_a(0, 0);
-  lds_barrier();
-  float bs0 = scale_of(br0, bok0), bs1;
+  if constexpr (AQ8) {
+    // Block-scaled MXFP4 loop. Steps are short here (no decode; half the
+    // MFMA time of the NF4 products), and per-lane weight loads (each lane
+    // its own weight row, 32 rows per instruction) kept the vector memory
+    // unit busy 83 % of the time. So the workgroup stages its 256 weight rows
+    // through LDS four K-steps at a time (a super-step: 128 bytes of codes
+    // and 8 scale bytes per row), loaded 128 contiguous bytes per 8 lanes, and
+    // each wave reads its MFMA operand (row l32, 32 codes of half g) from LDS.
+    // A goes through LDS per step, its loads four steps ahead as before.
+    constexpr int kBrow = 144;                       // LDS bytes per staged weight row
+    uint8_t *Bs = smem + 2 * ABUF;                    // after the two A buffers: [2][256][kBrow]
+    const int64_t n_ss = (K + 4 * kBK - 1) / (4 * kBK);  // super-steps
+    // global row of staged row i (wave i / 32, column i % 32), clamped when past N
+    auto staged_row = [&](int i) __attribute__((always_inline)) -> int64_t {
+      const int w = i >> 5, c = i & 31;
+      int64_t cl, nr;
+      if (EPI == EPI_SWIGLU) {
+        cl = (int64_t)nt * 128 + 32 * (w & 3) + c;
+        nr = (XF && p.glu_inter) ? 2 * cl + (w >> 2) : cl + (w >> 2) * ncol;
+      } else {
+        cl = (int64_t)nt * 256 + 32 * w + c;
+        nr = cl;
+      }
+      return cl < ncol ? nr : 0;
+    };
+    // staging registers of one super-step (named, not arrays: a loop over an
+    // array here is indexed at run time when the compiler first places it)
+    uint4 bst0, bst1, bst2, bst3;
+    uint32_t sst0 = 0, sst1 = 0, sst2 = 0, sst3 = 0;
+    auto bcode_src = [&](int64_t kb, int i) __attribute__((always_inline)) -> const uint4 * {
+      const int id = i * 512 + tid, r = id >> 3, part = id & 7;
+      const int64_t off = kb / 2 + 16 * part;
+      return reinterpret_cast<const uint4 *>(Be + staged_row(r) * rowbytes + (off < rowbytes ? off : 0));
+    };
+    // the two scale bytes of step i of the super-step (byte loads: MXFP4
+    // scales carry no alignment); K % 64 == 0, so both are in the row or
+    // the pair is clamped to its start
+    auto bscale_pair = [&](const uint8_t *sr, int64_t kb, int i) __attribute__((always_inline)) -> uint32_t {
+      const int64_t k32 = kb / 32 + 2 * i;
+      const uint8_t *q = sr + (k32 < sc_per_row ? k32 : 0);
+      return (uint32_t)q[0] | ((uint32_t)q[1] << 8);
+    };
+    auto load_bss = [&](int64_t j) __attribute__((always_inline)) {  // super-step j into registers (clamped addresses)
+      const int64_t kb = j * 4 * kBK;
+      bst0 = *bcode_src(kb, 0);
+      bst1 = *bcode_src(kb, 1);
+      bst2 = *bcode_src(kb, 2);
+      bst3 = *bcode_src(kb, 3);
+      if (tid < 256) {
+        const uint8_t *sr = reinterpret_cast<const uint8_t *>(p.B_scale) + sc_base + staged_row(tid) * sc_per_row;
+        sst0 = bscale_pair(sr, kb, 0);
+        sst1 = bscale_pair(sr, kb, 1);
+        sst2 = bscale_pair(sr, kb, 2);
+        sst3 = bscale_pair(sr, kb, 3);
+      }
+    };
+    auto store_bss = [&](int buf) __attribute__((always_inline)) {
+      uint8_t *base = Bs + buf * 256 * kBrow;
+      auto dst = [&](int i) __attribute__((always_inline)) -> uint4 * {
+        const int id = i * 512 + tid, r = id >> 3, part = id & 7;
+        return reinterpret_cast<uint4 *>(base + r * kBrow + 16 * part);
+      };
+      *dst(0) = bst0;
+      *dst(1) = bst1;
+      *dst(2) = bst2;
+      *dst(3) = bst3;
+      if (tid < 256)
+        *reinterpret_cast<uint2 *>(base + tid * kBrow + 128) = make_uint2(sst0 | (sst1 << 16), sst2 | (sst3 << 16));
+    };
+    // written out: a loop here would index the A register sets at run time
+    // when the compiler first places them (in scratch)
+    load_a(0, 0);
+    load_a(kBK, 1);
+    load_a(2 * kBK, 2);
+    load_a(3 * kBK, 3);
+    load_bss(0);
+    store_a(0, 0);
+    store_bss(0);
+    if (n_ss > 1) load_bss(1);
+    lds_barrier();
+    // step s of super-step j: A from LDS buffer cur, B from staged buffer j % 2
+    // (cur, set, s are compile-time constants: each call is its own
+    // instantiation, so the register sets are never indexed at run time)
+    auto qstep = [&](int64_t k0, auto cur_c, auto set_c, auto s_c, int64_t j) __attribute__((always_inline)) -> bool {
+      constexpr int cur = decltype(cur_c)::value, set = decltype(set_c)::value, s = decltype(s_c)::value;
+      const bool more = k0 + kBK < K;
+      load_a(k0 + 4 * kBK, set);
+      __builtin_amdgcn_sched_barrier(0);
+      // B: this lane's 32 e2m1 codes (k0 + 32 g ...) and their e8m0 scale; A:
+      // row l32 of each 32-row block, k = 16 g + 0..15 and 32 + 16 g + 0..15
+      // of each plane, and the row's scale for block g. C += A1 * B + A2 * B
+      // with both operands' block scales applied.
+      const uint8_t *brow = Bs + (j & 1) * 256 * kBrow + (wave * 32 + l32) * kBrow;
+      const uint4 bq = *reinterpret_cast<const uint4 *>(brow + 32 * s + 16 * g);
+      const int sb = brow[128 + 2 * s + g];
+      const i32x8_t bv = {(int)bq.x, (int)bq.y, (int)bq.z, (int)bq.w, 0, 0, 0, 0};
+      const uint8_t *A8 = reinterpret_cast<const uint8_t *>(abuf(0, cur));
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        const uint8_t *row = A8 + (mb * 32 + l32) * kQrow;
+        const uint4 p0 = *reinterpret_cast<const uint4 *>(row + 16 * g);
+        const uint4 p1 = *reinterpret_cast<const uint4 *>(row + 32 + 16 * g);
+        const uint4 q0 = *reinterpret_cast<const uint4 *>(row + 64 + 16 * g);
+        const uint4 q1 = *reinterpret_cast<const uint4 *>(row + 96 + 16 * g);
+        const int sa = row[128 + g];
+        const i32x8_t a1 = {(int)p0.x, (int)p0.y, (int)p0.z, (int)p0.w, (int)p1.x, (int)p1.y, (int)p1.z, (int)p1.w};
+        const i32x8_t a2 = {(int)q0.x, (int)q0.y, (int)q0.z, (int)q0.w, (int)q1.x, (int)q1.y, (int)q1.z, (int)q1.w};
+        C[mb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a1, bv, C[mb], 0, 4, 0, sa, 0, sb);
+        C[mb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a2, bv, C[mb], 0, 4, 0, sa, 0, sb);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      store_a(cur ^ 1, (set + 1) & 3);
+      if (s == 3) {  // super-step j + 1 into the other staged buffer (read last in j - 1)
+        store_bss((int)((j + 1) & 1));
+        if (j + 2 < n_ss) load_bss(j + 2);
+      }
+      lds_barrier();
+      return more;
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    using I3 = std::integral_constant<int, 3>;
+    for (int64_t j = 0;; ++j) {
+      const int64_t k0 = j * 4 * kBK;
+      if (!qstep(k0, I0{}, I0{}, I0{}, j)) break;
+      if (!qstep(k0 + kBK, I1{}, I1{}, I1{}, j)) break;
+      if (!qstep(k0 + 2 * kBK, I0{}, I2{}, I2{}, j)) break;
+      if (!qstep(k0 + 3 * kBK, I1{}, I3{}, I3{}, j)) break;
+    }
+  } else {
+    uint4 bq0, bq1;
+    uint32_t br0, br1;
+    bool bok0, bok1;
+    load_a(0, 0);
+    load_b(0, bq0, br0, bok0);
+    load_a(kBK, 1);
+    load_b(kBK, bq1, br1, bok1);
+    store_a(0, 0);
+    lds_barrier();
+    float bs0 = scale_of(br0, bok0), bs1;
 
-  // Unrolled by two so the register sets alternate without copies: step k
-  // computes on B set k % 2 and LDS buffer k % 2, loads A(k + 2) into set
-  // k % 2 and stores A(k + 1) from set (k + 1) % 2.
-  for (int64_t k0 = 0;; k0 += 2 * kBK) {
-    if (!step(k0, 0, 0, bq0, bs0, br0, bok0)) break;
-    bs1 = scale_of(br1, bok1);
-    if (!step(k0 + kBK, 1, 1, bq1, bs1, br1, bok1)) break;
-    bs0 = scale_of(br0, bok0);
+    // Unrolled by two so the register sets alternate without copies: step k
+    // computes on B set k % 2 and LDS buffer k % 2, loads A(k + 2) into set
+    // k % 2 and stores A(k + 1) from set (k + 1) % 2.
+    for (int64_t k0 = 0;; k0 += 2 * kBK) {
+      if (!step(k0, 0, 0, bq0, bs0, br0, bok0)) break;
+      bs1 = scale_of(br1, bok1);
+      if (!step(k0 + kBK, 1, 1, bq1, bs1, br1, bok1)) break;
+      bs0 = scale_of(br0, bok0);
+    }
   }
 
   // ---- epilogue. 32x32 accumulator: lane holds column l32, rows
@@ -412,8 +579,12 @@ template <int FMT, int EPI, int AM, int XF, int TR>
 __global__ __launch_bounds__(512) void k_mfma(GemmArgs p, int ntn, int per) {
   static_assert(TR == 64 || TR == 128, "tile rows");
   // the decode table and the A buffers of the tallest body (hi[2], and lo[2]
-  // for an fp32 A)
-  __shared__ __attribute__((aligned(16))) uint8_t smem[kTabBytes + (AM != 0 ? 4 : 2) * TR * kApad * 2];
+  // for an fp32 A); e4m3-split A: no table, two buffers, and room for the
+  // SwiGLU epilogue's exchange of the up values
+  constexpr int kXch = TR / 32 * 4 * 16 * 64 * 4;
+  constexpr int kQ8 = 2 * TR * kQrow + 2 * 256 * 144;  // A buffers + staged weight rows
+  constexpr int kSmem = AM == 3 ? (kQ8 > kXch ? kQ8 : kXch) : kTabBytes + (AM == 2 ? 4 : 2) * TR * kApad * 2;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kSmem];
   // XCD-aware order: hardware XCD = blockIdx.x % 8; give each XCD a contiguous
   // run of (n-tile major, tile minor) work, so the M-tiles of one expert and
   // one weight tile share that XCD's L2.
@@ -452,6 +623,83 @@ static hipError_t launch_mfma_t(const GemmArgs &g, hipStream_t s) {
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// bf16 activations as the MXFP4 kernels' block-scaled operand: per 32-element
+// block of a row, s = floor(log2 max |x|) - 7 (so |x| / 2^s < 256, inside
+// e4m3's range), the e8m0 byte s + 127, and two e4m3 parts a1 = RNE(x / 2^s),
+// a2 = RNE(x / 2^s - a1). A bf16 value has 8 significant bits and e4m3 4, so
+// a1 + a2 = x / 2^s exactly for every element within 2^9 of the block
+// maximum (smaller ones keep an error below 2^-17 of that maximum).
+// Layout: plane a1 [rows][K], plane a2 [rows][K], scales [rows][K / 32].
+// ---------------------------------------------------------------------------
+__device__ inline uint32_t e4m3_rne(float v) {  // finite, |v| <= 448
+  const uint32_t sgn = (__float_as_uint(v) >> 24) & 0x80u;
+  const float a = fabsf(v);
+  uint32_t c;
+  if (a < 0.015625f) {  // below 2^-6: steps of 2^-9 (8 is the smallest normal, code 0x08)
+    c = (uint32_t)__builtin_rintf(a * 512.0f);
+  } else {              // round the fp32 significand to 3 bits (to even), then rebias 127 -> 7
+    const uint32_t b = __float_as_uint(a);
+    c = ((b + 0x7ffffu + ((b >> 20) & 1u)) >> 20) - (120u << 3);
+  }
+  return sgn | c;
+}
+
+__device__ inline float e4m3_value(uint32_t c) {
+  const uint32_t ex = (c >> 3) & 15u, m = c & 7u;
+  const float mag = ex == 0 ? (float)m * 0.001953125f : __uint_as_float(((ex + 120u) << 23) | (m << 20));
+  return (c & 0x80u) ? -mag : mag;
+}
+
+__global__ __launch_bounds__(256) void k_e4m3_split(const uint16_t *__restrict__ x, int64_t rows, int K,
+                                                    uint8_t *__restrict__ q) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // 8 elements per thread
+  const int64_t n8 = rows * (K / 8);
+  const bool ok = i < n8;
+  const uint4 xv = ok ? reinterpret_cast<const uint4 *>(x)[i] : make_uint4(0, 0, 0, 0);
+  const uint32_t w[4] = {xv.x, xv.y, xv.z, xv.w};
+  float f[8];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    f[2 * j] = __uint_as_float(w[j] << 16);
+    f[2 * j + 1] = __uint_as_float(w[j] & 0xffff0000u);
+  }
+  float m = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(f[j]));
+  m = fmaxf(m, __shfl_xor(m, 1, 4));  // the 32-block: 4 consecutive lanes
+  m = fmaxf(m, __shfl_xor(m, 2, 4));
+  int sx = m > 0.0f ? (int)((__float_as_uint(m) >> 23) & 0xffu) - 127 - 7 : 0;
+  sx = sx < -127 ? -127 : (sx > 126 ? 126 : sx);
+  const float inv = __uint_as_float((uint32_t)(127 - sx) << 23);  // 2^-s
+  uint32_t p1[2] = {0u, 0u}, p2[2] = {0u, 0u};
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const float t = f[j] * inv;
+    const uint32_t c1 = e4m3_rne(t);
+    const uint32_t c2 = e4m3_rne(t - e4m3_value(c1));
+    p1[j / 4] |= c1 << (8 * (j % 4));
+    p2[j / 4] |= c2 << (8 * (j % 4));
+  }
+  if (!ok) return;
+  const int64_t row = i / (K / 8), c8 = i % (K / 8);
+  uint8_t *a1 = q + row * K + 8 * c8;
+  uint8_t *a2 = a1 + rows * K;
+  *reinterpret_cast<uint2 *>(a1) = make_uint2(p1[0], p1[1]);
+  *reinterpret_cast<uint2 *>(a2) = make_uint2(p2[0], p2[1]);
+  if ((c8 & 3) == 0) q[2 * rows * K + row * (K / 32) + c8 / 4] = (uint8_t)(sx + 127);
+}
+
+size_t e4m3_split_bytes(int64_t rows, int K) { return (size_t)rows * K * 2 + (size_t)rows * (K / 32); }
+
+hipError_t launch_e4m3_split(const uint16_t *x, int64_t rows, int K, uint8_t *q, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  if (K % 32) return hipErrorInvalidValue;
+  const int64_t n8 = rows * (K / 8);
+  hipLaunchKernelGGL(k_e4m3_split, dim3((unsigned)cdiv(n8, 256)), dim3(256), 0, s, x, rows, K, q);
+  return hipGetLastError();
+}
+
 // Instantiated operand modes: SwiGLU (gate_up) and plain outputs bf16 A; slot
 // output (down projection) the pre-split planes.
 template <int FMT>
@@ -460,6 +708,10 @@ static hipError_t mfma_pick(const GemmArgs &g, hipStream_t s) {
   if (xf && g.epi != EPI_SWIGLU && g.epi != EPI_SLOT) return hipErrorInvalidValue;
   switch (g.epi) {
     case EPI_SWIGLU:
+      if constexpr (FMT == 1) {  // MXFP4 with an e4m3-split A: block-scaled MFMAs
+        if (g.a_is_f32 == 3)
+          return xf ? launch_mfma_t<FMT, EPI_SWIGLU, 3, 1>(g, s) : launch_mfma_t<FMT, EPI_SWIGLU, 3>(g, s);
+      }
       if (g.a_is_f32 != 0) return hipErrorInvalidValue;
       return xf ? launch_mfma_t<FMT, EPI_SWIGLU, 0, 1>(g, s) : launch_mfma_t<FMT, EPI_SWIGLU, 0>(g, s);
     case EPI_PLAIN_F32:
