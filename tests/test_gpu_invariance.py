@@ -117,14 +117,14 @@ def test_mfma_row_count_invariance_per_router_window(wl):
     does not depend on the rows sharing its tile or on the tile height (64- or
     128-row tables and bodies)."""
     layer, o_layer, _ = build_layers(wl, 0, DEV, path=M.PATH_MFMA)
-    X = S.make_x(wl, 600)
+    X = S.make_x(wl, 1100)  # the router takes 128-token waves from 1024 tokens on
     full = _run(layer, X)
-    rows = [0, 599]
+    rows = [0, 599, 1099]
     ref = O.moe_forward(o_layer, X[rows], topk_ids_override=full[1][rows])
     check_bound(O.bf16_bits_to_f64(full[0][rows].view(np.uint16)), ref, f"{wl.name} MFMA")
-    for T in (17, 33, 177, 256, 257, 411):
-        _same(_run(layer, X[:T]), tuple(f[:T] for f in full), f"{wl.name} MFMA: first {T} of 600")
-    perm = np.array([599, 3, 300, 0, 1] + list(range(100, 120)))  # 25 tokens, another order
+    for T in (17, 33, 177, 256, 257, 411, 1023, 1024):
+        _same(_run(layer, X[:T]), tuple(f[:T] for f in full), f"{wl.name} MFMA: first {T} of 1100")
+    perm = np.array([1099, 3, 300, 0, 1] + list(range(100, 120)))  # 25 tokens, another order
     _same(_run(layer, np.ascontiguousarray(X[perm])), tuple(f[perm] for f in full), f"{wl.name} MFMA: permuted")
     upto = _run(layer, X[:16])
     for T in (1, 2, 9, 15):
