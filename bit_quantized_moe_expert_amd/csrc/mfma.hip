@@ -585,14 +585,36 @@ __global__ __launch_bounds__(512) void k_mfma(GemmArgs p, int ntn, int per) {
   constexpr int kQ8 = 2 * TR * kQrow + 2 * 256 * 144;  // A buffers + staged weight rows
   constexpr int kSmem = AM == 3 ? (kQ8 > kXch ? kQ8 : kXch) : kTabBytes + (AM == 2 ? 4 : 2) * TR * kApad * 2;
   __shared__ __attribute__((aligned(16))) uint8_t smem[kSmem];
-  // XCD-aware order: hardware XCD = blockIdx.x % 8; give each XCD a contiguous
-  // run of (n-tile major, tile minor) work, so the M-tiles of one expert and
-  // one weight tile share that XCD's L2.
+  // XCD-aware order: hardware XCD = blockIdx.x % 8; each XCD takes an equal
+  // contiguous run of the work, in one of two orders (results do not depend
+  // on it):
+  //  - tile major, n-tile minor, over the tiles the device table holds (the
+  //    grid is sized for the most tiles): the workgroups an XCD runs at once
+  //    cover a few row tiles across all their weight tiles, so a row tile's
+  //    activations, and a weight tile read by an expert's consecutive row
+  //    tiles, are fetched into that XCD's L2 once (gate_up FETCH_SIZE -64 %
+  //    at the OLMoE-shaped prefill; gpt-oss-shaped T = 2048 gate_up 716 ->
+  //    675 us, down 648 -> 577 us; Qwen3-shaped T = 512 gate_up 161 -> 132 us);
+  //  - n-tile major, tile minor over the whole grid, for the NF4 down
+  //    projections, which ran 3-10 % slower in tile-major order.
+  constexpr bool kTileMajor = EPI == EPI_SWIGLU || FMT == 1;
   const int L = blockIdx.x;
-  const int Lp = (L & 7) * per + (L >> 3);
-  if (Lp >= p.max_tiles * ntn) return;
-  const int nt = Lp / p.max_tiles, ti = Lp % p.max_tiles;
-  if (ti >= *p.n_tiles) return;
+  int ti, nt;
+  if constexpr (kTileMajor) {
+    const int total = min(*p.n_tiles, p.max_tiles) * ntn;
+    const int per_xcd = (total + 7) >> 3;
+    if ((L >> 3) >= per_xcd) return;
+    const int Lp = (L & 7) * per_xcd + (L >> 3);
+    if (Lp >= total) return;
+    ti = Lp / ntn;
+    nt = Lp % ntn;
+  } else {
+    const int Lp = (L & 7) * per + (L >> 3);
+    if (Lp >= p.max_tiles * ntn) return;
+    nt = Lp / p.max_tiles;
+    ti = Lp % p.max_tiles;
+    if (ti >= *p.n_tiles) return;
+  }
   const int4 tile = p.tiles[ti];  // expert, row0, rows, rows of the whole group
   const int rows = __builtin_amdgcn_readfirstlane(tile.z);
   if constexpr (TR == 128) {
