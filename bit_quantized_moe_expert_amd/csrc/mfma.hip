@@ -146,11 +146,14 @@ __device__ __forceinline__ void mfma_tile(const GemmArgs &p, uint8_t *smem, int 
     arow = arow < 0 ? 0 : (arow < p.a_rows ? arow : p.a_rows - 1);  // a bad index cannot read past a
   }
   constexpr int AW = AQ8 ? 128 / TPR / 16 : EPT * (AF32 ? 4 : 2) / 16;  // 16-byte words per thread
-  // Two register sets: the slice for K-step k + 2 is loaded while the one for
-  // k + 1 (loaded a step earlier) waits to be stored to LDS.
-  // Register sets of the A slice: two (the slice of step k + 2 loads while
-  // that of k + 1 waits to be stored), four for AQ8 (loads four steps ahead).
-  constexpr int NSET = AQ8 ? 4 : 2;
+  // Loads run NSET K-steps ahead, one register set per step in flight (the
+  // slice of step k + NSET loads while that of k + 1 waits to be stored to
+  // LDS): two, four for the 32-row body, whose short steps leave two steps
+  // little time to cover the memory latency (OLMoE-shaped batches of 16 and
+  // 48 tokens 2 % faster; four sets in the 64-row body too gained nothing),
+  // and four for AQ8.
+  constexpr int NSET = AQ8 || MB == 1 ? 4 : 2;
+  static_assert(NSET == 2 || NSET == 4, "register sets");
   uint4 aregs[NSET][AW];
   bool aoks[NSET] = {};
   uint32_t ascl[NSET] = {};  // AQ8: the row's two e8m0 scale bytes of the step
@@ -243,17 +246,17 @@ __device__ __forceinline__ void mfma_tile(const GemmArgs &p, uint8_t *smem, int 
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) C[mb] = zero16;
 
-  // One K-step on LDS buffer `cur` with codes bq and scale bs. Loads run two
-  // steps ahead: the activation slice of step k + 2 into register set `aset`
-  // at the start, the codes and scale of step k + 2 into bq / br / bok once
-  // this step's lookups have read bq; the slice of step k + 1 (set aset ^ 1)
-  // goes to the other LDS buffer at the end.
+  // One K-step on LDS buffer `cur` with codes bq and scale bs. Loads run
+  // NSET steps ahead: the activation slice of step k + NSET into register set
+  // `aset` at the start, the codes and scale of step k + NSET into bq / br /
+  // bok once this step's lookups have read bq; the slice of step k + 1 (set
+  // (aset + 1) % NSET) goes to the other LDS buffer at the end.
   auto step = [&](int64_t k0, int cur, int aset, uint4 &bq, float bs, uint32_t &br, bool &bok) __attribute__((always_inline)) {
     // Loads are issued (from clamped, valid addresses) and stored even past
     // the last step, so no branch splits the load/wait bookkeeping; the
     // extra data is unused.
     const bool more = k0 + kBK < K;
-    load_a(k0 + 2 * kBK, aset);
+    load_a(k0 + NSET * kBK, aset);
     __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the MFMAs
     const uint16_t *Ah = abuf(0, cur);
     const uint16_t *Al = abuf(1, AF32 ? cur : 0);
@@ -285,8 +288,8 @@ __device__ __forceinline__ void mfma_tile(const GemmArgs &p, uint8_t *smem, int 
           t[sn & 1][q] = *reinterpret_cast<const uint2 *>(smem + tab_offset(word, lanebyte, q));
       }
       __builtin_amdgcn_sched_barrier(0);
-      if (u == 3) {  // every lookup of this step has read bq: reuse it for step k + 2
-        load_b(k0 + 2 * kBK, bq, br, bok);
+      if (u == 3) {  // every lookup of this step has read bq: reuse it for step k + NSET
+        load_b(k0 + NSET * kBK, bq, br, bok);
         __builtin_amdgcn_sched_barrier(0);
       }
       if (u >= 0) {
@@ -339,11 +342,15 @@ __device__ __forceinline__ void mfma_tile(const GemmArgs &p, uint8_t *smem, int 
         for (int v = 0; v < 16; ++v) C[mb][v] = fmaf(bs, P[mb][v], C[mb][v]);
     }
     __builtin_amdgcn_sched_barrier(0);  // the A store waits for its loads: keep it last
-    store_a(cur ^ 1, aset ^ 1);
+    store_a(cur ^ 1, (aset + 1) % NSET);
     lds_barrier();
     return more;
   };
 
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
   if constexpr (AQ8) {
     // Block-scaled MXFP4 loop. Steps are short here (no decode; half the
     // MFMA time of the NF4 products), and per-lane weight loads (each lane
@@ -463,10 +470,6 @@ __device__ __forceinline__ void mfma_tile(const GemmArgs &p, uint8_t *smem, int 
       lds_barrier();
       return more;
     };
-    using I0 = std::integral_constant<int, 0>;
-    using I1 = std::integral_constant<int, 1>;
-    using I2 = std::integral_constant<int, 2>;
-    using I3 = std::integral_constant<int, 3>;
     for (int64_t j = 0;; ++j) {
       const int64_t k0 = j * 4 * kBK;
       if (!qstep(k0, I0{}, I0{}, I0{}, j)) break;
@@ -475,25 +478,40 @@ __device__ __forceinline__ void mfma_tile(const GemmArgs &p, uint8_t *smem, int 
       if (!qstep(k0 + 3 * kBK, I1{}, I3{}, I3{}, j)) break;
     }
   } else {
-    uint4 bq0, bq1;
-    uint32_t br0, br1;
-    bool bok0, bok1;
+    // B register sets (named, so that no array is ever indexed at run time)
+    uint4 bq0, bq1, bq2, bq3;
+    uint32_t br0, br1, br2 = 0, br3 = 0;
+    bool bok0, bok1, bok2 = false, bok3 = false;
     load_a(0, 0);
     load_b(0, bq0, br0, bok0);
     load_a(kBK, 1);
     load_b(kBK, bq1, br1, bok1);
+    if constexpr (NSET == 4) {
+      load_a(2 * kBK, 2);
+      load_b(2 * kBK, bq2, br2, bok2);
+      load_a(3 * kBK, 3);
+      load_b(3 * kBK, bq3, br3, bok3);
+    }
     store_a(0, 0);
     lds_barrier();
-    float bs0 = scale_of(br0, bok0), bs1;
 
-    // Unrolled by two so the register sets alternate without copies: step k
-    // computes on B set k % 2 and LDS buffer k % 2, loads A(k + 2) into set
-    // k % 2 and stores A(k + 1) from set (k + 1) % 2.
-    for (int64_t k0 = 0;; k0 += 2 * kBK) {
-      if (!step(k0, 0, 0, bq0, bs0, br0, bok0)) break;
-      bs1 = scale_of(br1, bok1);
-      if (!step(k0 + kBK, 1, 1, bq1, bs1, br1, bok1)) break;
-      bs0 = scale_of(br0, bok0);
+    // Unrolled by NSET so the register sets rotate without copies: step k
+    // computes on B set k % NSET and LDS buffer k % 2, loads A(k + NSET) into
+    // set k % NSET and stores A(k + 1) from set (k + 1) % NSET.
+    auto one = [&](int64_t k0, auto I) __attribute__((always_inline)) -> bool {
+      constexpr int i = decltype(I)::value;
+      uint4 &bq = i == 0 ? bq0 : (i == 1 ? bq1 : (i == 2 ? bq2 : bq3));
+      uint32_t &br = i == 0 ? br0 : (i == 1 ? br1 : (i == 2 ? br2 : br3));
+      bool &bok = i == 0 ? bok0 : (i == 1 ? bok1 : (i == 2 ? bok2 : bok3));
+      return step(k0, i & 1, i, bq, scale_of(br, bok), br, bok);
+    };
+    for (int64_t k0 = 0;; k0 += NSET * kBK) {
+      if (!one(k0, I0{})) break;
+      if (!one(k0 + kBK, I1{})) break;
+      if constexpr (NSET == 4) {
+        if (!one(k0 + 2 * kBK, I2{})) break;
+        if (!one(k0 + 3 * kBK, I3{})) break;
+      }
     }
   }
 
