@@ -108,8 +108,10 @@ void carve_route_scratch(Carve &cv, const RoutePlan &rp, int E, RouteBufs &rb) {
   rb.grp_row0 = cv.take<int32_t>(E);
   rb.grp_rows = cv.take<int32_t>(E);
   rb.counters = cv.take<int32_t>(16);
-  // room for 64-row tiles whatever the plan, so the size only grows with R
-  rb.tiles = cv.take<int4>((size_t)cdiv(rp.R, 64) + rp.max_grp + 1);
+  // room for 64-row tiles whatever the plan, so the size only grows with R;
+  // the table in two orders (by group, then by tile class) at tiles and
+  // tiles + max_tiles
+  rb.tiles = cv.take<int4>(2 * ((size_t)cdiv(rp.R, 64) + rp.max_grp + 1));
 }
 
 struct ForwardCarve {
@@ -350,7 +352,7 @@ size_t nf4moe_gemm_workspace_bytes(int32_t G, int32_t R) {
   cv.take<int32_t>(G);
   cv.take<int32_t>(G);
   cv.take<int32_t>(16);
-  cv.take<int4>((size_t)cdiv(R, 64) + G);  // room for 64-row tiles
+  cv.take<int4>(2 * ((size_t)cdiv(R, 64) + G));  // 64-row tiles, both orders
   return align_up(cv.off);
 }
 
@@ -395,7 +397,7 @@ nf4moe_status_t nf4moe_grouped_gemm(nf4moe_format_t fmt, const uint16_t *a, cons
   rb.grp_row0 = cv.take<int32_t>(G);
   rb.grp_rows = cv.take<int32_t>(G);
   rb.counters = cv.take<int32_t>(16);
-  rb.tiles = cv.take<int4>((size_t)cdiv(R, 64) + G);
+  rb.tiles = cv.take<int4>(2 * ((size_t)cdiv(R, 64) + G));
   const int bm = mfma_tile_rows(R, G);
   hipError_t e = launch_groups_from_offsets(group_offsets, group_experts, G, R, E, rb, bm, s);
   if (e != hipSuccess) return hip_status(e, "group table launch");
@@ -458,7 +460,7 @@ nf4moe_status_t nf4moe_grouped_dgrad(nf4moe_format_t fmt, const uint16_t *dc, co
   rb.grp_row0 = cv.take<int32_t>(G);
   rb.grp_rows = cv.take<int32_t>(G);
   rb.counters = cv.take<int32_t>(16);
-  rb.tiles = cv.take<int4>((size_t)cdiv(R, kMfmaBM) + G);
+  rb.tiles = cv.take<int4>(2 * ((size_t)cdiv(R, kMfmaBM) + G));
   hipError_t e = launch_groups_from_offsets(group_offsets, group_experts, G, R, E, rb, kMfmaBM, s);
   if (e != hipSuccess) return hip_status(e, "group table launch");
   DgradArgs a;

@@ -254,7 +254,9 @@ __device__ inline void route_publish(const GemmArgs &p, const RouteToken<EPL> &r
     if (lane == 0) {
       o.expert_offsets[E] = k;
       o.counters[0] = k;
-      o.counters[1] = k;
+      o.counters[1] = k;  // one-row tiles: all of class 2
+      o.counters[2] = 0;
+      o.counters[3] = 0;
     }
   }
 }

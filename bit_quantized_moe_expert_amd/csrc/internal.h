@@ -26,8 +26,8 @@ struct RouteBufs {
   int32_t *grp_expert = nullptr;      // [max groups] compacted non-empty groups
   int32_t *grp_row0 = nullptr;
   int32_t *grp_rows = nullptr;
-  int32_t *counters = nullptr;        // [0] groups, [1] tiles
-  int4 *tiles = nullptr;              // [max tiles] (expert, row0, rows, 0)
+  int32_t *counters = nullptr;        // [0] groups, [1] tiles, [2] / [3] class 0 / 1 tiles
+  int4 *tiles = nullptr;              // [2][max tiles] (expert, row0, rows, group rows): by group, by class
 };
 
 hipError_t launch_quantize(int fmt, const float *w, int64_t rows, int64_t K, uint8_t *packed,

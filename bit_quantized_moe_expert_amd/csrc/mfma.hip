@@ -37,6 +37,7 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 constexpr int kBK = 64;
+constexpr int kCUs = 256;     // compute units: one 512-thread workgroup on each at a time
 constexpr int kApad = 72;     // bf16 per LDS row of A (64 + 8 padding)
 constexpr int kQrow = 144;    // bytes per LDS row of an e4m3-split A: two 64-byte planes, 2 scale bytes, pad
 
@@ -603,29 +604,63 @@ __global__ __launch_bounds__(512) void k_mfma(GemmArgs p, int ntn, int per) {
   constexpr int kQ8 = 2 * TR * kQrow + 2 * 256 * 144;  // A buffers + staged weight rows
   constexpr int kSmem = AM == 3 ? (kQ8 > kXch ? kQ8 : kXch) : kTabBytes + (AM == 2 ? 4 : 2) * TR * kApad * 2;
   __shared__ __attribute__((aligned(16))) uint8_t smem[kSmem];
-  // XCD-aware order: hardware XCD = blockIdx.x % 8; each XCD takes an equal
-  // contiguous run of the work, in one of two orders (results do not depend
-  // on it):
+  // XCD-aware order: hardware XCD = blockIdx.x % 8, and the XCDs take equal
+  // shares of the work, in one of two orders (results do not depend on it):
   //  - tile major, n-tile minor, over the tiles the device table holds (the
   //    grid is sized for the most tiles): the workgroups an XCD runs at once
   //    cover a few row tiles across all their weight tiles, so a row tile's
   //    activations, and a weight tile read by an expert's consecutive row
   //    tiles, are fetched into that XCD's L2 once (gate_up FETCH_SIZE -64 %
   //    at the OLMoE-shaped prefill; gpt-oss-shaped T = 2048 gate_up 716 ->
-  //    675 us, down 648 -> 577 us; Qwen3-shaped T = 512 gate_up 161 -> 132 us);
+  //    675 us, down 648 -> 577 us; Qwen3-shaped T = 512 gate_up 161 -> 132 us).
+  //    When the launch takes more than one round of workgroups, the items come
+  //    from the class-ordered table, longest tiles first (class 0: more than
+  //    64 rows, then 33-64, then at most 32): each XCD takes a contiguous run
+  //    of each class, the classes' remainders dealt round the XCDs so that no
+  //    XCD gets more than its share of the whole, and starts its long tiles
+  //    first, so the short ones fill the end of the launch (OLMoE-shaped
+  //    prefill -1.8 %, gpt-oss-shaped T = 2048 -6 %, Qwen3-shaped T = 128 /
+  //    512 -4 / -3 %);
   //  - n-tile major, tile minor over the whole grid, for the NF4 down
-  //    projections, which ran 3-10 % slower in tile-major order.
+  //    projections, which ran 3-10 % slower in tile-major order (the table's
+  //    class order puts long tiles first within each n-tile there too).
   constexpr bool kTileMajor = EPI == EPI_SWIGLU || FMT == 1;
   const int L = blockIdx.x;
-  int ti, nt;
+  int ti = -1, nt = 0;
+  bool by_class = false;
   if constexpr (kTileMajor) {
-    const int total = min(*p.n_tiles, p.max_tiles) * ntn;
-    const int per_xcd = (total + 7) >> 3;
-    if ((L >> 3) >= per_xcd) return;
-    const int Lp = (L & 7) * per_xcd + (L >> 3);
-    if (Lp >= total) return;
-    ti = Lp / ntn;
-    nt = Lp % ntn;
+    const int nall = min(*p.n_tiles, p.max_tiles);
+    if (nall * ntn <= kCUs) {  // one round: every tile starts at once, in group order
+      const int total = nall * ntn, per_xcd = (total + 7) >> 3;
+      const int Lp = (L & 7) * per_xcd + (L >> 3);
+      if ((L >> 3) >= per_xcd || Lp >= total) return;
+      ti = Lp / ntn;
+      nt = Lp % ntn;
+    } else {
+      by_class = true;
+      const int na = min(p.n_tiles[1], nall), nb = min(p.n_tiles[2], nall - na);
+      const int x = L & 7;
+      int j = L >> 3, o = 0, tbase = 0;
+      for (int cls = 0; cls < 3; ++cls) {
+        const int ncl = cls == 0 ? na : (cls == 1 ? nb : nall - na - nb);
+        const int items = ncl * ntn, q = items >> 3, r = items & 7;
+        int start = x * q, mine = q;
+        for (int y = 0; y < 8; ++y) {  // this class's remainders go to XCDs o, o + 1, ... (mod 8)
+          const int extra = ((y - o) & 7) < r ? 1 : 0;
+          if (y < x) start += extra;
+          if (y == x) mine += extra;
+        }
+        if (j < mine) {
+          ti = tbase + (start + j) / ntn;
+          nt = (start + j) % ntn;
+          break;
+        }
+        j -= mine;
+        o = (o + r) & 7;
+        tbase += ncl;
+      }
+      if (ti < 0) return;
+    }
   } else {
     const int Lp = (L & 7) * per + (L >> 3);
     if (Lp >= p.max_tiles * ntn) return;
@@ -633,7 +668,9 @@ __global__ __launch_bounds__(512) void k_mfma(GemmArgs p, int ntn, int per) {
     ti = Lp % p.max_tiles;
     if (ti >= *p.n_tiles) return;
   }
-  const int4 tile = p.tiles[ti];  // expert, row0, rows, rows of the whole group
+  // expert, row0, rows, rows of the whole group (from the class-ordered table
+  // when the launch runs in more than one round)
+  const int4 tile = p.tiles[(by_class ? p.max_tiles : 0) + ti];
   const int rows = __builtin_amdgcn_readfirstlane(tile.z);
   if constexpr (TR == 128) {
     if (rows > 64) {

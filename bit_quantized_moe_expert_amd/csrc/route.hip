@@ -514,29 +514,133 @@ __device__ inline int block_scan_1024(int v, int *total) {
   return ex;
 }
 
-// Tiles of at most bm rows for every group; single workgroup of 1024 threads.
+// Exclusive scan of a pair of 32-bit counts (low, high word) per thread
+// across a 1024-thread block; *total receives the block totals.
+__device__ inline uint64_t block_scan_1024_u64(uint64_t v, uint64_t *total) {
+  __shared__ uint64_t wsum[16];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint64_t inc = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const uint64_t o = __shfl_up(inc, d, kWave);
+    if (lane >= d) inc += o;
+  }
+  if (lane == 63) wsum[wave] = inc;
+  __syncthreads();
+  if (wave == 0) {
+    const uint64_t w = lane < 16 ? wsum[lane] : 0;
+    uint64_t wi = w;
+#pragma unroll
+    for (int d = 1; d < 16; d <<= 1) {
+      const uint64_t o = __shfl_up(wi, d, kWave);
+      if (lane >= d) wi += o;
+    }
+    if (lane < 16) wsum[lane] = wi - w;
+    if (lane == 15) *total = wi;
+  }
+  __syncthreads();
+  const uint64_t ex = wsum[wave] + inc - v;
+  __syncthreads();
+  return ex;
+}
+
+// The MFMA tile table comes in two orders, each of n_tiles entries:
+//  - tiles[0, max_tiles): by group, within a group by rows (the n-tile-major
+//    kernels and dgrad: consecutive tiles of an expert share its weights);
+//  - tiles[max_tiles, 2 max_tiles): by class, the body a tile runs (0: more
+//    than 64 rows, 1: 33 to 64, 2: at most 32), then as above, so that the
+//    tile-major kernels start their longest tiles first and the short ones
+//    fill the end of the launch instead of trailing alone.
+// counters[1] = tiles, [2] = class 0 tiles, [3] = class 1 tiles.
+__device__ inline int tile_class(int rows) { return rows > 64 ? 0 : (rows > 32 ? 1 : 2); }
+
+// tiles of each class in a group of `rows` rows cut into tiles of bm rows
+__device__ inline void group_tile_counts(int rows, int bm, int &c0, int &c1, int &c2) {
+  const int full = rows / bm, rem = rows - full * bm;
+  const int fc = tile_class(bm);
+  c0 = fc == 0 ? full : 0;
+  c1 = fc == 1 ? full : 0;
+  c2 = fc == 2 ? full : 0;
+  if (rem > 0) {
+    const int rc = tile_class(rem);
+    c0 += rc == 0;
+    c1 += rc == 1;
+    c2 += rc == 2;
+  }
+}
+
+// the tiles of one group: first at pe in group order, first of each class at
+// b0 / b1 / b2 in class order
+__device__ inline void write_group_tiles(int e, int row0, int rows, int bm, int pe, int b0, int b1, int b2,
+                                         int max_tiles, int4 *tiles) {
+  const int full = rows / bm, rem = rows - full * bm;
+  const int fc = tile_class(bm);
+  const int fb = fc == 0 ? b0 : (fc == 1 ? b1 : b2);
+  for (int i = 0; i < full; ++i) {
+    const int4 t = make_int4(e, row0 + i * bm, bm, rows);
+    if (pe + i < max_tiles) tiles[pe + i] = t;
+    if (fb + i < max_tiles) tiles[max_tiles + fb + i] = t;
+  }
+  if (rem > 0) {
+    const int4 t = make_int4(e, row0 + full * bm, rem, rows);
+    const int rc = tile_class(rem);
+    const int pos = (rc == 0 ? b0 : (rc == 1 ? b1 : b2)) + (rc == fc ? full : 0);
+    if (pe + full < max_tiles) tiles[pe + full] = t;
+    if (pos < max_tiles) tiles[max_tiles + pos] = t;
+  }
+}
+
+// Tiles of at most bm rows for every group, in both orders; single workgroup
+// of 1024 threads. n_tiles_out[0] = tiles, [1] / [2] = class 0 / 1 tiles.
 __device__ void build_tiles(const int32_t *grp_expert, const int32_t *grp_row0,
                             const int32_t *grp_rows, int n_grp, int bm, int max_tiles, int4 *tiles,
                             int32_t *n_tiles_out) {
-  __shared__ int s_total;
-  __shared__ int s_carry;
-  if (threadIdx.x == 0) s_carry = 0;
-  __syncthreads();
+  __shared__ uint64_t s_t01;
+  __shared__ int s_t2;
+  int T0 = 0, T1 = 0, T2 = 0;
+  if (n_grp > 1024) {  // class totals first: class 1 tiles start after every class 0 tile
+    int a0 = 0, a1 = 0, a2 = 0;
+    for (int g = threadIdx.x; g < n_grp; g += 1024) {
+      int c0, c1, c2;
+      group_tile_counts(grp_rows[g], bm, c0, c1, c2);
+      a0 += c0;
+      a1 += c1;
+      a2 += c2;
+    }
+    block_scan_1024_u64((uint64_t)a0 | ((uint64_t)a1 << 32), &s_t01);
+    block_scan_1024(a2, &s_t2);
+    T0 = (int)(s_t01 & 0xffffffffu);
+    T1 = (int)(s_t01 >> 32);
+    T2 = s_t2;
+  }
+  int k0 = 0, k1 = 0, k2 = 0;  // tiles of each class before this round of groups
   for (int g0 = 0; g0 < n_grp; g0 += 1024) {
     const int g = g0 + threadIdx.x;
     const int rows = g < n_grp ? grp_rows[g] : 0;
-    const int nt = (rows + bm - 1) / bm;
-    const int ex = block_scan_1024(nt, &s_total);
-    const int base = s_carry + ex;
-    for (int i = 0; i < nt && base + i < max_tiles; ++i) {
-      const int r0 = i * bm;
-      tiles[base + i] = make_int4(grp_expert[g], grp_row0[g] + r0, min(bm, rows - r0), rows);
+    int c0, c1, c2;
+    group_tile_counts(rows, bm, c0, c1, c2);
+    const uint64_t e01 = block_scan_1024_u64((uint64_t)c0 | ((uint64_t)c1 << 32), &s_t01);
+    const int e2 = block_scan_1024(c2, &s_t2);
+    const int t0 = (int)(s_t01 & 0xffffffffu), t1 = (int)(s_t01 >> 32), t2 = s_t2;
+    if (n_grp <= 1024) {  // one round: its totals are the table's
+      T0 = t0;
+      T1 = t1;
+      T2 = t2;
     }
-    __syncthreads();
-    if (threadIdx.x == 0) s_carry += s_total;
-    __syncthreads();
+    const int e0 = k0 + (int)(e01 & 0xffffffffu), e1 = k1 + (int)(e01 >> 32), ee2 = k2 + e2;
+    if (rows > 0)
+      write_group_tiles(grp_expert[g], grp_row0[g], rows, bm, e0 + e1 + ee2, e0, T0 + e1, T0 + T1 + ee2,
+                        max_tiles, tiles);
+    k0 += t0;
+    k1 += t1;
+    k2 += t2;
+    __syncthreads();  // every thread has read the totals before the next scans
   }
-  if (threadIdx.x == 0) *n_tiles_out = min(s_carry, max_tiles);
+  if (threadIdx.x == 0) {
+    n_tiles_out[0] = min(T0 + T1 + T2, max_tiles);
+    n_tiles_out[1] = T0;
+    n_tiles_out[2] = T1;
+  }
 }
 
 // Grouping, stage 2 (single workgroup): flat exclusive scan of the histogram,
@@ -672,7 +776,7 @@ __global__ __launch_bounds__(1024) void k_route_tail_small(LogitSrc L, int T, in
   __shared__ int cnt[kSmallE];
   __shared__ int offs[kSmallE];
   __shared__ int wcnt[16][kSmallE];  // per wave: slots routed to each expert
-  __shared__ int s_total;
+  __shared__ uint64_t s_total64;
   const int tid = threadIdx.x;
   const int R = T * k;
   for (int e = tid; e < E; e += 1024) cnt[e] = 0;
@@ -723,27 +827,36 @@ __global__ __launch_bounds__(1024) void k_route_tail_small(LogitSrc L, int T, in
   for (int i = tid; i < 16 * E; i += 1024) wcnt[i / E][i % E] = 0;
   __syncthreads();
   // One scan gives each expert its first sorted row (11 bits: R <= 1024), its
-  // slot in the non-empty expert list (9 bits: E <= 256) and its first tile
-  // (11 bits: at most R + E tiles).
+  // slot in the non-empty expert list (9 bits: E <= 256), and in the high
+  // word its first tile of each class (10 bits each: at most R / 33 + 16
+  // tiles of classes 0 and 1, and E of class 2).
   const int c = tid < E ? cnt[tid] : 0;
-  const int nt = (c + bm - 1) / bm;
-  const int ex = block_scan_1024(c | ((c > 0 ? 1 : 0) << 11) | (nt << 20), &s_total);
-  const int off = ex & 0x7ff, slot = (ex >> 11) & 0x1ff, tile0 = ex >> 20;
+  int c0, c1, c2;
+  group_tile_counts(c, bm, c0, c1, c2);
+  const uint64_t ex64 = block_scan_1024_u64(
+      (uint64_t)(c | ((c > 0 ? 1 : 0) << 11)) | ((uint64_t)(c0 | (c1 << 10) | (c2 << 20)) << 32), &s_total64);
+  const int ex = (int)(ex64 & 0xffffffffu), exc = (int)(ex64 >> 32);
+  const int tot = (int)(s_total64 & 0xffffffffu), totc = (int)(s_total64 >> 32);
+  const int off = ex & 0x7ff, slot = (ex >> 11) & 0x1ff;
+  const int n_grp = (tot >> 11) & 0x1ff;
+  const int T0 = totc & 0x3ff, T1 = (totc >> 10) & 0x3ff, T2 = totc >> 20;
   if (tid < E) {
     offs[tid] = off;
     o.expert_offsets[tid] = off;
   }
   if (tid == 0) {
     o.expert_offsets[E] = R;
-    o.counters[0] = (s_total >> 11) & 0x1ff;
-    o.counters[1] = min(s_total >> 20, max_tiles);
+    o.counters[0] = n_grp;
+    o.counters[1] = min(T0 + T1 + T2, max_tiles);
+    o.counters[2] = T0;
+    o.counters[3] = T1;
   }
   if (c > 0) {
     o.grp_expert[slot] = tid;
     o.grp_row0[slot] = off;
     o.grp_rows[slot] = c;
-    for (int i = 0; i < nt && tile0 + i < max_tiles; ++i)
-      o.tiles[tile0 + i] = make_int4(tid, off + i * bm, min(bm, c - i * bm), c);
+    const int e0 = exc & 0x3ff, e1 = (exc >> 10) & 0x3ff, e2 = exc >> 20;
+    write_group_tiles(tid, off, c, bm, e0 + e1 + e2, e0, T0 + e1, T0 + T1 + e2, max_tiles, o.tiles);
   }
   // Stable position of slot s among the slots routed to its expert: its rank
   // among equal ids in its wave (one ballot per id bit) plus the counts of
