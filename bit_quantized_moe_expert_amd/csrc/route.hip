@@ -751,15 +751,20 @@ __global__ __launch_bounds__(256) void k_group_scatter(const int32_t *__restrict
 }
 
 // ---------------------------------------------------------------------------
-// Routing in one workgroup of 1024 threads for up to 1024 routed slots and
-// E <= kSmallE experts. TOPK: the tokens' logits are copied to LDS when they
-// fit (T * E <= kSmallTE, else read from L2) and ranked by wave_topk (one
-// wave per token, as k_topk), weights included; otherwise the ids come from
-// topk_ids, written by k_topk before. Then one block scan gives the expert
-// offsets, the non-empty expert list and the MFMA tiles, and ballots the
-// stable ranks.
+// Routing in one workgroup of 1024 threads for up to kTailR routed slots and
+// E <= kSmallE experts. TOPK (up to 1024 slots): the tokens' logits are copied
+// to LDS when they fit (T * E <= kSmallTE, else read from L2) and ranked by
+// wave_topk (one wave per token, as k_topk), weights included; otherwise the
+// ids come from topk_ids, written by k_topk before. Then one block scan gives
+// the expert offsets, the non-empty expert list and the MFMA tiles, and
+// ballots give the stable ranks, 1024 slots per pass with the per-expert
+// counts of the earlier passes carried in LDS.
 // ---------------------------------------------------------------------------
-constexpr int kSmallR = 1024;   // routed slots: one per thread
+constexpr int kSmallR = 1024;   // routed slots ranked in one pass (one per thread)
+// Routed slots grouped by the one-workgroup tail; above it the three-launch
+// grouping. Measured against it: routing stage 32.1 -> 28.6 us at 2048 slots
+// (Qwen3-shaped T = 256), even at 4096, 5 us slower at 8192.
+constexpr int kTailR = 4096;
 constexpr int kSmallE = 256;
 constexpr int kSmallTE = 4096;  // bounds the LDS copy of the logits (else read from L2)
 // Up to this many tokens the one-workgroup kernel also ranks the experts;
@@ -770,12 +775,13 @@ constexpr int kTailTopkMaxT = 16;
 template <bool TOPK>
 __global__ __launch_bounds__(1024) void k_route_tail_small(LogitSrc L, int T, int E, int k, int renorm,
                                                            int bm, int max_tiles, RouteBufs o) {
+  constexpr int kR = TOPK ? kSmallR : kTailR;
   __shared__ __attribute__((aligned(16))) float Ls[TOPK ? kSmallTE : 4];
-  __shared__ int sel_id[kSmallR];
+  __shared__ int sel_id[kR];
   __shared__ float sel_w[TOPK ? kSmallR : 4];
   __shared__ int cnt[kSmallE];
-  __shared__ int offs[kSmallE];
-  __shared__ int wcnt[16][kSmallE];  // per wave: slots routed to each expert
+  __shared__ int offs[kSmallE];   // first sorted row of each expert, plus the earlier passes' slots
+  __shared__ int wcnt[16][kSmallE];  // per wave of a pass: slots routed to each expert
   __shared__ uint64_t s_total64;
   const int tid = threadIdx.x;
   const int R = T * k;
@@ -811,34 +817,35 @@ __global__ __launch_bounds__(1024) void k_route_tail_small(LogitSrc L, int T, in
     }
   }
   __syncthreads();
-  if (tid < R) {
-    int id;
-    if constexpr (TOPK) {
-      id = sel_id[tid];
-      o.topk_ids[tid] = id;
-      o.topk_w[tid] = sel_w[tid];
-    } else {
-      id = o.topk_ids[tid];  // from k_topk: always in [0, E)
-      sel_id[tid] = id;
+  for (int s0 = 0; s0 < R; s0 += 1024) {
+    const int sl = s0 + tid;
+    if (sl < R) {
+      int id;
+      if constexpr (TOPK) {
+        id = sel_id[sl];
+        o.topk_ids[sl] = id;
+        o.topk_w[sl] = sel_w[sl];
+      } else {
+        id = o.topk_ids[sl];  // from k_topk: always in [0, E)
+        sel_id[sl] = id;
+      }
+      atomicAdd(&cnt[id], 1);
     }
-    atomicAdd(&cnt[id], 1);
   }
-  // zero the per-wave expert counts of the stable ranking below
-  for (int i = tid; i < 16 * E; i += 1024) wcnt[i / E][i % E] = 0;
   __syncthreads();
-  // One scan gives each expert its first sorted row (11 bits: R <= 1024), its
-  // slot in the non-empty expert list (9 bits: E <= 256), and in the high
-  // word its first tile of each class (10 bits each: at most R / 33 + 16
-  // tiles of classes 0 and 1, and E of class 2).
+  // One scan gives each expert its first sorted row (14 bits: R <= kTailR) and
+  // its slot in the non-empty expert list (9 bits: E <= 256), and in the high
+  // word its first tile of each class (10 bits each: at most R / 65 + 64 tiles
+  // of class 0, R / 33 + 128 of class 1, E of class 2).
   const int c = tid < E ? cnt[tid] : 0;
   int c0, c1, c2;
   group_tile_counts(c, bm, c0, c1, c2);
   const uint64_t ex64 = block_scan_1024_u64(
-      (uint64_t)(c | ((c > 0 ? 1 : 0) << 11)) | ((uint64_t)(c0 | (c1 << 10) | (c2 << 20)) << 32), &s_total64);
+      (uint64_t)(c | ((c > 0 ? 1 : 0) << 14)) | ((uint64_t)(c0 | (c1 << 10) | (c2 << 20)) << 32), &s_total64);
   const int ex = (int)(ex64 & 0xffffffffu), exc = (int)(ex64 >> 32);
   const int tot = (int)(s_total64 & 0xffffffffu), totc = (int)(s_total64 >> 32);
-  const int off = ex & 0x7ff, slot = (ex >> 11) & 0x1ff;
-  const int n_grp = (tot >> 11) & 0x1ff;
+  const int off = ex & 0x3fff, slot = (ex >> 14) & 0x1ff;
+  const int n_grp = (tot >> 14) & 0x1ff;
   const int T0 = totc & 0x3ff, T1 = (totc >> 10) & 0x3ff, T2 = totc >> 20;
   if (tid < E) {
     offs[tid] = off;
@@ -858,26 +865,39 @@ __global__ __launch_bounds__(1024) void k_route_tail_small(LogitSrc L, int T, in
     const int e0 = exc & 0x3ff, e1 = (exc >> 10) & 0x3ff, e2 = exc >> 20;
     write_group_tiles(tid, off, c, bm, e0 + e1 + e2, e0, T0 + e1, T0 + T1 + e2, max_tiles, o.tiles);
   }
-  // Stable position of slot s among the slots routed to its expert: its rank
-  // among equal ids in its wave (one ballot per id bit) plus the counts of
-  // the earlier waves.
+  // Stable position of slot s among the slots routed to its expert: the
+  // expert's first row plus the slots of earlier passes (carried in offs),
+  // the counts of the earlier waves of this pass, and its rank among equal
+  // ids in its wave (one ballot per id bit).
   const int wave = tid >> 6;
-  const bool valid = tid < R;
-  const int e = valid ? sel_id[tid] : E;  // E: sentinel shared by the idle lanes
-  uint64_t m = ~0ull;
-  for (int bit = 0; bit < 9; ++bit) {
-    const int on = (e >> bit) & 1;
-    const uint64_t bal = __ballot(on);
-    m &= on ? bal : ~bal;
-  }
-  const int rank = __popcll(m & lanemask_lt());
-  if (valid && rank == 0) wcnt[wave][e] = __popcll(m);
-  __syncthreads();
-  if (valid) {
-    int pos = offs[e] + rank;
-    for (int w = 0; w < wave; ++w) pos += wcnt[w][e];
-    o.sorted_slots[pos] = tid;
-    o.slot_pos[tid] = pos;
+  for (int s0 = 0; s0 < R; s0 += 1024) {
+    for (int i = tid; i < 16 * E; i += 1024) wcnt[i / E][i % E] = 0;
+    __syncthreads();
+    const int sl = s0 + tid;
+    const bool valid = sl < R;
+    const int e = valid ? sel_id[sl] : E;  // E: sentinel shared by the idle lanes
+    uint64_t m = ~0ull;
+    for (int bit = 0; bit < 9; ++bit) {
+      const int on = (e >> bit) & 1;
+      const uint64_t bal = __ballot(on);
+      m &= on ? bal : ~bal;
+    }
+    const int rank = __popcll(m & lanemask_lt());
+    if (valid && rank == 0) wcnt[wave][e] = __popcll(m);
+    __syncthreads();
+    if (valid) {
+      int pos = offs[e] + rank;
+      for (int w = 0; w < wave; ++w) pos += wcnt[w][e];
+      o.sorted_slots[pos] = sl;
+      o.slot_pos[sl] = pos;
+    }
+    __syncthreads();
+    if (tid < E) {  // this pass's slots of each expert come before the next pass's
+      int n = 0;
+      for (int w = 0; w < 16; ++w) n += wcnt[w][tid];
+      offs[tid] += n;
+    }
+    __syncthreads();  // wcnt and offs are read before the next pass rewrites them
   }
 }
 
@@ -900,9 +920,9 @@ static hipError_t launch_topk(const LogitSrc &L, int T, int E, int k, int renorm
 static hipError_t launch_route_src(const LogitSrc &L, int T, int E, int k, int renorm, const RouteBufs &rb,
                                    int bm, hipStream_t s) {
   const int R = T * k;
-  const bool one_wg = E <= kSmallE && R <= kSmallR;
+  const bool one_wg = E <= kSmallE && R <= kTailR;
   const int max_tiles = (int)cdiv(R, bm) + (R < E ? R : E);
-  if (one_wg && T <= kTailTopkMaxT) {
+  if (one_wg && T <= kTailTopkMaxT && R <= kSmallR) {
     hipLaunchKernelGGL(k_route_tail_small<true>, dim3(1), dim3(1024), 0, s, L, T, E, k, renorm, bm,
                        max_tiles, rb);
     return hipGetLastError();
