@@ -38,9 +38,9 @@ __global__ __launch_bounds__(256) void k_logits_rows(const uint16_t *__restrict_
   for (int h = threadIdx.x * 8; h < H; h += 256 * 8) {
     const float4 w0 = *reinterpret_cast<const float4 *>(w + h);
     const float4 w1 = *reinterpret_cast<const float4 *>(w + h + 4);
-    // Tokens in batches of up to 8: the batch's loads (clamped to a valid row,
+    // Tokens in batches of up to 16: the batch's loads (clamped to a valid row,
     // no branch) are all issued before the first is used.
-    constexpr int BT = TMAX < 8 ? TMAX : 8;
+    constexpr int BT = TMAX < 16 ? TMAX : 16;
 #pragma unroll
     for (int t0 = 0; t0 < TMAX; t0 += BT) {
       if (t0 >= T) break;  // uniform
@@ -326,6 +326,8 @@ hipError_t launch_router_rows(const uint16_t *x, int T, int H, const float *W, c
     hipLaunchKernelGGL(k_logits_rows<4>, dim3(E), dim3(256), 0, s, x, T, H, W, b, E, logits);
   else if (T <= 8)
     hipLaunchKernelGGL(k_logits_rows<8>, dim3(E), dim3(256), 0, s, x, T, H, W, b, E, logits);
+  else if (T <= 16)
+    hipLaunchKernelGGL(k_logits_rows<16>, dim3(E), dim3(256), 0, s, x, T, H, W, b, E, logits);
   else
     hipLaunchKernelGGL(k_logits_rows<32>, dim3(E, (unsigned)cdiv(T, 32)), dim3(256), 0, s, x, T, H, W, b,
                        E, logits);
@@ -789,11 +791,16 @@ __global__ __launch_bounds__(1024) void k_route_tail_small(LogitSrc L, int T, in
   if constexpr (TOPK) {
     const int Ep = (E + 3) & ~3;  // LDS row stride: 16-byte rows, padded with -inf
     const bool in_lds = T * Ep <= kSmallTE;  // uniform
-    if (in_lds) {
-      for (int i = tid; i < T * Ep; i += 1024) {
-        const int t = i / Ep, f = i - t * Ep;
-        Ls[i] = f < E ? logit_at(L, (int64_t)t * E + f, f) : -__builtin_inff();
+    if (in_lds) {  // every load issued before the first LDS store
+      float v[kSmallTE / 1024];
+#pragma unroll
+      for (int r = 0; r < kSmallTE / 1024; ++r) {
+        const int i = tid + r * 1024, t = i / Ep, f = i - t * Ep;
+        v[r] = i < T * Ep && f < E ? logit_at(L, (int64_t)t * E + f, f) : -__builtin_inff();
       }
+#pragma unroll
+      for (int r = 0; r < kSmallTE / 1024; ++r)
+        if (tid + r * 1024 < T * Ep) Ls[tid + r * 1024] = v[r];
     }
     __syncthreads();
     // top k of each token: one wave per token (wave_topk), weights included
