@@ -194,6 +194,15 @@ __device__ inline float2 pair_gather(float cb_lane, uint32_t b) {
                   : make_float2(codebook_gather(cb_lane, b & 15), codebook_gather(cb_lane, b >> 4));
 }
 
+// g * sigmoid(a g) = g / (1 + exp(-a g)), with the hardware exp2 and
+// reciprocal (about 1 ulp each; the gate epilogues spent most of their
+// instructions on the full-precision exp and the IEEE division). Large
+// negative a g gives 1 / inf = 0, large positive 1 / 1; NaN stays NaN.
+__device__ inline float sig_gate(float g, float a) {
+  const float e = __builtin_amdgcn_exp2f(g * (-1.44269504088896341f * a));
+  return g * __builtin_amdgcn_rcpf(1.0f + e);
+}
+
 // Gate_up epilogue: glu 0 is SwiGLU, silu(g) * u; glu 1 the clamped GLU,
 // (u' + 1) * g' / (1 + exp(-alpha g')) with g' = min(g, limit) and
 // u' = clamp(u, -limit, limit).
@@ -201,9 +210,9 @@ __device__ inline float glu_value(int glu, float alpha, float limit, float g, fl
   if (glu == 1) {
     g = fminf(g, limit);
     u = fminf(fmaxf(u, -limit), limit);
-    return (u + 1.0f) * (g / (1.0f + expf(-alpha * g)));
+    return (u + 1.0f) * sig_gate(g, alpha);
   }
-  return g / (1.0f + expf(-g)) * u;
+  return sig_gate(g, 1.0f) * u;
 }
 
 // Barrier that orders LDS only: global loads (and stores) issued before it

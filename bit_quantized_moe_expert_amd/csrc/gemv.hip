@@ -503,7 +503,7 @@ __global__ __launch_bounds__(gemv_waves<ROUTE>() * 64) void k_gemv(GemmArgs p) {
             }
             hval = glu_value(p.glu, p.glu_alpha, p.glu_limit, gv, uv);
           } else {
-            hval = v0 / (1.0f + expf(-v0)) * v1;
+            hval = sig_gate(v0, 1.0f) * v1;
           }
           reinterpret_cast<float *>(p.c)[r * ncol + col] = hval;
         } else if (EPI == EPI_PLAIN_F32) {

@@ -548,8 +548,7 @@ __device__ __forceinline__ void mfma_tile(const GemmArgs &p, uint8_t *smem, int 
         if constexpr (XF) {
           h = glu_value(p.glu, p.glu_alpha, p.glu_limit, C[mb][v] + bg, up + bu);
         } else {
-          const float gt = C[mb][v];
-          h = gt / (1.0f + expf(-gt)) * up;
+          h = sig_gate(C[mb][v], 1.0f) * up;
         }
         const int64_t o = (int64_t)(trow0 + m) * ncol + col;
         if (p.c_split) {  // (truncated bf16 hi, RNE bf16 of the rest) in one word
