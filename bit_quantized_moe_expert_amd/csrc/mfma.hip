@@ -537,25 +537,33 @@ __device__ __forceinline__ void mfma_tile(const GemmArgs &p, uint8_t *smem, int 
       bg = bb[nrow];
       bu = bb[p.glu_inter ? nrow + 1 : nrow + ncol];
     }
+    // values v and v + 1 of a lane are rows m and m + 1 of its column: their
+    // lo parts share one conversion instruction
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
+      for (int v = 0; v < 16; v += 2) {
         const int m = mb * 32 + 8 * (v >> 2) + 4 * g + (v & 3);
-        const float up = xch[((w4 * MB + mb) * 16 + v) * 64 + lane];
-        if (m >= trows || !nvalid) continue;
-        float h;
-        if constexpr (XF) {
-          h = glu_value(p.glu, p.glu_alpha, p.glu_limit, C[mb][v] + bg, up + bu);
-        } else {
-          h = sig_gate(C[mb][v], 1.0f) * up;
+        float h[2];
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {  // rows past the tile compute unused values
+          const float up = xch[((w4 * MB + mb) * 16 + v + q) * 64 + lane];
+          if constexpr (XF)
+            h[q] = glu_value(p.glu, p.glu_alpha, p.glu_limit, C[mb][v + q] + bg, up + bu);
+          else
+            h[q] = sig_gate(C[mb][v + q], 1.0f) * up;
         }
+        if (!nvalid) continue;
         const int64_t o = (int64_t)(trow0 + m) * ncol + col;
         if (p.c_split) {  // (truncated bf16 hi, RNE bf16 of the rest) in one word
-          const uint32_t hi = __float_as_uint(h) & 0xffff0000u;
-          reinterpret_cast<uint32_t *>(p.c)[o] = (hi >> 16) | (f32_to_bf16_rne(h - __uint_as_float(hi)) << 16);
+          const uint32_t b0 = __float_as_uint(h[0]), b1 = __float_as_uint(h[1]);
+          const uint32_t lo = f32x2_to_bf16x2_rne(h[0] - __uint_as_float(b0 & 0xffff0000u),
+                                                  h[1] - __uint_as_float(b1 & 0xffff0000u));
+          if (m < trows) reinterpret_cast<uint32_t *>(p.c)[o] = __builtin_amdgcn_perm(lo, b0, 0x05040302u);
+          if (m + 1 < trows) reinterpret_cast<uint32_t *>(p.c)[o + ncol] = __builtin_amdgcn_perm(lo, b1, 0x07060302u);
         } else {
-          reinterpret_cast<float *>(p.c)[o] = h;
+          if (m < trows) reinterpret_cast<float *>(p.c)[o] = h[0];
+          if (m + 1 < trows) reinterpret_cast<float *>(p.c)[o + ncol] = h[1];
         }
       }
     }
