@@ -569,6 +569,19 @@ __device__ __forceinline__ void mfma_tile(const GemmArgs &p, uint8_t *smem, int 
     }
     return;
   }
+  // slot epilogue: each row's slot and routing weight, loaded once per tile
+  // into LDS (free since the last K-step's closing barrier) instead of two
+  // dependent global loads per row in every lane
+  int *s_slot = reinterpret_cast<int *>(smem);
+  float *s_w = reinterpret_cast<float *>(smem) + kBM;
+  if constexpr (EPI == EPI_SLOT) {
+    if (tid < trows) {
+      const int sl = p.slot_of[trow0 + tid];
+      s_slot[tid] = sl;
+      s_w[tid] = p.slot_w[sl];
+    }
+    lds_barrier();
+  }
   if (!nvalid) return;
   const float yb = (XF && EPI == EPI_SLOT && p.bias) ? p.bias[(int64_t)e * N + col] : 0.0f;
 #pragma unroll
@@ -584,8 +597,8 @@ __device__ __forceinline__ void mfma_tile(const GemmArgs &p, uint8_t *smem, int 
       } else if (EPI == EPI_PLAIN_BF16) {
         reinterpret_cast<uint16_t *>(p.c)[r * N + col] = (uint16_t)f32_to_bf16_rne(y);
       } else {
-        const int64_t slot = p.slot_of[r];
-        reinterpret_cast<float *>(p.c)[slot * N + col] = p.slot_w[slot] * (XF ? y + yb : y);
+        const int64_t slot = s_slot[m];
+        reinterpret_cast<float *>(p.c)[slot * N + col] = s_w[m] * (XF ? y + yb : y);
       }
     }
   }
