@@ -94,6 +94,15 @@ __device__ __forceinline__ void mfma_tile(const GemmArgs &p, uint8_t *smem, int 
   constexpr bool AQ8 = AM == 3;                       // A as e4m3 planes: block-scaled MFMAs, no decode
   constexpr int kBM = 32 * MB;                        // rows per tile
   constexpr int ABUF = AQ8 ? kBM * kQrow : kBM * kApad * 2;  // bytes per A buffer
+  // Row-split SwiGLU layout of the block-scaled MXFP4 gate_up (tiles of more
+  // than 32 rows): wave w takes row blocks (w & 1) * MH .. + MH against the
+  // gate and the up rows of output columns 32 (w >> 1) .. + 32, so each wave
+  // reads half the A tile from LDS (two e4m3 planes: 4 KB per row block and
+  // step, against 1 KB of codes per weight block) and forms SwiGLU in its own
+  // registers. The NF4 bodies keep all rows per wave: there a weight block's
+  // LDS lookups cost twice its A fragment, so the split would move no bytes.
+  constexpr bool RS = AQ8 && EPI == EPI_SWIGLU && MB >= 2;
+  constexpr int MH = MB / 2 > 0 ? MB / 2 : 1;
 
   if constexpr (!AQ8) build_mfma_table<FMT>(reinterpret_cast<uint4 *>(smem));
   auto abuf = [&](int hi_lo, int buf) __attribute__((always_inline)) -> uint16_t * {
@@ -121,6 +130,7 @@ __device__ __forceinline__ void mfma_tile(const GemmArgs &p, uint8_t *smem, int 
   }
   const bool nvalid = col < ncol;
   const int64_t nrow_c = nvalid ? nrow : 0;
+  const int rs_rh = wave & 1, rs_cg = wave >> 1;      // RS: row half, output column block
 
   const int64_t rowbytes = K / 2;
   const uint8_t *Be = p.B + (int64_t)e * N * rowbytes;
@@ -444,11 +454,39 @@ __device__ __forceinline__ void mfma_tile(const GemmArgs &p, uint8_t *smem, int 
       // row l32 of each 32-row block, k = 16 g + 0..15 and 32 + 16 g + 0..15
       // of each plane, and the row's scale for block g. C += A1 * B + A2 * B
       // with both operands' block scales applied.
+      const uint8_t *A8 = reinterpret_cast<const uint8_t *>(abuf(0, cur));
+      if constexpr (RS) {
+        // half the tile's rows (row blocks rh * MH ..) against the gate and
+        // the up rows of the wave's 32 output columns (staged rows cg * 32
+        // and (cg + 4) * 32 onwards): C[0, MH) gate, C[MH, MB) up
+        const uint8_t *bb = Bs + (j & 1) * 256 * kBrow;
+        const uint8_t *brg = bb + (rs_cg * 32 + l32) * kBrow;
+        const uint8_t *bru = bb + ((rs_cg + 4) * 32 + l32) * kBrow;
+        const uint4 qg = *reinterpret_cast<const uint4 *>(brg + 32 * s + 16 * g);
+        const uint4 qu = *reinterpret_cast<const uint4 *>(bru + 32 * s + 16 * g);
+        const int sbg = brg[128 + 2 * s + g], sbu = bru[128 + 2 * s + g];
+        const i32x8_t bvg = {(int)qg.x, (int)qg.y, (int)qg.z, (int)qg.w, 0, 0, 0, 0};
+        const i32x8_t bvu = {(int)qu.x, (int)qu.y, (int)qu.z, (int)qu.w, 0, 0, 0, 0};
+#pragma unroll
+        for (int mh = 0; mh < MH; ++mh) {
+          const uint8_t *row = A8 + ((rs_rh * MH + mh) * 32 + l32) * kQrow;
+          const uint4 p0 = *reinterpret_cast<const uint4 *>(row + 16 * g);
+          const uint4 p1 = *reinterpret_cast<const uint4 *>(row + 32 + 16 * g);
+          const uint4 q0 = *reinterpret_cast<const uint4 *>(row + 64 + 16 * g);
+          const uint4 q1 = *reinterpret_cast<const uint4 *>(row + 96 + 16 * g);
+          const int sa = row[128 + g];
+          const i32x8_t a1 = {(int)p0.x, (int)p0.y, (int)p0.z, (int)p0.w, (int)p1.x, (int)p1.y, (int)p1.z, (int)p1.w};
+          const i32x8_t a2 = {(int)q0.x, (int)q0.y, (int)q0.z, (int)q0.w, (int)q1.x, (int)q1.y, (int)q1.z, (int)q1.w};
+          C[mh] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a1, bvg, C[mh], 0, 4, 0, sa, 0, sbg);
+          C[MH + mh] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a1, bvu, C[MH + mh], 0, 4, 0, sa, 0, sbu);
+          C[mh] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a2, bvg, C[mh], 0, 4, 0, sa, 0, sbg);
+          C[MH + mh] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a2, bvu, C[MH + mh], 0, 4, 0, sa, 0, sbu);
+        }
+      } else {
       const uint8_t *brow = Bs + (j & 1) * 256 * kBrow + (wave * 32 + l32) * kBrow;
       const uint4 bq = *reinterpret_cast<const uint4 *>(brow + 32 * s + 16 * g);
       const int sb = brow[128 + 2 * s + g];
       const i32x8_t bv = {(int)bq.x, (int)bq.y, (int)bq.z, (int)bq.w, 0, 0, 0, 0};
-      const uint8_t *A8 = reinterpret_cast<const uint8_t *>(abuf(0, cur));
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
         const uint8_t *row = A8 + (mb * 32 + l32) * kQrow;
@@ -461,6 +499,7 @@ __device__ __forceinline__ void mfma_tile(const GemmArgs &p, uint8_t *smem, int 
         const i32x8_t a2 = {(int)q0.x, (int)q0.y, (int)q0.z, (int)q0.w, (int)q1.x, (int)q1.y, (int)q1.z, (int)q1.w};
         C[mb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a1, bv, C[mb], 0, 4, 0, sa, 0, sb);
         C[mb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a2, bv, C[mb], 0, 4, 0, sa, 0, sb);
+      }
       }
       __builtin_amdgcn_sched_barrier(0);
       store_a(cur ^ 1, (set + 1) & 3);
@@ -518,6 +557,47 @@ __device__ __forceinline__ void mfma_tile(const GemmArgs &p, uint8_t *smem, int 
 
   // ---- epilogue. 32x32 accumulator: lane holds column l32, rows
   // 8 * (v / 4) + 4 * g + (v % 4) for v = 0..15 of each 32-row block mb.
+  // (truncated bf16 hi, RNE bf16 of the rest) of h values of rows m, m + 1 in
+  // one word each; their lo parts share one conversion instruction
+  auto store_h_pair = [&](int64_t o, int m, const float *h) __attribute__((always_inline)) {
+    if (p.c_split) {
+      const uint32_t b0 = __float_as_uint(h[0]), b1 = __float_as_uint(h[1]);
+      const uint32_t lo = f32x2_to_bf16x2_rne(h[0] - __uint_as_float(b0 & 0xffff0000u),
+                                              h[1] - __uint_as_float(b1 & 0xffff0000u));
+      if (m < trows) reinterpret_cast<uint32_t *>(p.c)[o] = __builtin_amdgcn_perm(lo, b0, 0x05040302u);
+      if (m + 1 < trows) reinterpret_cast<uint32_t *>(p.c)[o + ncol] = __builtin_amdgcn_perm(lo, b1, 0x07060302u);
+    } else {
+      if (m < trows) reinterpret_cast<float *>(p.c)[o] = h[0];
+      if (m + 1 < trows) reinterpret_cast<float *>(p.c)[o + ncol] = h[1];
+    }
+  };
+  if constexpr (RS) {  // gate in C[0, MH), up in C[MH, MB), both in this wave
+    const int64_t rcol = (int64_t)nt * 128 + 32 * rs_cg + l32;
+    if (rcol >= ncol) return;
+    float bg = 0.0f, bu = 0.0f;
+    if (XF && p.bias) {
+      const float *bb = p.bias + (int64_t)e * N;
+      bg = bb[p.glu_inter ? 2 * rcol : rcol];
+      bu = bb[p.glu_inter ? 2 * rcol + 1 : rcol + ncol];
+    }
+#pragma unroll
+    for (int mh = 0; mh < MH; ++mh) {
+#pragma unroll
+      for (int v = 0; v < 16; v += 2) {
+        const int m = (rs_rh * MH + mh) * 32 + 8 * (v >> 2) + 4 * g + (v & 3);
+        float h[2];
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {  // rows past the tile compute unused values
+          if constexpr (XF)
+            h[q] = glu_value(p.glu, p.glu_alpha, p.glu_limit, C[mh][v + q] + bg, C[MH + mh][v + q] + bu);
+          else
+            h[q] = sig_gate(C[mh][v + q], 1.0f) * C[MH + mh][v + q];
+        }
+        store_h_pair((int64_t)(trow0 + m) * ncol + rcol, m, h);
+      }
+    }
+    return;
+  }
   if (EPI == EPI_SWIGLU) {
     // up waves hand their values to the gate waves through LDS (the table
     // region: every lookup finished before the last step's barrier)
@@ -554,17 +634,7 @@ __device__ __forceinline__ void mfma_tile(const GemmArgs &p, uint8_t *smem, int 
             h[q] = sig_gate(C[mb][v + q], 1.0f) * up;
         }
         if (!nvalid) continue;
-        const int64_t o = (int64_t)(trow0 + m) * ncol + col;
-        if (p.c_split) {  // (truncated bf16 hi, RNE bf16 of the rest) in one word
-          const uint32_t b0 = __float_as_uint(h[0]), b1 = __float_as_uint(h[1]);
-          const uint32_t lo = f32x2_to_bf16x2_rne(h[0] - __uint_as_float(b0 & 0xffff0000u),
-                                                  h[1] - __uint_as_float(b1 & 0xffff0000u));
-          if (m < trows) reinterpret_cast<uint32_t *>(p.c)[o] = __builtin_amdgcn_perm(lo, b0, 0x05040302u);
-          if (m + 1 < trows) reinterpret_cast<uint32_t *>(p.c)[o + ncol] = __builtin_amdgcn_perm(lo, b1, 0x07060302u);
-        } else {
-          if (m < trows) reinterpret_cast<float *>(p.c)[o] = h[0];
-          if (m + 1 < trows) reinterpret_cast<float *>(p.c)[o + ncol] = h[1];
-        }
+        store_h_pair((int64_t)(trow0 + m) * ncol + col, m, h);
       }
     }
     return;
