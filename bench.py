@@ -480,6 +480,32 @@ def fresh_process_reps(n, steps, warmup):
     return reps
 
 
+def mfma_ceiling(dev, workgroups=2048, iters=1024, launches=5):
+    """Measured bf16 matrix-core rate under full load (nf4moe_mfma_peak: every
+    wave back-to-back MFMAs on random finite register operands, no memory
+    traffic): the median of `launches` event-timed launches after one untimed."""
+    import numpy as np
+    import torch
+    import bit_quantized_moe_expert_amd as M
+    sink = torch.empty(workgroups * 512, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    M.mfma_peak(workgroups, iters, sink)
+    times, flops = [], 0
+    for _ in range(launches):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        flops = M.mfma_peak(workgroups, iters, sink)
+        b.record(stream)
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b))
+    ms = float(np.median(times))
+    tf = flops / (ms * 1e-3) / 1e12
+    del sink
+    return {"bf16_TFLOPs": tf, "frac_of_spec": tf / BF16_PEAK_TFLOPS, "ms": ms, "flops_per_launch": flops,
+            "launch": f"{workgroups} workgroups x 8 waves x {iters} rounds of 8 v_mfma_f32_32x32x16_bf16, "
+                      "random finite bf16 register operands, median of 5"}
+
+
 def stream_ceiling(dev, sizes, launches=32, shapes=(2, 4, 8, 16)):
     """Measured single-launch HBM read rate (nf4moe_stream_read) at given byte
     counts, the fastest of several launch shapes (16-byte loads per thread):
@@ -580,6 +606,14 @@ def main():
                               "H": pwl.H, "I": pwl.I, "T": pT, "layers": pl},
                    "value": pres["tokens_per_s"], "unit": "tokens/s", "dtype": "bf16 (split operands), fp32 acc",
                    **pres}
+        ceil = mfma_ceiling(dev)
+        print(f"[bench] mfma ceiling {json.dumps(ceil)}", file=sys.stderr, flush=True)
+        prefill["mfma_ceiling"] = ceil
+        # the gate_up kernel's MFMA work (two bf16 products per useful one: B as
+        # hi + lo) and its useful flops, each against the measured ceiling
+        prefill["roofline"]["frac_of_measured_ceiling"] = prefill["roofline"]["achieved"] / ceil["bf16_TFLOPs"]
+        prefill["roofline"]["mfma_work_frac_of_measured_ceiling"] = (2.0 * prefill["roofline"]["achieved"]
+                                                                    / ceil["bf16_TFLOPs"])
 
     if reps is not None and res["timing"]["mode"] == "hip_graph":
         # the pages' discipline: the same measurement in several fresh processes,

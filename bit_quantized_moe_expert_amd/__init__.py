@@ -85,6 +85,8 @@ def lib() -> ctypes.CDLL:
         "nf4moe_auto_path": [ctypes.c_int, i64, i64],
         "nf4moe_stream_read_sink_words": [i64, i32],
         "nf4moe_stream_read": [vp, i64, i32, vp, vp],
+        "nf4moe_mfma_peak_flops": [i32, i32],
+        "nf4moe_mfma_peak": [i32, i32, vp, vp],
         "nf4moe_status_string": [ctypes.c_int],
         "nf4moe_last_error": [],
         "nf4moe_version": [],
@@ -97,6 +99,7 @@ def lib() -> ctypes.CDLL:
                  "nf4moe_router_workspace_bytes"):
         getattr(L, name).restype = ctypes.c_size_t
     L.nf4moe_stream_read_sink_words.restype = ctypes.c_int64
+    L.nf4moe_mfma_peak_flops.restype = ctypes.c_int64
     for name in ("nf4moe_status_string", "nf4moe_last_error", "nf4moe_version"):
         getattr(L, name).restype = ctypes.c_char_p
     _lib = L
@@ -191,6 +194,18 @@ def stream_read(buf, nbytes: int, sink, loads_per_thread: int = 4):
 
 def stream_read_sink_words(nbytes: int, loads_per_thread: int = 4) -> int:
     return int(lib().nf4moe_stream_read_sink_words(nbytes, loads_per_thread))
+
+
+def mfma_peak(workgroups: int, iters: int, sink) -> int:
+    """Launch the bf16 matrix-core rate probe (a measurement aid) on the current
+    stream; sink: float32 device tensor of at least workgroups * 512 elements.
+    Returns the launch's flops."""
+    torch = _torch()
+    _dev(sink, "sink", torch.float32)
+    if sink.numel() < workgroups * 512:
+        raise ValueError(f"sink holds {sink.numel()} floats, needs {workgroups * 512}")
+    _check(lib().nf4moe_mfma_peak(workgroups, iters, _ptr(sink), _stream()))
+    return int(lib().nf4moe_mfma_peak_flops(workgroups, iters))
 
 
 def quantize(w, fmt: int = FMT_NF4):

@@ -11,6 +11,7 @@
 #include "common.h"
 #include "dgrad.h"
 #include "internal.h"
+#include "probe.h"
 
 using namespace nf4moe;
 
@@ -678,6 +679,19 @@ nf4moe_status_t nf4moe_stream_read(const void *buf, int64_t bytes, int32_t loads
   if (!buf || !sink) return fail(NF4MOE_ERR_INVALID_ARG, "NULL pointer");
   if (!aligned(buf, 16) || !aligned(sink, 4)) return fail(NF4MOE_ERR_INVALID_ARG, "misaligned pointer");
   return hip_status(launch_stream_read(buf, bytes, loads_per_thread, sink, (hipStream_t)stream), "stream read launch");
+}
+
+int64_t nf4moe_mfma_peak_flops(int32_t workgroups, int32_t iters) {
+  return workgroups > 0 && iters > 0 && workgroups <= (1 << 20) ? mfma_peak_flops(workgroups, iters) : 0;
+}
+
+nf4moe_status_t nf4moe_mfma_peak(int32_t workgroups, int32_t iters, float *sink, void *stream) {
+  if (workgroups <= 0 || workgroups > (1 << 20))
+    return fail(NF4MOE_ERR_INVALID_ARG, "workgroups=%d outside 1..%d", workgroups, 1 << 20);
+  if (iters <= 0) return fail(NF4MOE_ERR_INVALID_ARG, "iters=%d must be positive", iters);
+  if (!sink) return fail(NF4MOE_ERR_INVALID_ARG, "NULL sink");
+  if (!aligned(sink, 4)) return fail(NF4MOE_ERR_INVALID_ARG, "misaligned sink");
+  return hip_status(launch_mfma_peak(workgroups, iters, sink, (hipStream_t)stream), "mfma peak launch");
 }
 
 }  // extern "C"

@@ -343,6 +343,19 @@ int64_t nf4moe_stream_read_sink_words(int64_t bytes, int32_t loads_per_thread);
 nf4moe_status_t nf4moe_stream_read(const void *buf, int64_t bytes, int32_t loads_per_thread, uint32_t *sink,
                                    void *stream);
 
+/* nf4moe_mfma_peak -- a measurement aid, not part of the layer: one launch of
+ * `workgroups` 512-thread workgroups in which every wave runs `iters` rounds of
+ * 8 independent bf16 MFMAs (32x32x16) on pseudo-random finite register
+ * operands, with no memory traffic; each thread writes one float to sink
+ * (device, workgroups * 512 floats). nf4moe_mfma_peak_flops(workgroups,
+ * iters) gives the launch's flops (0 for invalid arguments); flops over the
+ * launch's duration is the bf16 matrix-core rate the GPU sustains under full
+ * load, the measured ceiling beside the published dense peak. Errors:
+ * INVALID_ARG for workgroups outside 1..2^20, iters <= 0, a NULL or misaligned
+ * sink. */
+int64_t nf4moe_mfma_peak_flops(int32_t workgroups, int32_t iters);
+nf4moe_status_t nf4moe_mfma_peak(int32_t workgroups, int32_t iters, float *sink, void *stream);
+
 /* nf4moe_codebook -- host copy of the 16 fp32 decode values the kernels use for
  * `fmt` (index = 4-bit code). No device access. Returns INVALID_ARG for a bad fmt
  * or NULL out. */

@@ -234,6 +234,17 @@ def test_binding_refuses_mismatched_shapes():
         pkg.router_logits(x, torch.zeros(E, H + 64))
 
 
+def test_mfma_peak_validation():
+    assert L.nf4moe_mfma_peak_flops(2, 3) == 2 * 8 * 3 * 8 * 2 * 32 * 32 * 16
+    assert L.nf4moe_mfma_peak_flops(0, 3) == 0
+    assert L.nf4moe_mfma_peak_flops(2, 0) == 0
+    assert L.nf4moe_mfma_peak(0, 4, FAKE, STREAM) == INVALID
+    assert L.nf4moe_mfma_peak((1 << 20) + 1, 4, FAKE, STREAM) == INVALID
+    assert L.nf4moe_mfma_peak(4, 0, FAKE, STREAM) == INVALID
+    assert L.nf4moe_mfma_peak(4, 4, None, STREAM) == INVALID
+    assert L.nf4moe_mfma_peak(4, 4, FAKE + 2, STREAM) == INVALID
+
+
 def test_stream_read_validation():
     assert L.nf4moe_stream_read_sink_words(16 * 1024, 4) == 1
     assert L.nf4moe_stream_read_sink_words(16 * 1024, 1) == 4
