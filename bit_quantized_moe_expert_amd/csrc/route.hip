@@ -230,14 +230,19 @@ hipError_t launch_router_partials(const uint16_t *x, int T, int H, const float *
                                   hipStream_t s) {
   if (T <= 0) return hipSuccess;
   const int S = router_split(H), chunk = router_chunk(H);
-  // 128 tokens per wave from 1024 tokens on (each weight split and read once
-  // per 128 tokens; gpt-oss-shaped T = 2048: 27.5 against 38 us), 32 below
-  // (more waves for the latency-bound smaller calls; Qwen3-shaped T = 256 /
-  // 512: 9 us less routing than with 128). A row's arithmetic is the same
-  // either way.
-  if (T >= 1024) {
-    const int64_t units = cdiv(T, 128) * (int64_t)S * cdiv(E, 32);
-    hipLaunchKernelGGL((k_logits_ks<4, 4>), dim3((unsigned)cdiv(units, 4)), dim3(256), 0, s, x, T, H, W, E,
+  // 128 or 64 tokens per wave from 1024 tokens on (each weight split and read
+  // once per 128 or 64 tokens; gpt-oss-shaped T = 2048: 27.5 against 38 us
+  // with 32), the taller wave while it still gives a workgroup per CU, 32
+  // below (more waves for the latency-bound smaller calls; Qwen3-shaped
+  // T = 256 / 512: 9 us less routing than with 128). A row's arithmetic is the
+  // same either way.
+  const int64_t per128 = cdiv(T, 128) * (int64_t)S * cdiv(E, 32);
+  if (T >= 1024 && cdiv(per128, 4) >= 256) {
+    hipLaunchKernelGGL((k_logits_ks<4, 4>), dim3((unsigned)cdiv(per128, 4)), dim3(256), 0, s, x, T, H, W, E,
+                       chunk, S, P);
+  } else if (T >= 1024) {
+    const int64_t units = cdiv(T, 64) * (int64_t)S * cdiv(E, 32);
+    hipLaunchKernelGGL((k_logits_ks<2, 4>), dim3((unsigned)cdiv(units, 4)), dim3(256), 0, s, x, T, H, W, E,
                        chunk, S, P);
   } else {
     const int64_t units = cdiv(T, 32) * (int64_t)S * cdiv(E, 32);
