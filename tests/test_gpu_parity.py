@@ -333,6 +333,24 @@ def test_forward_small_shapes(wl, T, path):
     _forward_case(wl, T, path)
 
 
+# Wide routing through the whole forward: more experts than the one-workgroup
+# grouping takes (E = 300 > 256: the three-launch grouping at every T) with a
+# large top-k (20), and the largest top-k (32) over 64 experts (the one-token
+# routing inside the gate_up kernel at T = 1, more slots per token than the
+# token-centric down takes). T = 333 gives 6,660 and 10,656 routed rows.
+WIDE = [
+    S.custom(E=300, top_k=20, H=256, I=128, wid=25),
+    S.custom(E=64, top_k=32, H=256, I=192, zipf_s=1.2, wid=26),
+]
+
+
+@pytest.mark.parametrize("wl", WIDE, ids=lambda w: w.name)
+@pytest.mark.parametrize("T", [1, 3, 17, 333])
+@pytest.mark.parametrize("path", [M.PATH_AUTO, M.PATH_SMALL_M, M.PATH_MFMA])
+def test_forward_wide_routing(wl, T, path):
+    _forward_case(wl, T, path)
+
+
 # The gpt-oss expert form: clamped GLU (a small limit, so the clamps act),
 # per-expert biases, halves or interleaved gate / up rows.
 GPTOSS_SMALL = [
