@@ -111,11 +111,16 @@ constexpr int gemv_loads() {
 }
 // One token (ROUTE > 0): at most 4, so the few routed experts' rows spread
 // over twice the workgroups (C1: 512 of 8 waves, 2 per CU; against 8 wave-
-// loads, the gate_up kernel 9.25 -> 8.86 us).
+// loads, the gate_up kernel 9.25 -> 8.86 us). Rows of two chunks per lane
+// (2048 < K <= 4096) take 6 rows per wave: a gpt-oss-shaped token's 4 x 5760
+// gate_up rows at 4 rows per wave need 5760 waves, more than the 4096 that
+// are resident at once, so the launch ran in 1.4 rounds; at 6 it is 480
+// workgroups, one round (the chunk-major loop below keeps the registers under
+// the 128 that 16 waves per CU allow).
 template <int LPR, int NJ, int MS, int ROUTE>
 constexpr int gemv_wave_loads() {
   constexpr int n = gemv_loads<LPR, NJ, MS>();
-  return ROUTE > 0 && n > 4 ? 4 : n;
+  return ROUTE > 0 ? (NJ == 2 && MS == 1 ? 6 : (n > 4 ? 4 : n)) : n;
 }
 
 // Routing of a single token inside the gate_up kernel, spread over the
@@ -447,14 +452,48 @@ __global__ __launch_bounds__(gemv_waves<ROUTE>() * 64) void k_gemv(GemmArgs p) {
   const char *tab = reinterpret_cast<const char *>(tab_all);
   const uint32_t lanebyte = (uint32_t)(lane & (kGemvRep - 1)) * 8u;
   const int my_m = lane / UPW, my_u = lane % UPW;
+  // One token with two chunks per lane: chunk-major, each chunk's activations
+  // converted to fp32 just before its rows use them, so only one chunk is held
+  // as fp32 (a row's arithmetic and order are those of the loop below: per
+  // chunk j ascending, acc = fma(scale, dot, acc) from 0).
+  constexpr bool kChunkMajor = ROUTE > 0 && NJ == 2 && MS == 1 && !AF32;
   for (int m0 = 0; m0 < rows; m0 += MS) {
-    if (m0 > 0) {
-      issue_x(m0);
-      convert_x();
-    } else if constexpr (MS == 1) {
-      convert_x();
+    if constexpr (!kChunkMajor) {
+      if (m0 > 0) {
+        issue_x(m0);
+        convert_x();
+      } else if constexpr (MS == 1) {
+        convert_x();
+      }
     }
     float acc[MS][NL];
+    if constexpr (kChunkMajor) {
+#pragma unroll
+      for (int i = 0; i < NL; ++i) acc[0][i] = 0.0f;
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        float xj[1][32];
+#pragma unroll
+        for (int w = 0; w < XW; ++w) {
+          const uint4 v = xraw[0][j][w];
+          xj[0][8 * w + 0] = bf16lo_to_f32(v.x);
+          xj[0][8 * w + 1] = bf16hi_to_f32(v.x);
+          xj[0][8 * w + 2] = bf16lo_to_f32(v.y);
+          xj[0][8 * w + 3] = bf16hi_to_f32(v.y);
+          xj[0][8 * w + 4] = bf16lo_to_f32(v.z);
+          xj[0][8 * w + 5] = bf16hi_to_f32(v.z);
+          xj[0][8 * w + 6] = bf16lo_to_f32(v.w);
+          xj[0][8 * w + 7] = bf16hi_to_f32(v.w);
+        }
+#pragma unroll
+        for (int i = 0; i < NL; ++i) {
+          float dot = 0.0f;
+          chunk_dot<1>(tab, lanebyte, wq[i][j], xj, &dot);
+          acc[0][i] = fmaf(sok[i][j] ? sc[i][j] : 0.0f, dot, acc[0][i]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    } else {
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
 #pragma unroll
@@ -475,6 +514,7 @@ __global__ __launch_bounds__(gemv_waves<ROUTE>() * 64) void k_gemv(GemmArgs p) {
       }
       // keep the scheduler from hoisting every row's LDS lookups at once
       __builtin_amdgcn_sched_barrier(0);
+    }
     }
 #pragma unroll
     for (int i = 0; i < NL; ++i)
