@@ -682,9 +682,13 @@ hipError_t launch_gemv_grouped(const GemmArgs &g, int ms_hint, hipStream_t s) {
 // ---------------------------------------------------------------------------
 // NT: the weight loads are non-temporal (one token: every weight row is read
 // once; with several tokens the tokens that share an expert read its rows
-// again, and keeping them cached measured faster).
-template <int FMT, int LPR, int NJ, int NP, int RB, int XF, int NT>
-__global__ __launch_bounds__(256) void k_down_combine(const float *__restrict__ h,
+// again, and keeping them cached measured faster). RS: 4 * RS waves, the RB
+// rows split between RS groups of 4 (each wave the same lane segments and
+// slots, over RB / RS rows), for one token with two chunks per lane, whose
+// waves otherwise each decode 8 rows of 2 chunks in sequence with few waves
+// per CU.
+template <int FMT, int LPR, int NJ, int NP, int RB, int XF, int NT, int RS>
+__global__ __launch_bounds__(256 * RS) void k_down_combine(const float *__restrict__ h,
                                                       const int32_t *__restrict__ slot_pos,
                                                       const int32_t *__restrict__ topk_ids,
                                                       const float *__restrict__ topk_w, int T,
@@ -698,8 +702,12 @@ __global__ __launch_bounds__(256) void k_down_combine(const float *__restrict__ 
   __shared__ float red[kMaxTopK][RB];
   const int t = blockIdx.y;
   const int n0 = blockIdx.x * RB;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  static_assert(RS == 1 || (RS == 2 && RB % 2 == 0), "row split");
+  constexpr int RW = RB / RS;        // rows per wave
+  const int wave_all = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int wave = wave_all & 3, rg = wave_all >> 2;  // slot wave, row group
   const int seg = wave * SPW + lane / LPR, li = lane % LPR;
+  const int nr0 = rg * RW;           // this wave's first row within the workgroup's RB
   const int nch = I / 32;
   const int64_t rowbytes = I / 2;
   const int64_t sc_per_row = I / Fmt<FMT>::kBlock;
@@ -719,7 +727,7 @@ __global__ __launch_bounds__(256) void k_down_combine(const float *__restrict__ 
     praw[q] = slot_pos[slot];
   }
   __builtin_amdgcn_sched_barrier(0);
-  build_pair_table<FMT, kGemvRep>(tab_all, 0, 4);
+  build_pair_table<FMT, kGemvRep>(tab_all, 0, 4 * RS);
   __builtin_amdgcn_sched_barrier(0);
   // Chunks past the row end read chunk 0 and get scale 0, as in the GEMV.
   bool cok[NJ];
@@ -742,11 +750,11 @@ __global__ __launch_bounds__(256) void k_down_combine(const float *__restrict__ 
 #pragma unroll
       for (int w = 0; w < 8; ++w) hraw[q][jj][w] = src[w];
     }
-  uint4 wq[RB][NP][NJ];
-  float sc[RB][NP][NJ];
+  uint4 wq[RW][NP][NJ];
+  float sc[RW][NP][NJ];
 #pragma unroll
-  for (int n = 0; n < RB; ++n) {
-    const int row = n0 + n;
+  for (int n = 0; n < RW; ++n) {
+    const int row = n0 + nr0 + n;
     const int64_t rc = row < H ? row : H - 1;
 #pragma unroll
     for (int q = 0; q < NP; ++q)
@@ -766,7 +774,8 @@ __global__ __launch_bounds__(256) void k_down_combine(const float *__restrict__ 
   const char *tab = reinterpret_cast<const char *>(tab_all);
   const uint32_t lanebyte = (uint32_t)(lane & (kGemvRep - 1)) * 8u;
 #pragma unroll
-  for (int n = 0; n < RB; ++n) {
+  for (int n = 0; n < RW; ++n) {
+    const int nn = nr0 + n;          // row within the workgroup
 #pragma unroll
     for (int q = 0; q < NP; ++q) {
       float acc = 0.0f;
@@ -782,11 +791,11 @@ __global__ __launch_bounds__(256) void k_down_combine(const float *__restrict__ 
         }
         float dot = 0.0f;
         chunk_dot<1>(tab, lanebyte, wq[n][q][jj], xj, &dot);
-        acc = fmaf((cok[jj] && n0 + n < H) ? sc[n][q][jj] : 0.0f, dot, acc);
+        acc = fmaf((cok[jj] && n0 + nn < H) ? sc[n][q][jj] : 0.0f, dot, acc);
       }
       acc = seg_sum<LPR>(acc);
-      if constexpr (XF) acc += b2[(int64_t)eraw[q] * H + (n0 + n < H ? n0 + n : H - 1)];
-      if (li == 0 && live[q]) red[q * NSEG + seg][n] = wj[q] * acc;
+      if constexpr (XF) acc += b2[(int64_t)eraw[q] * H + (n0 + nn < H ? n0 + nn : H - 1)];
+      if (li == 0 && live[q]) red[q * NSEG + seg][nn] = wj[q] * acc;
     }
   }
   lds_barrier();
@@ -798,18 +807,18 @@ __global__ __launch_bounds__(256) void k_down_combine(const float *__restrict__ 
   }
 }
 
-template <int FMT, int LPR, int NJ, int NP, int RB, int NT = 0>
+template <int FMT, int LPR, int NJ, int NP, int RB, int NT = 0, int RS = 1>
 static void launch_down_combine_rb(const float *h, const int32_t *slot_pos, const int32_t *topk_ids,
                                    const float *topk_w, int T, int k, const uint8_t *w2,
                                    const void *w2_scale, const float *b2, int H, int I, uint16_t *out,
                                    hipStream_t s) {
   const dim3 grid((unsigned)cdiv(H, RB), (unsigned)T);
   if (b2)
-    hipLaunchKernelGGL((k_down_combine<FMT, LPR, NJ, NP, RB, 1, NT>), grid, dim3(256), 0, s, h, slot_pos,
-                       topk_ids, topk_w, T, k, w2, w2_scale, H, I, out, b2);
+    hipLaunchKernelGGL((k_down_combine<FMT, LPR, NJ, NP, RB, 1, NT, RS>), grid, dim3(256 * RS), 0, s, h,
+                       slot_pos, topk_ids, topk_w, T, k, w2, w2_scale, H, I, out, b2);
   else
-    hipLaunchKernelGGL((k_down_combine<FMT, LPR, NJ, NP, RB, 0, NT>), grid, dim3(256), 0, s, h, slot_pos,
-                       topk_ids, topk_w, T, k, w2, w2_scale, H, I, out, b2);
+    hipLaunchKernelGGL((k_down_combine<FMT, LPR, NJ, NP, RB, 0, NT, RS>), grid, dim3(256 * RS), 0, s, h,
+                       slot_pos, topk_ids, topk_w, T, k, w2, w2_scale, H, I, out, b2);
 }
 
 // Output rows per workgroup: the smallest of 4, 8, 12 that keeps the grid
@@ -834,8 +843,12 @@ static void launch_down_combine_t(const float *h, const int32_t *slot_pos, const
     else
       launch_down_combine_rb<FMT, LPR, NJ, NP, 4>(h, slot_pos, topk_ids, topk_w, T, k, w2, w2_scale, b2, H, I, out, s);
   } else if ((int64_t)T * cdiv(H, 8) <= kMaxWG) {
-    if (T == 1)
-      launch_down_combine_rb<FMT, LPR, NJ, NP, 8, 1>(h, slot_pos, topk_ids, topk_w, T, k, w2, w2_scale, b2, H, I, out, s);
+    if (T == 1) {
+      if constexpr (NJ == 2)  // two chunks per lane: the 8 rows over two groups of 4 waves
+        launch_down_combine_rb<FMT, LPR, NJ, NP, 8, 1, 2>(h, slot_pos, topk_ids, topk_w, T, k, w2, w2_scale, b2, H, I, out, s);
+      else
+        launch_down_combine_rb<FMT, LPR, NJ, NP, 8, 1>(h, slot_pos, topk_ids, topk_w, T, k, w2, w2_scale, b2, H, I, out, s);
+    }
     else
       launch_down_combine_rb<FMT, LPR, NJ, NP, 8>(h, slot_pos, topk_ids, topk_w, T, k, w2, w2_scale, b2, H, I, out, s);
   }
