@@ -685,8 +685,8 @@ hipError_t launch_gemv_grouped(const GemmArgs &g, int ms_hint, hipStream_t s) {
 // again, and keeping them cached measured faster). RS: 4 * RS waves, the RB
 // rows split between RS groups of 4 (each wave the same lane segments and
 // slots, over RB / RS rows), for one token with two chunks per lane, whose
-// waves otherwise each decode 8 rows of 2 chunks in sequence with few waves
-// per CU.
+// 4 waves otherwise each decode 8 rows of 2 chunks in sequence, at 158
+// VGPRs, with few waves per CU.
 template <int FMT, int LPR, int NJ, int NP, int RB, int XF, int NT, int RS>
 __global__ __launch_bounds__(256 * RS) void k_down_combine(const float *__restrict__ h,
                                                       const int32_t *__restrict__ slot_pos,
@@ -702,7 +702,7 @@ __global__ __launch_bounds__(256 * RS) void k_down_combine(const float *__restri
   __shared__ float red[kMaxTopK][RB];
   const int t = blockIdx.y;
   const int n0 = blockIdx.x * RB;
-  static_assert(RS == 1 || (RS == 2 && RB % 2 == 0), "row split");
+  static_assert(RS >= 1 && RS <= 4 && RB % RS == 0, "row split");
   constexpr int RW = RB / RS;        // rows per wave
   const int wave_all = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int wave = wave_all & 3, rg = wave_all >> 2;  // slot wave, row group
@@ -837,18 +837,25 @@ static void launch_down_combine_t(const float *h, const int32_t *slot_pos, const
   // one token: non-temporal weight loads (OLMoE-shaped layer 17.64 -> 16.9 us,
   // Qwen3-shaped 17.77 -> 16.77, gpt-oss-shaped 43.0 -> 41.3, same box, the
   // gate_up loads non-temporal too); T = 1 takes 4 or 8 rows for H <= 4096
+  // One token with two chunks per lane (I > 2048): 12 rows per workgroup over
+  // three groups of 4 waves (4 rows per wave), 240 workgroups, one per CU at
+  // the gpt-oss shape (against 8 rows over 8 waves, 360 workgroups of which
+  // 104 CUs ran two: gpt-oss-shaped T = 1 layer 35.7 -> 34.05 us, down +
+  // combine 17.5 -> 15.8 us; 6 rows over 8 waves, 480 workgroups: 34.1 us).
+  if constexpr (NJ == 2) {
+    if (T == 1) {
+      launch_down_combine_rb<FMT, LPR, NJ, NP, 12, 1, 3>(h, slot_pos, topk_ids, topk_w, T, k, w2, w2_scale, b2, H, I, out, s);
+      return;
+    }
+  }
   if ((int64_t)T * cdiv(H, 4) <= kMaxWG) {
     if (T == 1)
       launch_down_combine_rb<FMT, LPR, NJ, NP, 4, 1>(h, slot_pos, topk_ids, topk_w, T, k, w2, w2_scale, b2, H, I, out, s);
     else
       launch_down_combine_rb<FMT, LPR, NJ, NP, 4>(h, slot_pos, topk_ids, topk_w, T, k, w2, w2_scale, b2, H, I, out, s);
   } else if ((int64_t)T * cdiv(H, 8) <= kMaxWG) {
-    if (T == 1) {
-      if constexpr (NJ == 2)  // two chunks per lane: the 8 rows over two groups of 4 waves
-        launch_down_combine_rb<FMT, LPR, NJ, NP, 8, 1, 2>(h, slot_pos, topk_ids, topk_w, T, k, w2, w2_scale, b2, H, I, out, s);
-      else
-        launch_down_combine_rb<FMT, LPR, NJ, NP, 8, 1>(h, slot_pos, topk_ids, topk_w, T, k, w2, w2_scale, b2, H, I, out, s);
-    }
+    if (T == 1)
+      launch_down_combine_rb<FMT, LPR, NJ, NP, 8, 1>(h, slot_pos, topk_ids, topk_w, T, k, w2, w2_scale, b2, H, I, out, s);
     else
       launch_down_combine_rb<FMT, LPR, NJ, NP, 8>(h, slot_pos, topk_ids, topk_w, T, k, w2, w2_scale, b2, H, I, out, s);
   }
