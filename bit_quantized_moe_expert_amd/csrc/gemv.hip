@@ -110,7 +110,7 @@ constexpr int gemv_loads() {
   return a < b ? (a < c ? a : c) : (b < c ? b : c);
 }
 // One token (ROUTE > 0): at most 4, so the few routed experts' rows spread
-// over twice the workgroups (C1: 512 of 8 waves, 2 per CU; against 8 wave-
+// over twice the workgroups (an OLMoE-shaped token: 512 of 8 waves, 2 per CU; against 8 wave-
 // loads, the gate_up kernel 9.25 -> 8.86 us). Rows of two chunks per lane
 // (2048 < K <= 4096) take 6 rows per wave: a gpt-oss-shaped token's 4 x 5760
 // gate_up rows at 4 rows per wave need 5760 waves, more than the 4096 that

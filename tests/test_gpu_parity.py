@@ -81,7 +81,7 @@ def test_absmax_to_bf16_cast():
 
 
 def test_quantize_large_stack_bitexact_sample():
-    """A C1-sized gate_up stack quantized on the device; sampled experts bit-exact."""
+    """An OLMoE-1B-7B-sized gate_up stack (E=64, 2048 x 2048) quantized on the device; sampled experts bit-exact."""
     wl = S.WORKLOADS["olmoe_decode"]
     w13 = S.make_stack_torch(wl, 0, "w13", DEV)
     pk, sc = M.quantize(w13, wl.fmt)
