@@ -255,3 +255,16 @@ def test_stream_read_validation():
     assert L.nf4moe_stream_read(FAKE, 32, 5, FAKE, STREAM) == INVALID
     assert L.nf4moe_stream_read(FAKE + 8, 32, 4, FAKE, STREAM) == INVALID
     assert L.nf4moe_stream_read(None, 32, 4, FAKE, STREAM) == INVALID
+
+
+def test_auto_path_rule():
+    """AUTO's family choice, host only: the small-M kernels for at most 64 routed
+    rows (NF4, both absmax storages) or 48 (MXFP4), and only while K fits their
+    two 16-byte chunks per lane (K <= 4096); the MFMA kernels otherwise."""
+    SMALL, MFMA = pkg.PATH_SMALL_M, pkg.PATH_MFMA
+    for fmt, r_max in ((0, 64), (2, 64), (1, 48)):
+        assert pkg.auto_path(fmt, 1, 2048) == SMALL
+        assert pkg.auto_path(fmt, r_max, 4096) == SMALL
+        assert pkg.auto_path(fmt, r_max + 1, 2048) == MFMA
+        assert pkg.auto_path(fmt, 1, 4097) == MFMA
+        assert pkg.auto_path(fmt, 32768, 2048) == MFMA
